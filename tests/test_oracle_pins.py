@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against closed forms, invariants, brute force and
+library routines (runs without a GPU).
+
+Each test names the part of the oracle it pins and the plausible mistake it
+would catch.
+"""
+import dataclasses
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import erf, softmax
+
+import synth
+from oracle import expert as ex
+from oracle import int4 as q4
+from oracle import joint
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+TINY = synth.CONFIGS["tiny"]
+# very small dims for brute-force loops
+MICRO = synth.ExpertDims(n_layers=2, width=8, n_q_heads=2, n_kv_heads=1, head_dim=4, mlp_dim=8,
+                         prefix_len=3, chunk_len=2, action_dim=3, n_steps=2, batch=1,
+                         weight_dtype="f32", weight_std=0.3)
+
+
+def _inputs(d, seed=0, **kw):
+    return synth.make_expert_inputs(d, seed, **kw)
+
+
+# ---------------------------------------------------------------- P1 / P2 (Euler)
+def test_zero_weights_keep_noise_exactly():
+    """P1: all linear weights and biases zero => v == 0 => x_N == x_0 bit for bit."""
+    inp = _inputs(TINY)
+    for k in ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d"):
+        inp[k] = np.zeros_like(inp[k])
+    x = ex.denoise(inp, TINY)
+    assert np.array_equal(x, inp["noise"].astype(np.float64))
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "euler_closed_form.json")))["cases"])
+def test_linear_velocity_closed_form(case):
+    """P2: v = lambda x gives x_N = (1 + lambda dt)^N x_0 (golden factors).
+    Catches a wrong dt sign, a wrong step count or a schedule that does not end at 0."""
+    n, lam = case["n_steps"], case["lambda"]
+    x0 = synth.normal(0, "noise", (16, 8))
+    t = ex.schedule(n)
+    x = ex.euler(x0, t, lambda x, k: lam * x)
+    if "factor_num" in case:   # dt = -1/4 is exact in binary: the result is exact
+        assert np.array_equal(x, x0.astype(np.float64) * case["factor_num"] / case["factor_den"])
+    np.testing.assert_allclose(x, x0.astype(np.float64) * case["factor"], rtol=1e-12, atol=0)
+
+
+def test_schedule_and_step_sizes():
+    t = ex.schedule(4)
+    assert t.tolist() == [1.0, 0.75, 0.5, 0.25]
+    assert ex.step_sizes(t).tolist() == [-0.25] * 4
+    t10 = ex.schedule(10)
+    assert t10[0] == 1.0 and abs(float(t10[-1]) - 0.1) < 1e-7
+    assert abs(ex.step_sizes(t10).sum() + 1.0) < 1e-12      # integrates from 1 to 0
+
+
+# ---------------------------------------------------------------- P3 (cache)
+def _prefix_net(d, seed=1):
+    rng = lambda name, shape: synth.normal(seed, name, shape, d.weight_std).astype(np.float64)
+    pp = {
+        "w_qkv": rng("p_w_qkv", (d.n_layers, d.qkv_dim, d.width)),
+        "w_o": rng("p_w_o", (d.n_layers, d.width, d.n_q_heads * d.head_dim)),
+        "w_gu": rng("p_w_gu", (d.n_layers, 2 * d.mlp_dim, d.width)),
+        "w_d": rng("p_w_d", (d.n_layers, d.width, d.mlp_dim)),
+    }
+    tokens = synth.normal(seed, "p_tokens", (d.prefix_len, d.width)).astype(np.float64)
+    return pp, tokens
+
+
+@pytest.mark.parametrize("d", [TINY, dataclasses.replace(MICRO, weight_std=0.3)])
+def test_cached_prefix_equals_recomputed(d):
+    """P3: the cached path, fed the prefix K/V the prefix network produces, equals
+    the joint masked sequence recomputed every step.  Catches a wrong concat
+    order, a missing chunk-to-chunk attention, or a mask leak."""
+    inp = _inputs(d)
+    pp, tokens = _prefix_net(d)
+    kp, vp = joint.prefix_kv(tokens, pp, d)
+    inp["k_pre"], inp["v_pre"] = kp[None], vp[None]
+    cached = ex.denoise(inp, d)[0]
+    recomputed = joint.denoise_recomputed(inp, pp, tokens, d)
+    assert ex.rel_err(cached, recomputed) < 1e-12
+    # the prefix really matters (the check is not vacuous)
+    inp2 = dict(inp)
+    inp2["k_pre"] = inp["k_pre"] * 0.5
+    assert ex.rel_err(ex.denoise(inp2, d)[0], cached) > 1e-6
+
+
+# ---------------------------------------------------------------- P4 brute force
+def _bf_velocity(x, k, t, inp, d):
+    """Whole-network velocity with explicit Python loops, from the definitions
+    (independent of the vectorised oracle)."""
+    D, A, L, dh = d.width, d.action_dim, d.n_layers, d.head_dim
+    hq, hkv, F = d.n_q_heads, d.n_kv_heads, d.mlp_dim
+    half = D // 2
+    tk = float(t[k])
+    emb = [0.0] * D
+    for i in range(half):
+        period = 4e-3 * (4.0 / 4e-3) ** (i / (half - 1))
+        emb[i] = math.sin(2 * math.pi * tk / period)
+        emb[half + i] = math.cos(2 * math.pi * tk / period)
+
+    def mod(j):
+        sc = [float(inp["b_mod"][j][o]) + sum(float(inp["w_mod"][j][o][c]) * emb[c] for c in range(D))
+              for o in range(D)]
+        sh = [float(inp["b_mod"][j][D + o]) + sum(float(inp["w_mod"][j][D + o][c]) * emb[c] for c in range(D))
+              for o in range(D)]
+        return sc, sh
+
+    def norm(row, sc, sh):
+        ms = sum(v * v for v in row) / D
+        r = math.sqrt(ms + d.rms_eps)
+        return [row[i] / r * (1 + sc[i]) + sh[i] for i in range(D)]
+
+    def lin(w, row):  # w[out][in]
+        return [sum(float(w[o][i]) * row[i] for i in range(len(row))) for o in range(len(w))]
+
+    T = len(x)
+    h = []
+    for r in range(T):
+        h.append([float(inp["b_in"][o]) + sum(float(inp["w_in"][o][a]) * x[r][a] for a in range(A))
+                  for o in range(D)])
+    for l in range(L):
+        sc, sh = mod(2 * l)
+        us = [norm(h[r], sc, sh) for r in range(T)]
+        qkv = [lin(inp["w_qkv"][l], u) for u in us]
+        o_rows = [[0.0] * (hq * dh) for _ in range(T)]
+        P = inp["k_pre"].shape[2]
+        for head in range(hq):
+            kvh = head // (hq // hkv)
+            keys, vals = [], []
+            for p in range(P):
+                keys.append([float(inp["k_pre"][0][l][p][kvh][c]) for c in range(dh)])
+                vals.append([float(inp["v_pre"][0][l][p][kvh][c]) for c in range(dh)])
+            for r in range(T):
+                keys.append(qkv[r][hq * dh + kvh * dh: hq * dh + (kvh + 1) * dh])
+                vals.append(qkv[r][(hq + hkv) * dh + kvh * dh: (hq + hkv) * dh + (kvh + 1) * dh])
+            for r in range(T):
+                qv = qkv[r][head * dh:(head + 1) * dh]
+                sc_ = [sum(qv[c] * key[c] for c in range(dh)) / math.sqrt(dh) for key in keys]
+                m = max(sc_)
+                w = [math.exp(s - m) for s in sc_]
+                z = sum(w)
+                for c in range(dh):
+                    o_rows[r][head * dh + c] = sum(w[j] * vals[j][c] for j in range(len(keys))) / z
+        for r in range(T):
+            delta = lin(inp["w_o"][l], o_rows[r])
+            h[r] = [h[r][i] + delta[i] for i in range(D)]
+        sc, sh = mod(2 * l + 1)
+        for r in range(T):
+            u = norm(h[r], sc, sh)
+            g = lin(inp["w_gu"][l][:F], u)
+            up = lin(inp["w_gu"][l][F:], u)
+            a = [0.5 * g[i] * (1 + math.tanh(math.sqrt(2 / math.pi) * (g[i] + 0.044715 * g[i] ** 3))) * up[i]
+                 for i in range(F)]
+            delta = lin(inp["w_d"][l], a)
+            h[r] = [h[r][i] + delta[i] for i in range(D)]
+    sc, sh = mod(2 * L)
+    out = []
+    for r in range(T):
+        u = norm(h[r], sc, sh)
+        out.append([float(inp["b_out"][a]) + sum(float(inp["w_out"][a][i]) * u[i] for i in range(D))
+                    for a in range(A)])
+    return out
+
+
+def test_brute_force_whole_network():
+    """P4: the vectorised oracle equals explicit loops on tiny inputs to 1e-12.
+    Catches transposed weights, wrong head/KV-head indexing, swapped norm
+    indices, a gelu on the wrong half, a wrong embedding time."""
+    d = MICRO
+    inp = _inputs(d)
+    t = ex.schedule(d.n_steps)
+    x = [[float(v) for v in row] for row in inp["noise"][0]]
+    for k, dt in enumerate(ex.step_sizes(t)):
+        v = _bf_velocity(x, k, t, inp, d)
+        x = [[x[r][a] + dt * v[r][a] for a in range(d.action_dim)] for r in range(len(x))]
+    ref = ex.denoise(inp, d)[0]
+    np.testing.assert_allclose(np.array(x), ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- attention pins
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_uniform_attention_when_queries_are_zero():
+    """P5: zero queries => every score equal => o = mean of all value rows."""
+    q = np.zeros((4, 5, 8))
+    k, v = _rand((1, 9, 8), 1), _rand((1, 9, 8), 2)
+    o = ex.attention(q, k, v)
+    np.testing.assert_allclose(o, np.broadcast_to(v[0].mean(axis=0), o.shape), rtol=0, atol=1e-14)
+
+
+def test_one_hot_attention():
+    """P6: one key aligned with the query and scaled so its score leads by >= 30
+    => output equals that key's value row to within e^-30."""
+    dh = 16
+    q = _rand((1, 1, dh), 3)
+    k = _rand((1, 12, dh), 4) * 0.01
+    k[0, 7] = q[0, 0] * (40 * math.sqrt(dh) / (q[0, 0] @ q[0, 0]))
+    v = _rand((1, 12, dh), 5)
+    o = ex.attention(q, k, v)
+    np.testing.assert_allclose(o[0, 0], v[0, 7], rtol=0, atol=12 * math.exp(-30) * np.abs(v).max())
+
+
+def test_prefix_permutation_invariance():
+    """P7: permuting key/value rows together leaves the output unchanged."""
+    q, k, v = _rand((8, 5, 16), 6), _rand((1, 30, 16), 7), _rand((1, 30, 16), 8)
+    perm = np.random.default_rng(9).permutation(30)
+    np.testing.assert_allclose(ex.attention(q, k[:, perm], v[:, perm]), ex.attention(q, k, v),
+                               rtol=0, atol=1e-13)
+
+
+def _lse_merge(q, k, v, splits):
+    """Attention computed per key block and combined by log-sum-exp weights."""
+    dh = q.shape[-1]
+    parts = []
+    for lo, hi in zip(splits[:-1], splits[1:]):
+        s = q @ k[lo:hi].T / math.sqrt(dh)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        parts.append((m, p.sum(axis=1, keepdims=True), p @ v[lo:hi]))
+    mg = np.max(np.concatenate([m for m, _, _ in parts], axis=1), axis=1, keepdims=True)
+    num = sum(np.exp(m - mg) * o for m, _, o in parts)
+    den = sum(np.exp(m - mg) * l for m, l, _ in parts)
+    return num / den
+
+
+def test_split_key_lse_merge_identity():
+    """P8: any partition of the keys merged by log-sum-exp equals unsplit softmax."""
+    q, k, v = _rand((6, 16), 10) * 3, _rand((50, 16), 11), _rand((50, 16), 12)
+    ref = ex.attention(q[None], k[None], v[None])[0]
+    for splits in ([0, 50], [0, 1, 50], [0, 16, 32, 48, 50], [0, 7, 8, 30, 49, 50]):
+        np.testing.assert_allclose(_lse_merge(q, k, v, splits), ref, rtol=0, atol=1e-13)
+
+
+def test_gqa_reductions():
+    """P9: Hkv == Hq is per-head textbook attention; Hq == Hkv == 1 is textbook
+    attention; Hq=4, Hkv=2 maps query heads {0,1}->kv 0 and {2,3}->kv 1."""
+    def textbook(q, k, v):
+        return softmax(q @ k.T / math.sqrt(q.shape[-1]), axis=1) @ v
+
+    q, k, v = _rand((3, 5, 8), 13), _rand((3, 9, 8), 14), _rand((3, 9, 8), 15)
+    o = ex.attention(q, k, v)
+    for i in range(3):
+        np.testing.assert_allclose(o[i], textbook(q[i], k[i], v[i]), rtol=0, atol=1e-14)
+    o1 = ex.attention(q[:1], k[:1], v[:1])
+    np.testing.assert_allclose(o1[0], textbook(q[0], k[0], v[0]), rtol=0, atol=1e-14)
+    q4_, k2, v2 = _rand((4, 5, 8), 16), _rand((2, 9, 8), 17), _rand((2, 9, 8), 18)
+    o = ex.attention(q4_, k2, v2)
+    for i in range(4):
+        np.testing.assert_allclose(o[i], textbook(q4_[i], k2[i // 2], v2[i // 2]), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- norm / gelu / embedding
+def test_ada_rms_invariants():
+    """P10: scale invariance, and a constant row a*1 maps to sign(a)(1+s)+c."""
+    h = _rand((4, 64), 19)
+    s, c = _rand(64, 20) * 0.3, _rand(64, 21) * 0.3
+    np.testing.assert_allclose(ex.ada_rms(7.5 * h, s, c, 0.0), ex.ada_rms(h, s, c, 0.0), rtol=1e-13)
+    for a in (3.0, -0.25):
+        row = np.full((1, 64), a)
+        np.testing.assert_allclose(ex.ada_rms(row, s, c, 0.0)[0], np.sign(a) * (1 + s) + c, rtol=1e-14)
+    # eps enters under the root: the all-zero row maps to the shift
+    np.testing.assert_array_equal(ex.ada_rms(np.zeros((1, 64)), s, c, 1e-6)[0], c)
+
+
+def test_gelu_identities():
+    """P11: gelu(z) - gelu(-z) = z, gelu(0) = 0, and the tanh form stays within
+    1e-3 of the exact z*Phi(z) (catches a wrong constant)."""
+    z = np.linspace(-6, 6, 2001)
+    np.testing.assert_allclose(ex.gelu_tanh(z) - ex.gelu_tanh(-z), z, rtol=0, atol=1e-14)
+    assert ex.gelu_tanh(np.array([0.0]))[0] == 0.0
+    exact = 0.5 * z * (1 + erf(z / math.sqrt(2)))
+    assert np.max(np.abs(ex.gelu_tanh(z) - exact)) < 1e-3
+    assert np.max(np.abs(ex.gelu_tanh(z) - exact)) > 1e-6     # and it is the tanh form, not erf
+
+
+def test_timestep_embedding():
+    """P12: e(0) = [0..0, 1..1]; each (sin, cos) pair has unit norm; the shortest
+    period is 4e-3 and the longest 4.0."""
+    D = 256
+    e0 = ex.timestep_embedding(0.0, D)
+    assert np.array_equal(e0, np.concatenate([np.zeros(D // 2), np.ones(D // 2)]))
+    for t in (0.1, 0.75, 1.0):
+        e = ex.timestep_embedding(t, D)
+        np.testing.assert_allclose(e[:D // 2] ** 2 + e[D // 2:] ** 2, 1.0, rtol=1e-14)
+    # quarter period of the longest component at t=1, of the shortest at t=1e-3
+    assert abs(ex.timestep_embedding(1.0, D)[D // 2 - 1] - 1.0) < 1e-14
+    assert abs(ex.timestep_embedding(1e-3, D)[0] - 1.0) < 1e-14
+    assert abs(ex.timestep_embedding(1e-3, D)[D // 2]) < 1e-13
+
+
+def test_modulation_tables_wiring():
+    """Tables: zero weights give the bias; a one-hot weight row selects one
+    embedding component into the right (step, norm, scale/shift, column) slot."""
+    n_mod, D = 3, 16
+    b = _rand((n_mod, 2 * D), 22)
+    w = np.zeros((n_mod, 2 * D, D))
+    t = [1.0, 0.5]
+    tab = ex.modulation_tables(t, w, b)
+    assert tab.shape == (2, n_mod, 2, D)
+    np.testing.assert_array_equal(tab[1, 2, 1], b[2, D:])
+    w[2, D + 5, 3] = 1.0       # shift of norm 2, column 5 <- e_3
+    tab = ex.modulation_tables(t, w, np.zeros_like(b))
+    assert tab[1, 2, 1, 5] == ex.timestep_embedding(0.5, D)[3]
+    assert np.count_nonzero(tab[1]) == 1
+
+
+# ---------------------------------------------------------------- int4 (P13)
+def test_int4_golden_nibbles():
+    g = json.load(open(os.path.join(GOLDEN, "int4_nibbles.json")))
+    row = np.zeros((1, 128), np.float32)
+    row[0, :8] = g["row_head"]
+    packed, s = q4.quantize(row)
+    assert s[0, 0] == g["scale_bits"]
+    assert packed[0, :4].tolist() == g["bytes_head"]
+    assert q4.unpack_codes(packed)[0, :8].tolist() == g["codes_head"]
+    assert not packed[0, 4:].any()
+
+
+def test_int4_round_trip_and_bounds():
+    w = synth.normal(0, "w_qkv", (64, 512), 0.02)
+    packed, s = q4.quantize(w)
+    codes = q4.unpack_codes(packed)
+    assert codes.min() >= -8 and codes.max() <= 7
+    # repack the unpacked codes: identity on bytes
+    nib = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    assert np.array_equal(nib[:, 0::2] | (nib[:, 1::2] << 4), packed)
+    deq = q4.dequantize(packed, s)
+    sc = np.repeat(q4.scales_f64(s), 128, axis=1)
+    assert np.all(np.abs(w - deq) <= sc / 2 * (1 + 1e-6))
+    # each group's largest magnitude lands on +-7
+    assert np.all(np.abs(codes.reshape(64, 4, 128)).max(axis=2) == 7)
+    # lossless when W is exactly q*s
+    w2 = deq.astype(np.float32)
+    p2, s2 = q4.quantize(w2)
+    assert np.array_equal(s2, s) and np.array_equal(p2, packed)
+    # all-zero group -> scale 0, codes 0
+    w3 = w.copy()
+    w3[5, 128:256] = 0
+    p3, s3 = q4.quantize(w3)
+    assert s3[5, 1] == 0 and not q4.unpack_codes(p3)[5, 128:256].any()
+
+
+def test_int4_scale_is_bf16_rne_of_amax_over_7():
+    # amax/7 = 1.1428571 -> bf16 1.140625 (0x3F92); 7.0/7 -> 1.0
+    w = np.zeros((2, 128), np.float32)
+    w[0, 3] = -8.0
+    w[1, 9] = 7.0
+    _, s = q4.quantize(w)
+    assert s[0, 0] == 0x3F92 and s[1, 0] == 0x3F80
+    codes = q4.unpack_codes(q4.quantize(w)[0])
+    assert codes[0, 3] == -7       # -8 / 1.140625 = -7.01 -> -7
+
+
+# ---------------------------------------------------------------- P15 batch independence
+def test_batch_independence():
+    d = dataclasses.replace(TINY, batch=3)
+    inp = _inputs(d)
+    xb = ex.denoise(inp, d)
+    one = _inputs(d, batch=1, samples=[2])
+    assert np.array_equal(ex.denoise(one, d)[0], xb[2])
+    assert np.array_equal(one["noise"][0], inp["noise"][2])
