@@ -1,0 +1,197 @@
+"""Thin Python binding of libphyai.so (the MI355X cached-prefix flow-matching denoise loop).
+
+Only argument marshalling lives here: every step of the loop runs in the HIP
+kernels behind the C ABI declared in ``include/phyai.h``.  PyTorch supplies device
+memory (``tensor.data_ptr()``) and the stream (``torch.cuda.current_stream()``).
+The library must be built first (``python -m flow_matching_action_cached_amd.build``);
+nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libphyai.so")
+
+F32, BF16, INT4_G128 = 0, 1, 2
+_DTYPES = {"f32": F32, "bf16": BF16, "int4": INT4_G128}
+STATUS = {0: "ok", 1: "invalid argument", 2: "bad state", 3: "out of memory", 4: "device error",
+          5: "unsupported"}
+
+EXPORTED = (
+    "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_timestep_tables",
+    "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
+    "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
+)
+
+
+class PhyaiError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("width", ctypes.c_int), ("n_q_heads", ctypes.c_int),
+                ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("mlp_dim", ctypes.c_int),
+                ("action_dim", ctypes.c_int), ("chunk_len", ctypes.c_int), ("max_prefix_len", ctypes.c_int),
+                ("max_batch", ctypes.c_int), ("weight_dtype", ctypes.c_int), ("rms_eps", ctypes.c_float),
+                ("max_arena_bytes", ctypes.c_size_t)]
+
+
+_WFIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d",
+            "s_qkv", "s_o", "s_gu", "s_d")
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WFIELDS]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libphyai.so (raises if it is not built: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m flow_matching_action_cached_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.phyai_create.argtypes = [ctypes.POINTER(Config), vp, ctypes.POINTER(vp)]
+    lib.phyai_set_weights.argtypes = [vp, ctypes.POINTER(Weights)]
+    lib.phyai_set_prefix_kv.argtypes = [vp, vp, vp, ci, ci]
+    lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
+    lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
+    lib.phyai_set_graph_mode.argtypes = [vp, ci]
+    lib.phyai_sync.argtypes = [vp]
+    lib.phyai_last_error.argtypes = [vp]
+    lib.phyai_last_error.restype = ctypes.c_char_p
+    lib.phyai_status_string.argtypes = [ci]
+    lib.phyai_status_string.restype = ctypes.c_char_p
+    lib.phyai_destroy.argtypes = [vp]
+    lib.phyai_destroy.restype = None
+    lib.phyai_quantize_int4_g128.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+    lib.phyai_get_modulation.argtypes = [vp, vp]
+    lib.phyai_version.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("phyai_last_error", "phyai_status_string", "phyai_destroy", "phyai_version"):
+            getattr(lib, name).restype = ci
+    _lib = lib
+    return lib
+
+
+def _stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class ActionExpert:
+    """One runner context: owns the device arena, the prefix KV cache, the tables
+    and the captured denoise graphs (see include/phyai.h)."""
+
+    def __init__(self, *, n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim,
+                 chunk_len, max_prefix_len, max_batch=1, weight_dtype="bf16", rms_eps=1e-6,
+                 max_arena_bytes=0, stream=None):
+        self._lib = load_library()
+        self.weight_dtype = weight_dtype
+        cfg = Config(n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim, chunk_len,
+                     max_prefix_len, max_batch, _DTYPES[weight_dtype], rms_eps, max_arena_bytes)
+        self.cfg = cfg
+        self._stream = stream
+        h = ctypes.c_void_p()
+        st = self._lib.phyai_create(ctypes.byref(cfg), _stream_handle(stream), ctypes.byref(h))
+        if st != 0:
+            raise PhyaiError(st, "phyai_create failed")
+        self._h = h
+        self._batch = None
+
+    @classmethod
+    def from_dims(cls, d, **kw):
+        """Build from a ``synth.ExpertDims``-like object."""
+        return cls(n_layers=d.n_layers, width=d.width, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                   head_dim=d.head_dim, mlp_dim=d.mlp_dim, action_dim=d.action_dim, chunk_len=d.chunk_len,
+                   max_prefix_len=kw.pop("max_prefix_len", d.prefix_len), max_batch=kw.pop("max_batch", d.batch),
+                   weight_dtype=d.weight_dtype, rms_eps=d.rms_eps, **kw)
+
+    def _check(self, st):
+        if st != 0:
+            raise PhyaiError(st, self._lib.phyai_last_error(self._h).decode())
+
+    def set_weights(self, w: dict):
+        """w: dict of contiguous cuda tensors named as in phyai_weights."""
+        for k, t in w.items():
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{k} must be contiguous")
+        ws = Weights(*[_ptr(w.get(n)) for n in _WFIELDS])
+        self._check(self._lib.phyai_set_weights(self._h, ctypes.byref(ws)))
+        self.sync()
+
+    def set_prefix_kv(self, k, v):
+        """k, v: cuda [B][L][P][Hkv][dh] in the weight element type."""
+        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        self._check(self._lib.phyai_set_prefix_kv(self._h, _ptr(k), _ptr(v), int(k.shape[0]), int(k.shape[2])))
+        self._batch = int(k.shape[0])
+        self.sync()
+
+    def set_timestep_tables(self, t):
+        arr = (ctypes.c_float * len(t))(*[float(x) for x in t])
+        self._check(self._lib.phyai_set_timestep_tables(self._h, arr, len(t)))
+        self.n_steps = len(t)
+
+    def set_graph_mode(self, use_graph: bool):
+        self._check(self._lib.phyai_set_graph_mode(self._h, int(bool(use_graph))))
+
+    def denoise(self, noise, out=None):
+        """noise: cuda float32 [B][H][A]; returns x at t=0 (asynchronous on the stream)."""
+        import torch
+        assert noise.dtype == torch.float32 and noise.is_contiguous()
+        if out is None:
+            out = torch.empty_like(noise)
+        self._check(self._lib.phyai_denoise(self._h, _ptr(noise), int(noise.shape[0]), self.n_steps, _ptr(out)))
+        return out
+
+    def get_modulation(self):
+        import torch
+        c = self.cfg
+        out = torch.empty((self.n_steps, 2 * c.n_layers + 1, 2, c.width), dtype=torch.float32, device="cuda")
+        self._check(self._lib.phyai_get_modulation(self._h, _ptr(out)))
+        self.sync()
+        return out
+
+    def sync(self):
+        self._check(self._lib.phyai_sync(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.phyai_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def quantize_int4_g128(w, stream=None):
+    """Offline int4 quantiser on the GPU: w cuda float32 [..., K] (K % 128 == 0) ->
+    (packed uint8 [..., K/2], scales int16 holding bf16 bits [..., K/128])."""
+    import torch
+    lib = load_library()
+    assert w.dtype == torch.float32 and w.is_contiguous() and w.shape[-1] % 128 == 0
+    cols = int(w.shape[-1])
+    rows = int(w.numel() // cols)
+    packed = torch.empty((*w.shape[:-1], cols // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((*w.shape[:-1], cols // 128), dtype=torch.int16, device=w.device)
+    st = lib.phyai_quantize_int4_g128(_ptr(w), rows, cols, _ptr(packed), _ptr(scales), _stream_handle(stream))
+    if st != 0:
+        raise PhyaiError(st, "phyai_quantize_int4_g128 failed")
+    return packed, scales

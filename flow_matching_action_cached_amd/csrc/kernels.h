@@ -1,0 +1,67 @@
+// Internal interface between the host runtime (runtime.cpp) and the HIP kernels
+// (kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace phyai {
+
+enum WDtype { W_F32 = 0, W_BF16 = 1, W_INT4 = 2 };
+
+// Model, batch and schedule dimensions of one denoise launch.
+struct Dims {
+  int L, D, Hq, Hkv, dh, F, A, H;  // layers, width, heads, head_dim, MLP dim, action dim, chunk
+  int B, M, Mst;                   // batch, token rows (B*H), row stride of ssq (>= M)
+  int P, KS;                       // prefix length, key stride of the cache (>= P + H)
+  int qkv, nmod;                   // (Hq + 2 Hkv) * dh, 2L + 1
+  int N;                           // Euler steps
+  float eps;
+};
+
+// Device pointers of one context.  Element types depend on the weight dtype:
+// "io" = fp32 (F32) or bf16 (BF16, INT4); "act" = fp32 (F32) or bf16 (BF16, INT4);
+// expert linears: fp32 / bf16 / repacked int4 codes + bf16 scales.
+struct Bufs {
+  const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;  // io
+  const void *w_qkv, *w_o, *w_gu, *w_d;                     // expert linears
+  const uint16_t *s_qkv, *s_o, *s_gu, *s_d;                 // int4 scales (bf16 bits)
+  void *kc, *vt;          // K cache [Bmax][L][Hkv][KS][dh], V^T cache [Bmax][L][Hkv][dh][KS] (act)
+  const float* mod;       // [N][nmod][2][D] (scale, shift)
+  const float* cvec;      // [N][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
+  const float* dt;        // [N]
+  int cv_stride, cv_gu_off, cv_out_off;
+  float *x, *h, *ssq;     // state [M][A], residual [M][D], row sum-of-squares partials [D/16][Mst]
+  void *hs, *q, *o, *act; // act-typed: [M][D], [M][Hq dh], [M][Hq dh], [M][F]
+  float* attn_ws; unsigned* attn_cnt;
+  float* gemm_ws; unsigned* gemm_cnt;
+};
+
+// Launch shape of the split reductions (chosen by the host once per context).
+struct Plan {
+  int s_qkv, s_o, s_gu, s_d;  // k-splits across workgroups per linear
+  int attn_bps;               // 32-key blocks per attention split
+};
+
+// Scratch sizes the plan needs (floats / counters).
+size_t attn_ws_floats(const Dims& d, const Plan& p);
+size_t attn_counters(const Dims& d);
+size_t gemm_ws_floats(const Dims& d, const Plan& p);
+size_t gemm_counters(const Dims& d);
+Plan make_plan(const Dims& d, WDtype wt);
+
+// Enqueue the whole Euler loop (N steps) on `stream`.  x must already hold the noise.
+hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t stream);
+
+// One-off kernels.
+hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,
+                          float* mod_out, float* cvec_out, hipStream_t stream);
+hipError_t enqueue_install_prefix(const Dims& d, const void* k, const void* v, int batch, int prefix_len,
+                                  void* kc, void* vt, size_t elem_bytes, hipStream_t stream);
+hipError_t enqueue_quantize_int4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                                 uint16_t* scales, hipStream_t stream);
+hipError_t enqueue_repack_int4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t cols,
+                               hipStream_t stream);
+
+}  // namespace phyai

@@ -1,0 +1,423 @@
+// Host runtime behind include/phyai.h: the runner-like context that owns the
+// device arena (weights, prefix KV cache, activations, split scratch), the
+// timestep tables and the captured step graphs (PhyAI reading "PhyAI: Real-Time
+// Physical AI at the Edge, Scalable Rollouts in the Cloud", Figure 3 and
+// Sec. 5.5: stateful runners own KV caches, buffers and graph buckets).
+#include "../../include/phyai.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace phyai;
+
+struct phyai_ctx {
+  phyai_config cfg{};
+  int device = 0;
+  hipStream_t stream = nullptr;      // caller's stream: every call is ordered on it
+  hipStream_t cap_stream = nullptr;  // private stream used only for graph capture
+  std::string err;
+  WDtype wt = W_F32;
+  size_t es_io = 4, es_act = 4;      // element bytes of io weights / GEMM activations
+
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  Bufs b{};
+  Dims base{};
+
+  // tables (own allocation, grows with n_steps)
+  void* tab = nullptr;
+  int tab_cap = 0;
+  float* t_dev = nullptr;
+  double* e_dev = nullptr;
+
+  bool have_weights = false, have_prefix = false, have_tables = false;
+  int batch = 0, prefix_len = 0, n_steps = 0;
+  int use_graph = 1;
+  std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
+};
+
+namespace {
+
+phyai_status fail(phyai_ctx* c, phyai_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+#define HIPCHK(c, call)                                                                        \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess)                                                                      \
+      return fail((c), PHYAI_ERR_DEVICE, std::string(#call) + ": " + hipGetErrorString(e_));  \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  }
+};
+
+size_t wrow_bytes(WDtype wt, int K) { return wt == W_F32 ? (size_t)K * 4 : wt == W_BF16 ? (size_t)K * 2 : (size_t)K / 2; }
+
+void drop_graphs(phyai_ctx* c) {
+  for (auto& kv : c->graphs) hipGraphExecDestroy(kv.second);
+  c->graphs.clear();
+}
+
+Dims launch_dims(const phyai_ctx* c, int batch, int prefix_len, int n_steps) {
+  Dims d = c->base;
+  d.B = batch;
+  d.M = batch * d.H;
+  d.P = prefix_len;
+  d.N = n_steps;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* phyai_version(void) { return "phyai-mi355x 0.1 (gfx950)"; }
+
+const char* phyai_status_string(phyai_status s) {
+  switch (s) {
+    case PHYAI_OK: return "ok";
+    case PHYAI_ERR_INVALID_ARG: return "invalid argument";
+    case PHYAI_ERR_BAD_STATE: return "bad state";
+    case PHYAI_ERR_OOM: return "out of memory";
+    case PHYAI_ERR_DEVICE: return "device error";
+    case PHYAI_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* phyai_last_error(const phyai_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx** out) {
+  if (!out) return PHYAI_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!cfg) return PHYAI_ERR_INVALID_ARG;
+  const phyai_config& g = *cfg;
+  if (g.n_layers < 1 || g.width < 1 || g.n_q_heads < 1 || g.n_kv_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 ||
+      g.action_dim < 1 || g.chunk_len < 1 || g.max_prefix_len < 1 || g.max_batch < 1 || !(g.rms_eps > 0.f))
+    return PHYAI_ERR_INVALID_ARG;
+  if (g.weight_dtype != PHYAI_F32 && g.weight_dtype != PHYAI_BF16 && g.weight_dtype != PHYAI_INT4_G128)
+    return PHYAI_ERR_INVALID_ARG;
+  if (g.width % 128 || g.mlp_dim % 128 || (g.n_q_heads * g.head_dim) % 128 || g.head_dim % 32 ||
+      g.head_dim > 256 || g.n_q_heads % g.n_kv_heads || g.action_dim > 256 || g.chunk_len * g.max_batch > 64)
+    return PHYAI_ERR_UNSUPPORTED;
+  if (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) return PHYAI_ERR_UNSUPPORTED;
+
+  phyai_ctx* c = new phyai_ctx();
+  c->cfg = g;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->wt = g.weight_dtype == PHYAI_F32 ? W_F32 : g.weight_dtype == PHYAI_BF16 ? W_BF16 : W_INT4;
+  c->es_io = c->wt == W_F32 ? 4 : 2;
+  c->es_act = c->es_io;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+
+  Dims& d = c->base;
+  d.L = g.n_layers; d.D = g.width; d.Hq = g.n_q_heads; d.Hkv = g.n_kv_heads; d.dh = g.head_dim;
+  d.F = g.mlp_dim; d.A = g.action_dim; d.H = g.chunk_len;
+  d.B = g.max_batch; d.M = g.max_batch * g.chunk_len; d.Mst = d.M;
+  d.P = g.max_prefix_len;
+  d.KS = (g.max_prefix_len + g.chunk_len + 31) / 32 * 32;
+  d.qkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim;
+  d.nmod = 2 * g.n_layers + 1;
+  d.N = 1;
+  d.eps = g.rms_eps;
+
+  const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
+  Layout lay;
+  const size_t o_w_in = lay.take((size_t)D * A * c->es_io), o_b_in = lay.take((size_t)D * c->es_io);
+  const size_t o_w_out = lay.take((size_t)A * D * c->es_io), o_b_out = lay.take((size_t)A * c->es_io);
+  const size_t o_w_mod = lay.take((size_t)d.nmod * 2 * D * D * c->es_io);
+  const size_t o_b_mod = lay.take((size_t)d.nmod * 2 * D * c->es_io);
+  const size_t o_w_qkv = lay.take(wrow_bytes(c->wt, D) * d.qkv * L);
+  const size_t o_w_o = lay.take(wrow_bytes(c->wt, qd) * D * L);
+  const size_t o_w_gu = lay.take(wrow_bytes(c->wt, D) * 2 * F * L);
+  const size_t o_w_d = lay.take(wrow_bytes(c->wt, F) * D * L);
+  size_t o_s_qkv = 0, o_s_o = 0, o_s_gu = 0, o_s_d = 0;
+  if (c->wt == W_INT4) {
+    o_s_qkv = lay.take((size_t)d.qkv * (D / 128) * 2 * L);
+    o_s_o = lay.take((size_t)D * (qd / 128) * 2 * L);
+    o_s_gu = lay.take((size_t)2 * F * (D / 128) * 2 * L);
+    o_s_d = lay.take((size_t)D * (F / 128) * 2 * L);
+  }
+  const size_t kv_elems = (size_t)d.B * L * d.Hkv * d.KS * d.dh;
+  const size_t o_kc = lay.take(kv_elems * c->es_act), o_vt = lay.take(kv_elems * c->es_act);
+  const size_t zero_begin = o_kc;
+  const size_t o_x = lay.take((size_t)d.M * A * 4), o_h = lay.take((size_t)d.M * D * 4);
+  const size_t o_ssq = lay.take((size_t)(D / 16) * d.Mst * 4);
+  const size_t o_hs = lay.take((size_t)d.M * D * c->es_act), o_q = lay.take((size_t)d.M * qd * c->es_act);
+  const size_t o_o = lay.take((size_t)d.M * qd * c->es_act), o_act = lay.take((size_t)d.M * F * c->es_act);
+  // scratch for split reductions: upper bounds over every batch / prefix length
+  const int nblk_max = (d.P + d.H + 31) / 32;
+  const size_t attn_ws = attn_counters(d) * nblk_max * ((size_t)(d.dh / 16) * 256 + 32);
+  Plan pmax = make_plan(d, c->wt);
+  const size_t o_attn_ws = lay.take(attn_ws * 4);
+  const size_t o_attn_cnt = lay.take(attn_counters(d) * 4);
+  const size_t o_gemm_ws = lay.take(std::max<size_t>(gemm_ws_floats(d, pmax), 1) * 4);
+  const size_t o_gemm_cnt = lay.take(gemm_counters(d) * 4);
+  c->arena_bytes = lay.off;
+  if (g.max_arena_bytes && c->arena_bytes > g.max_arena_bytes) {
+    delete c;
+    return PHYAI_ERR_OOM;
+  }
+  if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+  if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+    hipStreamDestroy(c->cap_stream);
+    delete c;
+    return PHYAI_ERR_OOM;
+  }
+  char* base = static_cast<char*>(c->arena);
+  Bufs& b = c->b;
+  b.w_in = base + o_w_in; b.b_in = base + o_b_in; b.w_out = base + o_w_out; b.b_out = base + o_b_out;
+  b.w_mod = base + o_w_mod; b.b_mod = base + o_b_mod;
+  b.w_qkv = base + o_w_qkv; b.w_o = base + o_w_o; b.w_gu = base + o_w_gu; b.w_d = base + o_w_d;
+  if (c->wt == W_INT4) {
+    b.s_qkv = reinterpret_cast<uint16_t*>(base + o_s_qkv);
+    b.s_o = reinterpret_cast<uint16_t*>(base + o_s_o);
+    b.s_gu = reinterpret_cast<uint16_t*>(base + o_s_gu);
+    b.s_d = reinterpret_cast<uint16_t*>(base + o_s_d);
+  }
+  b.kc = base + o_kc; b.vt = base + o_vt;
+  b.x = reinterpret_cast<float*>(base + o_x);
+  b.h = reinterpret_cast<float*>(base + o_h);
+  b.ssq = reinterpret_cast<float*>(base + o_ssq);
+  b.hs = base + o_hs; b.q = base + o_q; b.o = base + o_o; b.act = base + o_act;
+  b.attn_ws = reinterpret_cast<float*>(base + o_attn_ws);
+  b.attn_cnt = reinterpret_cast<unsigned*>(base + o_attn_cnt);
+  b.gemm_ws = reinterpret_cast<float*>(base + o_gemm_ws);
+  b.gemm_cnt = reinterpret_cast<unsigned*>(base + o_gemm_cnt);
+  // cache (keys past the live rows must read as finite), activations and counters start at 0
+  if (hipMemsetAsync(base + zero_begin, 0, c->arena_bytes - zero_begin, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess) {
+    hipFree(c->arena);
+    hipStreamDestroy(c->cap_stream);
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+  *out = c;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!w || !w->w_in || !w->b_in || !w->w_out || !w->b_out || !w->w_mod || !w->b_mod || !w->w_qkv || !w->w_o ||
+      !w->w_gu || !w->w_d)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: null weight pointer");
+  if (c->wt == W_INT4 && (!w->s_qkv || !w->s_o || !w->s_gu || !w->s_d))
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: int4 weights need the four scale arrays");
+  const Dims& d = c->base;
+  const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
+  const size_t e = c->es_io;
+  auto cp = [&](const void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(const_cast<void*>(dst), src, bytes, hipMemcpyDeviceToDevice, c->stream);
+  };
+  HIPCHK(c, cp(c->b.w_in, w->w_in, (size_t)D * A * e));
+  HIPCHK(c, cp(c->b.b_in, w->b_in, (size_t)D * e));
+  HIPCHK(c, cp(c->b.w_out, w->w_out, (size_t)A * D * e));
+  HIPCHK(c, cp(c->b.b_out, w->b_out, (size_t)A * e));
+  HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * 2 * D * D * e));
+  HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * 2 * D * e));
+  if (c->wt != W_INT4) {
+    HIPCHK(c, cp(c->b.w_qkv, w->w_qkv, wrow_bytes(c->wt, D) * d.qkv * L));
+    HIPCHK(c, cp(c->b.w_o, w->w_o, wrow_bytes(c->wt, qd) * D * L));
+    HIPCHK(c, cp(c->b.w_gu, w->w_gu, wrow_bytes(c->wt, D) * 2 * F * L));
+    HIPCHK(c, cp(c->b.w_d, w->w_d, wrow_bytes(c->wt, F) * D * L));
+  } else {
+    auto rp = [&](const void* dst, const void* src, int64_t rows, int64_t cols) {
+      return enqueue_repack_int4(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(const_cast<void*>(dst)),
+                                 rows, cols, c->stream);
+    };
+    HIPCHK(c, rp(c->b.w_qkv, w->w_qkv, (int64_t)L * d.qkv, D));
+    HIPCHK(c, rp(c->b.w_o, w->w_o, (int64_t)L * D, qd));
+    HIPCHK(c, rp(c->b.w_gu, w->w_gu, (int64_t)L * 2 * F, D));
+    HIPCHK(c, rp(c->b.w_d, w->w_d, (int64_t)L * D, F));
+    HIPCHK(c, cp(c->b.s_qkv, w->s_qkv, (size_t)L * d.qkv * (D / 128) * 2));
+    HIPCHK(c, cp(c->b.s_o, w->s_o, (size_t)L * D * (qd / 128) * 2));
+    HIPCHK(c, cp(c->b.s_gu, w->s_gu, (size_t)L * 2 * F * (D / 128) * 2));
+    HIPCHK(c, cp(c->b.s_d, w->s_d, (size_t)L * D * (F / 128) * 2));
+  }
+  c->have_weights = true;
+  c->have_tables = false;  // the tables fold the weights in: they must be rebuilt
+  drop_graphs(c);
+  return PHYAI_OK;
+}
+
+phyai_status phyai_set_prefix_kv(phyai_ctx* c, const void* k, const void* v, int batch, int prefix_len) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!k || !v) return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefix_kv: null pointer");
+  if (batch < 1 || batch > c->cfg.max_batch)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefix_kv: batch out of range [1, max_batch]");
+  if (prefix_len < 1 || prefix_len > c->cfg.max_prefix_len)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefix_kv: prefix_len out of range [1, max_prefix_len]");
+  HIPCHK(c, enqueue_install_prefix(c->base, k, v, batch, prefix_len, c->b.kc, c->b.vt, c->es_act, c->stream));
+  c->batch = batch;
+  c->prefix_len = prefix_len;
+  c->have_prefix = true;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_steps) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!t_host || n_steps < 1) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: need n_steps >= 1 times");
+  if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "set_timestep_tables: weights not set");
+  for (int i = 0; i < n_steps; ++i)
+    if (!std::isfinite(t_host[i])) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: non-finite time");
+  Dims d = c->base;
+  d.N = n_steps;
+  const size_t mod_f = (size_t)n_steps * d.nmod * 2 * d.D;
+  const int cv_stride = d.L * d.qkv + d.L * 2 * d.F + d.A;
+  const size_t cv_f = (size_t)n_steps * cv_stride;
+  if (n_steps > c->tab_cap) {
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    drop_graphs(c);
+    if (c->tab) hipFree(c->tab);
+    c->tab = nullptr;
+    c->tab_cap = 0;
+    const size_t bytes = align256(mod_f * 4) + align256(cv_f * 4) + align256((size_t)n_steps * 4) * 2 +
+                         align256((size_t)n_steps * d.D * 8);
+    if (hipMalloc(&c->tab, bytes) != hipSuccess) return fail(c, PHYAI_ERR_OOM, "set_timestep_tables: hipMalloc");
+    c->tab_cap = n_steps;
+  }
+  // layout for capacity tab_cap (pointers stay fixed for smaller schedules)
+  const int cap = c->tab_cap;
+  char* p = static_cast<char*>(c->tab);
+  float* mod = reinterpret_cast<float*>(p);
+  p += align256((size_t)cap * d.nmod * 2 * d.D * 4);
+  float* cvec = reinterpret_cast<float*>(p);
+  p += align256((size_t)cap * cv_stride * 4);
+  float* dt = reinterpret_cast<float*>(p);
+  p += align256((size_t)cap * 4);
+  c->t_dev = reinterpret_cast<float*>(p);
+  p += align256((size_t)cap * 4);
+  c->e_dev = reinterpret_cast<double*>(p);
+  // step sizes dt_k = t_{k+1} - t_k with t_N = 0
+  std::vector<float> dth(n_steps);
+  for (int i = 0; i < n_steps; ++i) {
+    const double nxt = (i + 1 < n_steps) ? (double)t_host[i + 1] : 0.0;
+    dth[i] = (float)(nxt - (double)t_host[i]);
+  }
+  HIPCHK(c, hipMemcpyAsync(c->t_dev, t_host, (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipMemcpyAsync(dt, dth.data(), (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
+  c->b.mod = mod;
+  c->b.cvec = cvec;
+  c->b.dt = dt;
+  c->b.cv_stride = cv_stride;
+  c->b.cv_gu_off = d.L * d.qkv;
+  c->b.cv_out_off = d.L * d.qkv + d.L * 2 * d.F;
+  HIPCHK(c, enqueue_tables(d, c->b, c->wt, c->t_dev, c->e_dev, mod, cvec, c->stream));
+  // host buffers above must outlive the async copies
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->n_steps = n_steps;
+  c->have_tables = true;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_set_graph_mode(phyai_ctx* c, int use_graph) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->use_graph = use_graph ? 1 : 0;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_steps, float* out) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!noise || !out) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: null pointer");
+  if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: weights not set");
+  if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: prefix KV not set");
+  if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: timestep tables not set");
+  if (n_steps != c->n_steps) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: n_steps differs from the tables");
+  if (batch != c->batch) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: batch differs from the installed prefix");
+  const Dims d = launch_dims(c, batch, c->prefix_len, n_steps);
+  const Plan plan = make_plan(d, c->wt);
+  const size_t xbytes = (size_t)d.M * d.A * 4;
+  HIPCHK(c, hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  if (c->use_graph) {
+    auto key = std::make_tuple(batch, c->prefix_len, n_steps);
+    auto it = c->graphs.find(key);
+    if (it == c->graphs.end()) {
+      hipGraph_t graph = nullptr;
+      HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+      hipError_t e = enqueue_denoise(d, c->b, plan, c->wt, c->cap_stream);
+      hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+      if (e != hipSuccess || e2 != hipSuccess) {
+        if (graph) hipGraphDestroy(graph);
+        return fail(c, PHYAI_ERR_DEVICE,
+                    std::string("denoise: graph capture failed: ") + hipGetErrorString(e != hipSuccess ? e : e2));
+      }
+      hipGraphExec_t exec = nullptr;
+      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      hipGraphDestroy(graph);
+      if (e != hipSuccess) return fail(c, PHYAI_ERR_DEVICE, std::string("denoise: graph instantiate: ") + hipGetErrorString(e));
+      it = c->graphs.emplace(key, exec).first;
+    }
+    HIPCHK(c, hipGraphLaunch(it->second, c->stream));
+  } else {
+    HIPCHK(c, enqueue_denoise(d, c->b, plan, c->wt, c->stream));
+  }
+  HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
+}
+
+phyai_status phyai_sync(phyai_ctx* c) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  HIPCHK(c, hipGetLastError());
+  return PHYAI_OK;
+}
+
+phyai_status phyai_get_modulation(phyai_ctx* c, float* dst) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!dst) return fail(c, PHYAI_ERR_INVALID_ARG, "get_modulation: null pointer");
+  if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "get_modulation: tables not set");
+  const size_t bytes = (size_t)c->n_steps * c->base.nmod * 2 * c->base.D * 4;
+  HIPCHK(c, hipMemcpyAsync(dst, c->b.mod, bytes, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
+}
+
+void phyai_destroy(phyai_ctx* c) {
+  if (!c) return;
+  hipStreamSynchronize(c->stream);
+  drop_graphs(c);
+  if (c->tab) hipFree(c->tab);
+  if (c->arena) hipFree(c->arena);
+  if (c->cap_stream) hipStreamDestroy(c->cap_stream);
+  delete c;
+}
+
+phyai_status phyai_quantize_int4_g128(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                                      uint16_t* scales, void* hip_stream) {
+  if (rows < 0 || cols < 0 || cols % 128) return PHYAI_ERR_INVALID_ARG;
+  if (rows * cols == 0) return PHYAI_OK;
+  if (!w || !packed || !scales) return PHYAI_ERR_INVALID_ARG;
+  hipError_t e = enqueue_quantize_int4(w, rows, cols, packed, scales, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? PHYAI_OK : PHYAI_ERR_DEVICE;
+}
+
+}  // extern "C"

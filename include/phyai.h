@@ -1,0 +1,166 @@
+/*
+ * phyai.h -- C ABI of the MI355X (gfx950) cached-prefix flow-matching denoise loop.
+ *
+ * What the library computes (pages: "PhyAI: Real-Time Physical AI at the Edge,
+ * Scalable Rollouts in the Cloud", reading Sec. 5.1 and Sec. 5.5; Figure 3):
+ * a pi0.5-style action expert integrates a chunk of noisy action tokens with a
+ * fixed number of explicit Euler steps of its learned velocity.  The
+ * vision-language prefix is fixed during the whole loop, so its per-layer K/V
+ * is handed over once ("cached") and reused by every step; the timestep /
+ * modulation tables of a fixed schedule are precomputed once; a new
+ * observation replaces (invalidates) the prefix before the next prediction.
+ * The runner-like context owns the KV cache, the tables, the buffers and the
+ * captured step graphs, which gives every cached tensor a defined lifetime
+ * (Figure 3 and the Sec. 5.5 "separate request state from computation" item).
+ *
+ * Network of one step (readings of the pages, which print no architecture):
+ *   h  = x W_in^T + b_in
+ *   per layer l:  u = adaRMS(h; norm 2l);   [q|k|v] = u W_qkv[l]^T
+ *                 K = [K_pre[l]; k], V = [V_pre[l]; v]   (chunk sees prefix + chunk)
+ *                 o_i = softmax(q_i K_{i/g}^T / sqrt(dh)) V_{i/g}   (g = Hq/Hkv)
+ *                 h += o W_o[l]^T
+ *                 u = adaRMS(h; norm 2l+1);  h += (gelu_tanh(u W_g^T) * (u W_u^T)) W_d^T
+ *   v  = adaRMS(h; norm 2L) W_out^T + b_out;   x += dt_k v
+ *   adaRMS(h; j) = h / sqrt(mean(h^2) + eps) * (1 + scale_j(t_k)) + shift_j(t_k)
+ *   [scale_j; shift_j](t) = W_mod[j] e(t) + b_mod[j],  e(t) = [sin(2 pi t/p_i) | cos(2 pi t/p_i)],
+ *   p_i = 4e-3 * (4/4e-3)^(i/(D/2-1)).
+ *
+ * Conventions for every entry point:
+ *  - Matrices are row-major, PyTorch Linear layout [out][in]; stacks over layers
+ *    are outermost.  "dev" pointers are HIP device memory, "host" pointers are
+ *    host memory.
+ *  - Every input pointer is borrowed for the duration of the call only: the
+ *    library copies what it keeps into its own device arena (stream-ordered on
+ *    the context stream), so the caller may reuse its buffers afterwards.
+ *  - Argument and state errors are reported synchronously as a status and a
+ *    per-context message (phyai_last_error); the library never aborts.  Device
+ *    errors of asynchronous work surface at the next call or at phyai_sync().
+ *  - A context is not thread-safe; calls on one context must be serialised.
+ */
+#ifndef PHYAI_H
+#define PHYAI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct phyai_ctx phyai_ctx;
+
+typedef enum {
+  PHYAI_OK = 0,
+  PHYAI_ERR_INVALID_ARG = 1,   /* bad pointer, size or dimension */
+  PHYAI_ERR_BAD_STATE = 2,     /* call order violated (e.g. denoise before weights) */
+  PHYAI_ERR_OOM = 3,           /* arena larger than max_arena_bytes or hipMalloc failed */
+  PHYAI_ERR_DEVICE = 4,        /* a HIP runtime call failed */
+  PHYAI_ERR_UNSUPPORTED = 5    /* dimensions the kernels do not implement */
+} phyai_status;
+
+typedef enum {
+  PHYAI_F32 = 0,        /* weights, prefix K/V and activations fp32 */
+  PHYAI_BF16 = 1,       /* weights and prefix K/V bf16; GEMM inputs bf16; fp32 accumulation,
+                           residual stream, norm statistics, softmax and state */
+  PHYAI_INT4_G128 = 2   /* as BF16, but the four expert linears (QKV, O, gate/up, down) are
+                           symmetric int4 with one bf16 scale per 128 consecutive inputs */
+} phyai_dtype;
+
+/* Model and capacity.  Constraints (else PHYAI_ERR_UNSUPPORTED): width, mlp_dim and
+ * n_q_heads*head_dim multiples of 128; head_dim a multiple of 32 and <= 256;
+ * n_q_heads a multiple of n_kv_heads; action_dim <= 256; chunk_len*max_batch <= 64
+ * (the weight-streaming path; larger token counts use the tiled path when built). */
+typedef struct {
+  int n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim;
+  int action_dim, chunk_len, max_prefix_len, max_batch;
+  phyai_dtype weight_dtype;
+  float rms_eps;              /* > 0, e.g. 1e-6 */
+  size_t max_arena_bytes;     /* 0 = no limit; else creation fails with OOM above it */
+} phyai_config;
+
+/* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,
+ * except the four expert linears under PHYAI_INT4_G128, which are packed codes
+ * (uint8 [L][N][K/2]: byte j of a row holds input 2j in its low nibble and 2j+1 in
+ * its high nibble, two's complement) with bf16 scales s_* [L][N][K/128]
+ * (w = code * scale), as written by phyai_quantize_int4_g128.
+ *   w_in [D][A], b_in [D], w_out [A][D], b_out [A]
+ *   w_mod [2L+1][2D][D], b_mod [2L+1][2D]   (rows 0..D-1 scale, D..2D-1 shift; norm j:
+ *                                           2l attention norm, 2l+1 MLP norm, 2L final)
+ *   w_qkv [L][(Hq+2Hkv)*dh][D]  (rows: q heads, then k heads, then v heads)
+ *   w_o [L][D][Hq*dh], w_gu [L][2F][D] (rows 0..F-1 gate, F..2F-1 up), w_d [L][D][F] */
+typedef struct {
+  const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;
+  const void *w_qkv, *w_o, *w_gu, *w_d;
+  const void *s_qkv, *s_o, *s_gu, *s_d;
+} phyai_weights;
+
+/* Create a context on the current HIP device.  hip_stream: the hipStream_t every
+ * call is ordered on (NULL = the null stream).  Allocates the whole device arena
+ * (weights, KV cache for max_batch x (max_prefix_len + chunk_len) keys, buffers) at
+ * once.  *out receives the context, or NULL on error (no message is kept then). */
+phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx** out);
+
+/* Copy the weights (dev pointers, layouts above) into the arena.  Must precede
+ * phyai_set_timestep_tables (the tables fold the weights' response to the shift). */
+phyai_status phyai_set_weights(phyai_ctx* ctx, const phyai_weights* w);
+
+/* Install the cached prefix K/V (PhyAI reading Sec. 5.1: computed once per
+ * observation and reused by every Euler step).  k, v: dev [batch][L][prefix_len][Hkv][dh]
+ * in the weight element type (fp32 or bf16).  Replaces any previous prefix: this
+ * is the cache invalidation point.  1 <= batch <= max_batch,
+ * 1 <= prefix_len <= max_prefix_len. */
+phyai_status phyai_set_prefix_kv(phyai_ctx* ctx, const void* k, const void* v,
+                                 int batch, int prefix_len);
+
+/* Precompute the timestep / modulation tables of a schedule (PhyAI reading
+ * Sec. 5.1: fixed tables over the fixed schedule).  t_host: host float[n_steps], the
+ * times at which the velocity is evaluated; step k advances by dt_k = t_{k+1} - t_k
+ * with t_{n_steps} = 0 (uniform: t_k = 1 - k/N, dt = -1/N).  Requires weights. */
+phyai_status phyai_set_timestep_tables(phyai_ctx* ctx, const float* t_host, int n_steps);
+
+/* Run the whole Euler loop: actions_out = x at t = 0 starting from x = noise at t_0.
+ * noise, actions_out: dev float [batch][chunk_len][action_dim]; batch must equal the
+ * batch of the installed prefix; n_steps must equal the table length.  Asynchronous
+ * on the context stream; the whole loop is one hipGraph launch (captured on first use
+ * for each (batch, prefix_len, n_steps)). */
+phyai_status phyai_denoise(phyai_ctx* ctx, const float* noise, int batch, int n_steps,
+                           float* actions_out);
+
+/* Choose graph replay (1, default) or eager kernel launches (0) for phyai_denoise.
+ * Both run the same kernels in the same order and give bitwise identical results. */
+phyai_status phyai_set_graph_mode(phyai_ctx* ctx, int use_graph);
+
+/* Wait for the context stream; reports asynchronous device errors. */
+phyai_status phyai_sync(phyai_ctx* ctx);
+
+/* Message of the last failed call on ctx ("" if none).  Valid until the next call. */
+const char* phyai_last_error(const phyai_ctx* ctx);
+
+/* Static name of a status code. */
+const char* phyai_status_string(phyai_status s);
+
+/* Free the context and its arena (synchronises its stream first).  NULL is a no-op. */
+void phyai_destroy(phyai_ctx* ctx);
+
+/* Offline round-to-nearest int4 quantiser (PhyAI reading Sec. 5.4 and Figure 3:
+ * the quantizer prepares low-precision artifacts offline).  w: dev float [rows][cols],
+ * cols a multiple of 128.  Per row and group G of 128 columns: s = bf16_rne(max|W_G| / 7)
+ * (fp32 division; s = 0 for an all-zero group), code = clamp(round_half_even(W / s), -8, 7)
+ * (fp32 division; 0 when s = 0).  Writes packed dev uint8 [rows][cols/2] (nibble order as
+ * in phyai_weights) and scales dev uint16 (bf16 bits) [rows][cols/128].  Asynchronous on
+ * hip_stream. */
+phyai_status phyai_quantize_int4_g128(const float* w, int64_t rows, int64_t cols,
+                                      uint8_t* packed, uint16_t* scales, void* hip_stream);
+
+/* Copy the precomputed modulation tables out, for checking: dst dev float
+ * [n_steps][2L+1][2][D] holding (scale, shift) of every norm at every step. */
+phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
+
+/* Library version string. */
+const char* phyai_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PHYAI_H */
