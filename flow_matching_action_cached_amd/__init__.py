@@ -23,6 +23,7 @@ EXPORTED = (
     "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_timestep_tables",
     "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
+    "phyai_enqueue_kernel_repeat",
 )
 
 
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_destroy.restype = None
     lib.phyai_quantize_int4_g128.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
     lib.phyai_get_modulation.argtypes = [vp, vp]
+    lib.phyai_enqueue_kernel_repeat.argtypes = [vp, ci, ci, ci]
     lib.phyai_version.restype = ctypes.c_char_p
     for name in EXPORTED:
         if name not in ("phyai_last_error", "phyai_status_string", "phyai_destroy", "phyai_version"):
@@ -157,6 +159,10 @@ class ActionExpert:
             out = torch.empty_like(noise)
         self._check(self._lib.phyai_denoise(self._h, _ptr(noise), int(noise.shape[0]), self.n_steps, _ptr(out)))
         return out
+
+    def enqueue_kernel_repeat(self, which: int, layer: int, reps: int):
+        """One graph replay of `reps` launches of a single loop kernel (see phyai.h)."""
+        self._check(self._lib.phyai_enqueue_kernel_repeat(self._h, which, layer, reps))
 
     def get_modulation(self):
         import torch

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphyai.so")
 
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "runtime.cpp")]
+SOURCES = [os.path.join(CSRC, "loop_b1.hip"), os.path.join(CSRC, "tables.hip"), os.path.join(CSRC, "runtime.cpp")]
 HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "kernels.h"), os.path.join(INCLUDE, "phyai.h")]
 
 # Packed-fp32 VALU forms are kept out of every code object (they are not needed here and

@@ -63,6 +63,32 @@ __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
   return c;
 }
 
+// ---- fragment-native ("swizzled") matrix layout
+// A matrix X [R][K] (R a multiple of 16, K of 32) is stored block by block: the 16 x 32
+// block (row tile rt = r / 16, k-block kb = k / 32) occupies 64 lanes x 8 contiguous
+// elements, lane = 16 * ((k % 32) / 8) + r % 16 -- exactly the MFMA fragment each lane of
+// a wave holds -- so a wave loads one block with a single contiguous 16 B/lane access.
+// Blocks are ordered row tile major, k-block minor.  Stacks of matrices whose row count is
+// a multiple of 16 are stacks of swizzled matrices.
+__host__ __device__ __forceinline__ size_t sw_idx(int r, int k, int K) {
+  return ((((size_t)(r >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) << 3) +
+         (size_t)(k & 7);
+}
+__device__ __forceinline__ size_t sw_frag(int rt, int kb, int K, int lane) {
+  return (((size_t)rt * (size_t)(K >> 5) + (size_t)kb) * 64 + lane) << 3;
+}
+// int4 weights: per (row tile, 128-wide quad) each lane owns one 16-byte slot whose word j
+// holds its 8 codes of k-block j of the quad.  Inside a word, the offset-binary code
+// (q + 8) of element 2i sits in bits [4i, 4i+4) and that of element 2i+1 in [16+4i, 20+4i).
+__host__ __device__ __forceinline__ size_t sw4_word(int r, int k, int K) {
+  return ((((size_t)(r >> 4) * (size_t)(K >> 7) + (size_t)(k >> 7)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) << 2) +
+         (size_t)((k >> 5) & 3);
+}
+__host__ __device__ __forceinline__ int sw4_shift(int k) {
+  const int e = k & 7;
+  return (e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1);
+}
+
 // fp32 -> storage element (bf16: round to nearest even).
 template <class T> __device__ __forceinline__ T to_elem(float v);
 template <> __device__ __forceinline__ float to_elem<float>(float v) { return v; }
@@ -97,36 +123,59 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
 }
 
-// Split-reduction arrival: every participant calls this after writing its partial.
-// Returns true for exactly one caller (the last to arrive), which may then read all
-// partials.  The counter is reset by that caller, so it is 0 again for the next use.
-// Must be called by all threads of a workgroup (wg = true) or of one wave (wg = false).
-template <bool WG>
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned n_parts, unsigned* lds_flag) {
-  __threadfence();  // release this participant's partial stores at device scope
-  if (WG) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned old = atomicAdd(counter, 1u);
-      bool last = (old == n_parts - 1);
-      if (last) atomicExch(counter, 0u);
-      *lds_flag = last ? 1u : 0u;
-    }
-    __syncthreads();
-    bool last = *lds_flag != 0;
-    if (last) __threadfence();  // acquire the other participants' partials
-    return last;
-  } else {
-    unsigned old = 0;
-    if ((threadIdx.x & 63) == 0) {
-      old = atomicAdd(counter, 1u);
-      if (old == n_parts - 1) atomicExch(counter, 0u);
-    }
-    old = __shfl(old, 0, 64);
-    bool last = (old == n_parts - 1);
-    if (last) __threadfence();
-    return last;
+// ---- cross-workgroup hand-off inside one kernel
+// Partial results that another workgroup reads within the same kernel are written
+// and read with relaxed agent-scope atomics (gfx950: global_store/load ... sc1), which
+// are coherent across the XCDs' separate L2s.  Before a participant signals arrival it
+// waits for its own stores to complete (s_waitcnt 0); the arrival counter is an
+// agent-scope atomic.  This avoids the whole-L2 write-back/invalidate that a
+// device-scope fence costs on this chip.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_agent(float* p, f32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_agent4(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  f32x2 a = __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  f32x2 b = __builtin_bit_cast(f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Arrival of one workgroup (all threads call it) at a split reduction with n_parts
+// participants.  True for exactly the last arrival; that workgroup resets the counter.
+__device__ __forceinline__ bool split_arrive_wg(unsigned* counter, unsigned n_parts, unsigned* lds_flag) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned last = (old == n_parts - 1) ? 1u : 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = last;
   }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+// Same for one wave (all 64 lanes call it).
+__device__ __forceinline__ bool split_arrive_wave(unsigned* counter, unsigned n_parts) {
+  wait_all_mem();
+  unsigned old = 0;
+  if ((threadIdx.x & 63) == 0) {
+    old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == n_parts - 1) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  old = __shfl(old, 0, 64);
+  return old == n_parts - 1;
 }
 
 }  // namespace phyai

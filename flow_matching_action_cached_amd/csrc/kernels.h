@@ -32,8 +32,8 @@ struct Bufs {
   const float* cvec;      // [N][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
   const float* dt;        // [N]
   int cv_stride, cv_gu_off, cv_out_off;
-  float *x, *h, *ssq;     // state [M][A], residual [M][D], row sum-of-squares partials [D/16][Mst]
-  void *hs, *q, *o, *act; // act-typed: [M][D], [M][Hq dh], [M][Hq dh], [M][F]
+  float *x, *h, *ssq;     // state [M][A], residual [M][D], row sum-of-squares partials [Mst][D/16]
+  void *hs, *q, *o, *act; // act-typed: hs [Mpad][D], o [Mpad][Hq dh], act [Mpad][F] swizzled; q [M][Hq dh]
   float* attn_ws; unsigned* attn_cnt;
   float* gemm_ws; unsigned* gemm_cnt;
 };
@@ -54,6 +54,11 @@ Plan make_plan(const Dims& d, WDtype wt);
 // Enqueue the whole Euler loop (N steps) on `stream`.  x must already hold the noise.
 hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t stream);
 
+// Enqueue one launch of loop kernel `which` (0 QKV, 1 attention, 2 O, 3 gate/up, 4 down,
+// 5 out/Euler/in-projection, 6 first in-projection) with the arguments of step k, layer l.
+hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, int which, int k, int l,
+                       hipStream_t stream);
+
 // One-off kernels.
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,
                           float* mod_out, float* cvec_out, hipStream_t stream);
@@ -61,7 +66,8 @@ hipError_t enqueue_install_prefix(const Dims& d, const void* k, const void* v, i
                                   void* kc, void* vt, size_t elem_bytes, hipStream_t stream);
 hipError_t enqueue_quantize_int4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
                                  uint16_t* scales, hipStream_t stream);
-hipError_t enqueue_repack_int4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t cols,
-                               hipStream_t stream);
+// Weight layout conversion at load time (see the swizzled layout in common.h).
+hipError_t enqueue_swizzle(const void* src, void* dst, int64_t rows, int K, size_t elem_bytes, hipStream_t stream);
+hipError_t enqueue_swizzle_int4(const uint8_t* src, uint8_t* dst, int64_t rows, int K, hipStream_t stream);
 
 }  // namespace phyai

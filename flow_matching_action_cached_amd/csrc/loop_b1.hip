@@ -1,0 +1,845 @@
+// Euler-loop kernels for few token rows (batch x chunk <= 64), gfx950.
+//
+// One Euler step (PhyAI reading "PhyAI: Real-Time Physical AI at the Edge,
+// Scalable Rollouts in the Cloud", Sec. 5.1 and 5.5) is, per layer,
+//   k_gemm<QKV>    adaptive-RMSNorm folded in, fused Q|K|V projection, chunk K/V
+//                  written straight into the cache rows after the prefix;
+//   k_attn         split-key flash decode over [cached prefix ; chunk] keys,
+//                  online softmax, deterministic log-sum-exp merge;
+//   k_gemm<RESID>  output projection + residual;
+//   k_gemm<GEGLU>  adaptive-RMSNorm folded in, gate/up projection, gelu(g)*u;
+//   k_gemm<RESID>  down projection + residual;
+// and once per step k_out_euler (final norm, out-projection, x += dt v, and the
+// next step's in-projection).
+//
+// Norm folding.  adaRMS(h) W^T = rinv * ((h * (1 + scale)) W^T) + W shift, with
+// rinv = 1/sqrt(mean(h^2) + eps) per token row.  The producer of h (residual
+// epilogues, in-projection) writes h itself (fp32), hs = h * (1 + scale) in the
+// GEMM input type, and per-16-column partial sums of h^2; the consumer GEMM
+// multiplies its accumulator by rinv and adds the per-step vector W shift, which
+// is precomputed with the timestep tables.  No kernel needs a whole row of h
+// before its matrix product, and the norm costs no extra launch.
+//
+// Weight streaming.  With at most 64 token rows every weight byte is used by
+// only 64 rows, so these linears are bound by reading the weights once from
+// HBM and by latency.  A workgroup owns 16 (or 16 gate + 16 up) output columns
+// and a contiguous share of K; each of its four waves issues every load it will
+// need (weights and activations) before its first MFMA, so one memory round
+// trip covers the whole kernel.  K is walked in "quads" of 128: inside a quad,
+// lane group g (lanes 16g..16g+15) owns k in [32g, 32g+32) -- 64 contiguous bytes
+// of a bf16 row -- and MFMA j of the quad takes k in [32g+8j, 32g+8j+8) from both
+// operands.  Partial sums across waves meet in LDS; across workgroups they meet
+// through agent-scope stores and the last workgroup to arrive adds them in split
+// order, so results never depend on arrival order.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace phyai {
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2 };
+
+struct GemmLaunch {
+  const void* A;             // activations [M][K] (row stride lda)
+  int lda, K;
+  const void* W;             // weights of this layer, [N][K] (int4: repacked codes)
+  const uint16_t* Ws;        // int4 scales of this layer [N][K/128]
+  int n_second;              // row offset of the second weight tile (gate/up: F)
+  int S;                     // k-splits across workgroups
+  int layer;
+  const float* cvec;         // norm-folded bias of this step/layer (QKV, GEGLU)
+  const float* scale_next;   // raw scale of the norm that consumes h (RESID)
+};
+
+// ------------------------------------------------------------------ int4 fragments
+// Swizzled int4 word (8 codes of one lane for one k-block, see sw4_word in common.h):
+// OR-ing a pair of offset-binary codes into 0x4300 (bf16 128.0, whose mantissa step is 1)
+// gives the exact bf16 pair (q + 136, q' + 136); the +136 is removed afterwards with the
+// per-group row sums of the activations.
+__device__ __forceinline__ bf16x8 int4_frag_biased(uint32_t w) {
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// ------------------------------------------------------------------ weight-streaming GEMM
+template <class AT, class WT, int MT, int NT, int KBW, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_GEGLU);
+  constexpr bool INT4 = __is_same(WT, i4);
+  __shared__ f32x4 red[4][NT][MT][64];
+  __shared__ float rinv_s[64];
+  __shared__ unsigned flag;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int s = blockIdx.x % g.S, tile = blockIdx.x / g.S;
+  int nrow[NT];
+  nrow[0] = tile * 16;
+  if (NT == 2) nrow[NT - 1] = g.n_second + tile * 16;
+
+  // this wave's k-blocks: [kbeg, min(kbeg + KBW, kend)), contiguous
+  const int KB = g.K / 32, kbs = KB / g.S;
+  const int kbeg = s * kbs + w * KBW, kend = s * kbs + kbs;
+
+  // ---- 1. loads, in the order their results are needed (vmcnt retires in order):
+  // epilogue operands and norm statistics (L2) first, then per quad the weights (HBM)
+  // and activations (L2).  Addresses are clamped to valid rows/quads instead of
+  // predicating the loads; rows/quads past the end are masked out afterwards.
+  const int mt = w;                            // M-tile this wave finishes in the epilogue
+  float epi_h[4] = {0.f, 0.f, 0.f, 0.f};       // residual rows (RESID)
+  float epi_c0 = 0.f, epi_c1 = 0.f;            // cvec / scale_next of this lane's column(s)
+  if constexpr (EPI == EPI_RESID) {
+    const int col = nrow[0] + r16;
+    epi_c0 = g.scale_next[col];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = min(mt * 16 + grp * 4 + i, d.M - 1);
+      epi_h[i] = bf.h[(size_t)m * d.D + col];
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    epi_c0 = g.cvec[nrow[0] + r16];
+  } else {
+    epi_c0 = g.cvec[nrow[0] + r16];
+    epi_c1 = g.cvec[g.n_second + nrow[0] + r16];
+  }
+  // row statistics: 4 threads per token row, each a quarter of the D/16 partials
+  f32x4 ssv[8];
+  const int srow = min(tid >> 2, d.M - 1), squart = tid & 3;
+  const int n4 = d.D / 256;                    // f32x4 per quarter (D % 256 == 0 here)
+  if constexpr (NORM) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(bf.ssq + (size_t)srow * (d.D / 16) + squart * (d.D / 64));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ssv[j] = p[min(j, n4 - 1)];
+  }
+  // A wave owns exactly KBW k-blocks (the host sizes splits so that every wave is full),
+  // except int4 splits of fewer than four quads, whose surplus waves are idle: the
+  // branch below is uniform and no per-block exit exists that the compiler could sink
+  // the loads behind.
+  const bool wave_active = kbeg < kend;
+  const AT* A = static_cast<const AT*>(g.A);
+  typedef typename FragOf<AT>::type AFrag;
+  AFrag af[KBW][MT];
+  typename FragOf<AT>::type wf[INT4 ? 1 : KBW][INT4 ? 1 : NT];   // fp32 / bf16 weight fragments
+  constexpr int NQW = (INT4 && KBW >= 4) ? KBW / 4 : 1;          // int4 quads per wave (KBW >= 4)
+  u32x4 wq[NQW][NT];                                               // int4: one 16-byte slot per quad
+  float wsc[NQW][NT];
+  if (wave_active) {
+#pragma unroll
+    for (int i = 0; i < KBW; ++i) {
+      const int kb = kbeg + i;
+      if constexpr (!INT4) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          wf[i][nt] = load_frag(static_cast<const WT*>(g.W) + sw_frag(nrow[nt] >> 4, kb, g.K, lane));
+      } else {
+        if ((i & 3) == 0) {
+          const int q = kb >> 2;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            wq[i >> 2][nt] =
+                reinterpret_cast<const u32x4*>(g.W)[((size_t)(nrow[nt] >> 4) * (g.K >> 7) + q) * 64 + lane];
+            wsc[i >> 2][nt] = bf16_bits_to_f32(g.Ws[(size_t)(nrow[nt] + r16) * (g.K >> 7) + q]);
+          }
+        }
+      }
+#pragma unroll
+      for (int mtl = 0; mtl < MT; ++mtl) af[i][mtl] = load_frag(A + sw_frag(mtl, kb, g.K, lane));
+    }
+  }
+  if constexpr (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < n4) {
+        ss += ssv[j][0];
+        ss += ssv[j][1];
+        ss += ssv[j][2];
+        ss += ssv[j][3];
+      }
+    // fixed-order combination of the four quarters of a row
+    const float s1 = __shfl_xor(ss, 1, 64);
+    const float s2 = __shfl_xor(ss, 2, 64);
+    const float s3 = __shfl_xor(ss, 3, 64);
+    float q0, q1, q2, q3;  // quarter 0..3 of this row
+    q0 = squart == 0 ? ss : squart == 1 ? s1 : squart == 2 ? s2 : s3;
+    q1 = squart == 1 ? ss : squart == 0 ? s1 : squart == 3 ? s2 : s3;
+    q2 = squart == 2 ? ss : squart == 3 ? s1 : squart == 0 ? s2 : s3;
+    q3 = squart == 3 ? ss : squart == 2 ? s1 : squart == 1 ? s2 : s3;
+    if (squart == 0 && (tid >> 2) < d.M) rinv_s[tid >> 2] = 1.0f / sqrtf((((q0 + q1) + q2) + q3) / (float)d.D + d.eps);
+  }
+
+  // ---- 2. MFMA
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave_active) {
+    if constexpr (!INT4) {
+#pragma unroll
+      for (int i = 0; i < KBW; ++i)
+#pragma unroll
+        for (int mtl = 0; mtl < MT; ++mtl)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][mtl] = mma(af[i][mtl], wf[i][nt], acc[nt][mtl]);
+    } else {
+      // one 128-wide quad = one scale group: sum(x (q + 136)) - 136 sum(x), times the scale
+      const bf16x8 ones = {(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
+                           (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+#pragma unroll
+      for (int qi = 0; qi < (KBW >= 4 ? KBW / 4 : 0); ++qi) {
+        f32x4 part[NT][MT], rs[MT];
+#pragma unroll
+        for (int mtl = 0; mtl < MT; ++mtl) {
+          rs[mtl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) part[nt][mtl] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mtl = 0; mtl < MT; ++mtl) {
+            const bf16x8 a = af[4 * qi + j][mtl];
+            rs[mtl] = mma(a, ones, rs[mtl]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) part[nt][mtl] = mma(a, int4_frag_biased(wq[qi][nt][j]), part[nt][mtl]);
+          }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int mtl = 0; mtl < MT; ++mtl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[nt][mtl][e] += wsc[qi][nt] * (part[nt][mtl][e] - 136.0f * rs[mtl][e]);
+      }
+    }
+  }
+
+  // ---- 3. cross-wave reduction in a fixed order; wave w then owns M-tile w
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[w][nt][mt][lane] = acc[nt][mt];
+  __syncthreads();
+  f32x4 tot[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tot[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mt < MT) {
+      f32x4 v = red[0][nt][mt][lane];
+      v += red[1][nt][mt][lane];
+      v += red[2][nt][mt][lane];
+      v += red[3][nt][mt][lane];
+      tot[nt] = v;
+    }
+  }
+
+  // ---- 4. cross-workgroup split: the last arrival sums the partials in split order
+  if (g.S > 1) {
+    const size_t part_floats = (size_t)NT * MT * 256;
+    float* base = bf.gemm_ws + (size_t)tile * g.S * part_floats;
+    if (mt < MT)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st_agent(base + s * part_floats + ((nt * MT + mt) * 64 + lane) * 4, tot[nt]);
+    if (!split_arrive_wg(bf.gemm_cnt + tile, (unsigned)g.S, &flag)) return;
+    if (mt < MT) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 parts[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+          parts[s2] = ld_agent4(base + min(s2, g.S - 1) * part_floats + ((nt * MT + mt) * 64 + lane) * 4);
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+          if (s2 < g.S) sum += (s2 == s) ? tot[nt] : parts[s2];
+        tot[nt] = sum;
+      }
+    }
+  }
+  if (mt >= MT) return;
+
+  // ---- 5. epilogues.  tot[nt][i] is row mt*16 + 4*grp + i, column nrow[nt] + r16.
+  if constexpr (EPI == EPI_QKV) {
+    const int col = nrow[0] + r16;
+    const float c = epi_c0;
+    const int qd = d.Hq * d.dh, kd = d.Hkv * d.dh;
+    AT* q = static_cast<AT*>(bf.q);
+    AT* kc = static_cast<AT*>(bf.kc);
+    AT* vt = static_cast<AT*>(bf.vt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + grp * 4 + i;
+      if (m >= d.M) continue;
+      const float y = rinv_s[m] * tot[0][i] + c;
+      const int b = m / d.H, t = m % d.H;
+      if (col < qd) {
+        q[(size_t)m * qd + col] = to_elem<AT>(y);
+      } else if (col < qd + kd) {
+        const int r = (col - qd) / d.dh, dd = (col - qd) % d.dh;
+        kc[((((size_t)b * d.L + g.layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
+      } else {
+        const int r = (col - qd - kd) / d.dh, dd = (col - qd - kd) % d.dh;
+        vt[((((size_t)b * d.L + g.layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const int col = nrow[0] + r16;
+    const float sc1 = 1.0f + epi_c0;
+    AT* hs = static_cast<AT*>(bf.hs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + grp * 4 + i;
+      float hn = 0.f;
+      if (m < d.M) {
+        hn = epi_h[i] + tot[0][i];
+        bf.h[(size_t)m * d.D + col] = hn;
+        hs[sw_idx(m, col, d.D)] = to_elem<AT>(hn * sc1);
+      }
+      const float sq = sum16(hn * hn);
+      if (r16 == 0 && m < d.M) bf.ssq[(size_t)m * (d.D / 16) + tile] = sq;
+    }
+  } else {  // EPI_GEGLU
+    const int f = nrow[0] + r16;
+    const float cg = epi_c0, cu = epi_c1;
+    AT* act = static_cast<AT*>(bf.act);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + grp * 4 + i;
+      if (m >= d.M) continue;
+      const float yg = rinv_s[m] * tot[0][i] + cg;
+      const float yu = rinv_s[m] * tot[NT - 1][i] + cu;
+      act[sw_idx(m, f, d.F)] = to_elem<AT>(gelu_tanh(yg) * yu);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// Split-key flash decode.  The query rows of one KV head r are the g*H pairs
+// (query head r*g + j, chunk token t), row j*H + t, in 16-row tiles; the keys are
+// the P cached prefix rows followed by the H chunk rows (no mask among them).
+// A workgroup owns (sample, KV head, 4 query tiles, key split); its 256 threads
+// stage each 32-key block of K and V^T in LDS (the next block is loaded into
+// registers while the current one is used), and each wave runs one query tile:
+// S^T = K q^T and O^T += V^T P^T on MFMA, so the softmax probabilities come out
+// of the first product already laid out as the second product's B operand.  V is
+// kept transposed in the cache for the same reason.  Splits are merged with
+// log-sum-exp weights in split order by the last wave to finish.
+template <class AT, int DH>
+__global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
+  typedef typename FragOf<AT>::type Frag;
+  constexpr int ES = sizeof(AT);
+  constexpr int PK = 16 / ES;                       // K row pad (16 B)
+  constexpr int PV = 4;                             // V^T row pad (4 elements)
+  constexpr int KROW = DH + PK, VROW = 32 + PV;
+  constexpr int KCH = 32 * DH * ES / 16;            // 16-byte chunks of one K block
+  constexpr int CPT = 2 * KCH / 256;                // chunks per thread (K and V)
+  static_assert(CPT >= 1 && (2 * KCH) % 256 == 0, "block size");
+  __shared__ __attribute__((aligned(16))) AT ks[32 * KROW];
+  __shared__ __attribute__((aligned(16))) AT vs[DH * VROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int gq = d.Hq / d.Hkv;
+  const int QT = (gq * d.H + 15) / 16, QG = (QT + 3) / 4;
+  int idx = blockIdx.x;
+  const int s = idx % S;
+  idx /= S;
+  const int qg = idx % QG;
+  idx /= QG;
+  const int r = idx % d.Hkv;
+  const int b = idx / d.Hkv;
+  const int qt = qg * 4 + w;
+  const bool active = qt < QT;
+  const int T = d.P + d.H;
+  const int nblk = (T + 31) / 32;
+  const int blk0 = s * bps, blk1 = min(nblk, blk0 + bps);
+
+  const int qrow = qt * 16 + r16;
+  const bool qvalid = active && qrow < gq * d.H;
+  const int head = r * gq + (qvalid ? qrow / d.H : 0);
+  const int tok = qvalid ? qrow % d.H : 0;
+  const int m = b * d.H + tok;
+  const int qd = d.Hq * DH;
+
+  const size_t kvbase = ((size_t)b * d.L + layer) * d.Hkv + r;
+  const AT* Kc = static_cast<const AT*>(bf.kc) + kvbase * d.KS * DH;
+  const AT* Vt = static_cast<const AT*>(bf.vt) + kvbase * DH * d.KS;
+
+  // staged copy of one block: chunk c < KCH is K (row c / (DH*ES/16)), else V^T (row (c-KCH) / 4)
+  u32x4 stage[CPT];
+  auto fetch = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const char* src;
+      if (c < KCH) {
+        constexpr int CPR = DH * ES / 16;  // chunks per K row
+        src = reinterpret_cast<const char*>(Kc + (size_t)(blk * 32 + c / CPR) * DH) + (c % CPR) * 16;
+      } else {
+        const int cv = c - KCH;
+        constexpr int CPRV = 32 * ES / 16;  // chunks per V^T row of one block
+        src = reinterpret_cast<const char*>(Vt + (size_t)(cv / CPRV) * d.KS + blk * 32) + (cv % CPRV) * 16;
+      }
+      stage[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      char* dst;
+      if (c < KCH) {
+        constexpr int CPR = DH * ES / 16;
+        dst = reinterpret_cast<char*>(ks + (c / CPR) * KROW) + (c % CPR) * 16;
+      } else {
+        const int cv = c - KCH;
+        constexpr int CPRV = 32 * ES / 16;
+        dst = reinterpret_cast<char*>(vs + (cv / CPRV) * VROW) + (cv % CPRV) * 16;
+      }
+      // V^T rows are 8-byte aligned only (pad of 4 elements): store as two halves
+      const u32x4 v = stage[i];
+      reinterpret_cast<u32x2*>(dst)[0] = u32x2{v[0], v[1]};
+      reinterpret_cast<u32x2*>(dst)[1] = u32x2{v[2], v[3]};
+    }
+  };
+
+  Frag qf[DH / 32];
+  {
+    const AT* qp = static_cast<const AT*>(bf.q) + (size_t)m * qd + head * DH + grp * 8;
+#pragma unroll
+    for (int j = 0; j < DH / 32; ++j) qf[j] = qvalid ? load_frag(qp + 32 * j) : zero_frag<AT>();
+  }
+  fetch(blk0);
+
+  const float sc = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[DH / 16];
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int blk = blk0; blk < blk1; ++blk) {
+    __syncthreads();
+    commit();
+    __syncthreads();
+    if (blk + 1 < blk1) fetch(blk + 1);
+    if (!active) continue;
+    const int kb = blk * 32;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < DH / 32; ++j) {
+      s0 = mma(load_frag(ks + r16 * KROW + 32 * j + grp * 8), qf[j], s0);
+      s1 = mma(load_frag(ks + (16 + r16) * KROW + 32 * j + grp * 8), qf[j], s1);
+    }
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + grp * 4 + i;
+      v[i] = key < T ? s0[i] * sc : -INFINITY;
+      v[4 + i] = key + 16 < T ? s1[i] * sc : -INFINITY;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, v[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2f(v[e] - m_new);
+      ps += p[e];
+    }
+    l_part = l_part * alpha + ps;
+    m_run = m_new;
+    Frag pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = to_elem<AT>(p[e]);
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) {
+      o[t] *= alpha;
+      const AT* vp = vs + (t * 16 + r16) * VROW + grp * 4;
+      o[t] = mma(load_frag_split4(vp, vp + 16), pf, o[t]);
+    }
+  }
+  if (!active) return;
+  float l_row = l_part;
+  l_row += __shfl_xor(l_row, 16, 64);
+  l_row += __shfl_xor(l_row, 32, 64);
+
+  if (S > 1) {
+    // Partial of this split: (m, l) in fp32 and O / l in the activation type (bf16 halves
+    // the hand-off; fp32 workloads keep fp32).  Every split, the merging one included,
+    // enters the merge through the stored (rounded) value, so the result does not depend
+    // on which split finishes last.
+    constexpr int PW = (DH / 16) * 64 * (ES == 2 ? 2 : 4);  // payload floats
+    const size_t item = ((size_t)(b * d.Hkv + r) * QT + qt);
+    const size_t stride = (size_t)PW + 32;
+    float* base = bf.attn_ws + item * S * stride;
+    float* mine = base + s * stride;
+    const float inv_l = 1.0f / l_row;
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) {
+      const f32x4 v = o[t] * inv_l;
+      if constexpr (ES == 2) {
+        const bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(mine) + t * 64 + lane, __builtin_bit_cast(uint64_t, pk),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        st_agent(mine + (t * 64 + lane) * 4, v);
+      }
+    }
+    if (grp == 0) {
+      st_agent(mine + PW + r16, m_run);
+      st_agent(mine + PW + 16 + r16, l_row);
+    }
+    if (!split_arrive_wave(bf.attn_cnt + item, (unsigned)S)) return;
+    float ms[8], ls[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const float* p2 = base + min(s2, S - 1) * stride;
+      ms[s2] = ld_agent(p2 + PW + r16);
+      ls[s2] = ld_agent(p2 + PW + 16 + r16);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if (s2 < S) M = fmaxf(M, ms[s2]);
+    float wgt[8], den = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      wgt[s2] = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+      den += wgt[s2];
+    }
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h2 = 0; h2 < 8; h2 += 4) {
+      if (h2 >= S) break;
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float* p2 = base + min(h2 + u, S - 1) * stride;
+          if constexpr (ES == 2) {
+            const bf16x4 pk = __builtin_bit_cast(
+                bf16x4, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p2) + t * 64 + lane, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT));
+            v[u] = f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+          } else {
+            v[u] = ld_agent4(p2 + (t * 64 + lane) * 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[t] += wgt[h2 + u] * v[u];
+      }
+    }
+    l_row = den;
+  }
+  if (!qvalid) return;
+  const float inv = 1.0f / l_row;
+  // o is the A operand of the output projection: swizzled [Mpad][Hq*dh].  The four values
+  // of (t, i = 0..3) are consecutive columns inside one 8-wide lane slot.
+  AT* op = static_cast<AT*>(bf.o);
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) {
+    AT* dst = op + sw_idx(m, head * DH + t * 16 + grp * 4, qd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(o[t][i] * inv);
+  }
+}
+
+// ------------------------------------------------------------------ out-projection + Euler + in-projection
+// One workgroup per token row.  k_prev >= 0: final adaptive norm of step k_prev,
+// v = rinv (hs W_out^T) + W_out shift + b_out, x += dt v.  k_next >= 0: in-projection
+// h = x W_in^T + b_in for step k_next, writing h, hs = h * (1 + scale) of that step's
+// first norm, and the row's sum-of-squares partials.  Loads are 16-byte vectors at
+// clamped addresses, issued before any of them is consumed.
+template <class AT, class IOT>
+__global__ __launch_bounds__(256) void k_out_euler(Dims d, Bufs bf, int k_prev, int k_next) {
+  typedef typename FragOf<AT>::type AF;    // 8 activations
+  typedef typename FragOf<IOT>::type WF;   // 8 weights
+  __shared__ float xs[256];
+  __shared__ float vres[256];
+  __shared__ float wred[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = blockIdx.x;
+  if (k_prev >= 0) {
+    const int n16 = d.D / 16;
+    float ss = 0.f;
+    if (w == 0) {
+      const float a0 = bf.ssq[(size_t)m * n16 + min(lane, n16 - 1)];
+      const float a1 = bf.ssq[(size_t)m * n16 + min(lane + 64, n16 - 1)];
+      ss = (lane < n16 ? a0 : 0.f) + (lane + 64 < n16 ? a1 : 0.f);
+    }
+    // hs chunks of this lane: k = lane*8 + 512*j (8 consecutive k are contiguous when swizzled)
+    const AT* hsr = static_cast<const AT*>(bf.hs);
+    const IOT* wo = static_cast<const IOT*>(bf.w_out);
+    AF hv[4];
+    float hmask[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = lane * 8 + 512 * j;
+      hmask[j] = k < d.D ? 1.f : 0.f;
+      hv[j] = load_frag(hsr + sw_idx(m, min(k, d.D - 8), d.D));
+    }
+    for (int a0 = w; a0 < d.A; a0 += 32) {  // 8 outputs (a0, a0+4, ...) per pass
+      WF wv[8][4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int a = min(a0 + 4 * u, d.A - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wv[u][j] = load_frag(wo + (size_t)a * d.D + min(lane * 8 + 512 * j, d.D - 8));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part += to_f32(hv[j][e]) * to_f32(wv[u][j][e]);
+          acc += hmask[j] * part;
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && a0 + 4 * u < d.A) vres[a0 + 4 * u] = acc;
+      }
+    }
+    if (w == 0) {
+      ss = wave_sum(ss);
+      if (lane == 0) wred[0] = ss;
+    }
+    __syncthreads();
+    const float rinv = 1.0f / sqrtf(wred[0] / (float)d.D + d.eps);
+    for (int a = tid; a < d.A; a += 256) {
+      const IOT* bo = static_cast<const IOT*>(bf.b_out);
+      const float* cv = bf.cvec + (size_t)k_prev * bf.cv_stride + bf.cv_out_off;
+      const float v = rinv * vres[a] + cv[a] + to_f32(bo[a]);
+      const float xn = bf.x[(size_t)m * d.A + a] + bf.dt[k_prev] * v;
+      bf.x[(size_t)m * d.A + a] = xn;
+      xs[a] = xn;
+    }
+    __syncthreads();
+  } else {
+    for (int a = tid; a < d.A; a += 256) xs[a] = bf.x[(size_t)m * d.A + a];
+    __syncthreads();
+  }
+  if (k_next < 0) return;
+  const IOT* wi = static_cast<const IOT*>(bf.w_in);
+  const IOT* bi = static_cast<const IOT*>(bf.b_in);
+  const float* scl = bf.mod + (size_t)k_next * d.nmod * 2 * d.D;  // norm 0, scale row
+  AT* hs = static_cast<AT*>(bf.hs);
+  const int na = d.A / 8;
+  for (int n0 = 0; n0 < d.D; n0 += 256) {
+    const int n = n0 + tid;  // D % 256 == 0: every thread has a column
+    const IOT* wr = wi + (size_t)n * d.A;
+    float hn = to_f32(bi[n]);
+    const float sc1 = 1.0f + scl[n];
+    for (int c0 = 0; c0 < na; c0 += 8) {
+      WF wv[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) wv[c] = load_frag(wr + 8 * min(c0 + c, na - 1));
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c0 + c < na)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hn += xs[8 * (c0 + c) + e] * to_f32(wv[c][e]);
+    }
+    bf.h[(size_t)m * d.D + n] = hn;
+    hs[sw_idx(m, n, d.D)] = to_elem<AT>(hn * sc1);
+    const float sq = sum16(hn * hn);
+    if ((tid & 15) == 0) bf.ssq[(size_t)m * (d.D / 16) + n / 16] = sq;
+  }
+}
+
+// ================================================================== host side
+size_t attn_counters(const Dims& d) {
+  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
+  return (size_t)d.B * d.Hkv * QT;
+}
+size_t attn_ws_floats(const Dims& d, const Plan& p) {
+  const int T = d.P + d.H, nblk = (T + 31) / 32;
+  const int S = (nblk + p.attn_bps - 1) / p.attn_bps;
+  return attn_counters(d) * S * ((size_t)(d.dh / 16) * 256 + 32);
+}
+size_t gemm_counters(const Dims& d) {
+  size_t n = d.qkv / 16;
+  if ((size_t)d.D / 16 > n) n = d.D / 16;
+  if ((size_t)d.F / 16 > n) n = d.F / 16;
+  return n;
+}
+size_t gemm_ws_floats(const Dims& d, const Plan& p) {
+  const int MT = (d.M + 15) / 16;
+  size_t n = 0;
+  auto upd = [&](size_t tiles, int S, int NT) {
+    if (S > 1) n = std::max(n, tiles * S * NT * MT * 256);
+  };
+  upd(d.qkv / 16, p.s_qkv, 1);
+  upd(d.D / 16, p.s_o, 1);
+  upd(d.F / 16, p.s_gu, 2);
+  upd(d.D / 16, p.s_d, 1);
+  return n;
+}
+
+// Splits across workgroups for a linear with K inputs and `tiles` 16-column tiles: a
+// power of two dividing the K/128 quads (int4 waves own whole quads), at most 32 k-blocks
+// per split (8 per wave), and enough workgroups to cover the 256 CUs when possible.
+static int pick_split(int K, int tiles) {
+  const int nq = K / 128;
+  int S = 1;
+  while (S < 8 && nq % (2 * S) == 0 && (nq / S > 8 || tiles * S < 256)) S *= 2;
+  return S;
+}
+
+Plan make_plan(const Dims& d, WDtype wt) {
+  (void)wt;
+  Plan p;
+  p.s_qkv = pick_split(d.D, d.qkv / 16);
+  p.s_o = pick_split(d.Hq * d.dh, d.D / 16);
+  p.s_gu = pick_split(d.D, d.F / 16);
+  p.s_d = pick_split(d.F, d.D / 16);
+  // about four 32-key blocks per split
+  const int T = d.P + d.H, nblk = (T + 31) / 32;
+  p.attn_bps = nblk < 4 ? nblk : 4;
+  return p;
+}
+
+template <class AT, class WT, int EPI, int NT, int MT>
+static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& g, int tiles, hipStream_t st) {
+  const int kbs = g.K / 32 / g.S;        // k-blocks per split (a multiple of 4), shared by 4 waves
+  // every wave owns exactly kbw k-blocks; int4 waves own whole 128-wide quads (one scale
+  // group each), so splits of fewer than four quads leave the surplus waves idle
+  const int qps = kbs / 4;
+  const int kbw = __is_same(WT, i4) ? (qps >= 4 ? qps : 4) : qps;
+  if (__is_same(WT, i4) && qps > 4 && qps % 4) return hipErrorInvalidValue;
+  dim3 grid(tiles * g.S), block(256);
+  switch (kbw) {
+    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, d, b, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, d, b, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, d, b, g); break;
+    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, d, b, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class AT, class WT, int EPI, int NT>
+static hipError_t launch_gemm(const Dims& d, const Bufs& b, const GemmLaunch& g, int tiles, hipStream_t st) {
+  switch ((d.M + 15) / 16) {
+    case 1: return launch_gemm_q<AT, WT, EPI, NT, 1>(d, b, g, tiles, st);
+    case 2: return launch_gemm_q<AT, WT, EPI, NT, 2>(d, b, g, tiles, st);
+    case 3: return launch_gemm_q<AT, WT, EPI, NT, 3>(d, b, g, tiles, st);
+    case 4: return launch_gemm_q<AT, WT, EPI, NT, 4>(d, b, g, tiles, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class AT>
+static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int layer, hipStream_t st) {
+  const int T = d.P + d.H, nblk = (T + 31) / 32;
+  const int S = (nblk + p.attn_bps - 1) / p.attn_bps;
+  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16, QG = (QT + 3) / 4;
+  dim3 grid(d.B * d.Hkv * QG * S), block(256);
+  switch (d.dh) {
+    case 32: hipLaunchKernelGGL((k_attn<AT, 32>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+    case 64: hipLaunchKernelGGL((k_attn<AT, 64>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+    case 128: hipLaunchKernelGGL((k_attn<AT, 128>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+    case 256: hipLaunchKernelGGL((k_attn<AT, 256>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class T> static size_t wbytes_row(int K);
+template <> size_t wbytes_row<float>(int K) { return (size_t)K * 4; }
+template <> size_t wbytes_row<bf16>(int K) { return (size_t)K * 2; }
+template <> size_t wbytes_row<i4>(int K) { return (size_t)K / 2; }
+
+// One launch of kernel `which` for (step k, layer l).  Kinds: 0 QKV, 1 attention,
+// 2 O + residual, 3 gate/up GeGLU, 4 down + residual, 5 out-projection/Euler/in-projection
+// (layer ignored), 6 in-projection of step 0 (layer ignored).
+template <class AT, class WT, class IOT>
+static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
+                             hipStream_t st) {
+  const int qd = d.Hq * d.dh;
+  const float* cv = b.cvec + (size_t)k * b.cv_stride;
+  GemmLaunch g{};
+  g.layer = l;
+  switch (which) {
+    case 0:
+      g.A = b.hs; g.lda = d.D; g.K = d.D;
+      g.W = static_cast<const char*>(b.w_qkv) + wbytes_row<WT>(d.D) * d.qkv * l;
+      g.Ws = b.s_qkv ? b.s_qkv + (size_t)l * d.qkv * (d.D / 128) : nullptr;
+      g.S = p.s_qkv; g.cvec = cv + (size_t)l * d.qkv;
+      return launch_gemm<AT, WT, EPI_QKV, 1>(d, b, g, d.qkv / 16, st);
+    case 1:
+      return launch_attn<AT>(d, b, p, l, st);
+    case 2:  // consumer of h is the MLP norm 2l+1
+      g.A = b.o; g.lda = qd; g.K = qd;
+      g.W = static_cast<const char*>(b.w_o) + wbytes_row<WT>(qd) * d.D * l;
+      g.Ws = b.s_o ? b.s_o + (size_t)l * d.D * (qd / 128) : nullptr;
+      g.S = p.s_o; g.scale_next = b.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D;
+      return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
+    case 3:
+      g.A = b.hs; g.lda = d.D; g.K = d.D;
+      g.W = static_cast<const char*>(b.w_gu) + wbytes_row<WT>(d.D) * 2 * d.F * l;
+      g.Ws = b.s_gu ? b.s_gu + (size_t)l * 2 * d.F * (d.D / 128) : nullptr;
+      g.n_second = d.F; g.S = p.s_gu; g.cvec = cv + b.cv_gu_off + (size_t)l * 2 * d.F;
+      return launch_gemm<AT, WT, EPI_GEGLU, 2>(d, b, g, d.F / 16, st);
+    case 4: {  // consumer of h is norm 2(l+1), or the final norm 2L
+      g.A = b.act; g.lda = d.F; g.K = d.F;
+      g.W = static_cast<const char*>(b.w_d) + wbytes_row<WT>(d.F) * d.D * l;
+      g.Ws = b.s_d ? b.s_d + (size_t)l * d.D * (d.F / 128) : nullptr;
+      g.S = p.s_d;
+      const int jn = (l + 1 < d.L) ? 2 * (l + 1) : 2 * d.L;
+      g.scale_next = b.mod + (((size_t)k * d.nmod + jn) * 2) * d.D;
+      return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
+    }
+    case 5:
+      hipLaunchKernelGGL((k_out_euler<AT, IOT>), dim3(d.M), dim3(256), 0, st, d, b, k, k + 1 < d.N ? k + 1 : -1);
+      return hipGetLastError();
+    case 6:
+      hipLaunchKernelGGL((k_out_euler<AT, IOT>), dim3(d.M), dim3(256), 0, st, d, b, -1, 0);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class AT, class WT, class IOT>
+static hipError_t denoise_impl(const Dims& d, const Bufs& b, const Plan& p, hipStream_t st) {
+  hipError_t e = launch_one<AT, WT, IOT>(d, b, p, 6, 0, 0, st);
+  for (int k = 0; k < d.N && e == hipSuccess; ++k) {
+    for (int l = 0; l < d.L && e == hipSuccess; ++l)
+      for (int which = 0; which < 5 && e == hipSuccess; ++which) e = launch_one<AT, WT, IOT>(d, b, p, which, k, l, st);
+    if (e == hipSuccess) e = launch_one<AT, WT, IOT>(d, b, p, 5, k, 0, st);
+  }
+  return e;
+}
+
+hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, int which, int k, int l,
+                       hipStream_t st) {
+  switch (wt) {
+    case W_F32: return launch_one<float, float, float>(d, b, p, which, k, l, st);
+    case W_BF16: return launch_one<bf16, bf16, bf16>(d, b, p, which, k, l, st);
+    case W_INT4: return launch_one<bf16, i4, bf16>(d, b, p, which, k, l, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t st) {
+  switch (wt) {
+    case W_F32: return denoise_impl<float, float, float>(d, b, p, st);
+    case W_BF16: return denoise_impl<bf16, bf16, bf16>(d, b, p, st);
+    case W_INT4: return denoise_impl<bf16, i4, bf16>(d, b, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace phyai

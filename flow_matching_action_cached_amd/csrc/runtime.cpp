@@ -43,6 +43,8 @@ struct phyai_ctx {
   int batch = 0, prefix_len = 0, n_steps = 0;
   int use_graph = 1;
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
+  // single-kernel repeat graphs for measurement: (which, layer, reps, batch, prefix, steps)
+  std::map<std::tuple<int, int, int, int, int, int>, hipGraphExec_t> kgraphs;
 };
 
 namespace {
@@ -75,6 +77,8 @@ size_t wrow_bytes(WDtype wt, int K) { return wt == W_F32 ? (size_t)K * 4 : wt ==
 void drop_graphs(phyai_ctx* c) {
   for (auto& kv : c->graphs) hipGraphExecDestroy(kv.second);
   c->graphs.clear();
+  for (auto& kv : c->kgraphs) hipGraphExecDestroy(kv.second);
+  c->kgraphs.clear();
 }
 
 Dims launch_dims(const phyai_ctx* c, int batch, int prefix_len, int n_steps) {
@@ -116,8 +120,9 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
     return PHYAI_ERR_INVALID_ARG;
   if (g.weight_dtype != PHYAI_F32 && g.weight_dtype != PHYAI_BF16 && g.weight_dtype != PHYAI_INT4_G128)
     return PHYAI_ERR_INVALID_ARG;
-  if (g.width % 128 || g.mlp_dim % 128 || (g.n_q_heads * g.head_dim) % 128 || g.head_dim % 32 ||
-      g.head_dim > 256 || g.n_q_heads % g.n_kv_heads || g.action_dim > 256 || g.chunk_len * g.max_batch > 64)
+  if (g.width % 256 || g.width > 2048 || g.mlp_dim % 128 || (g.n_q_heads * g.head_dim) % 128 ||
+      g.head_dim % 32 || g.head_dim > 256 || g.n_q_heads % g.n_kv_heads || g.action_dim > 256 ||
+      g.action_dim % 8 || g.chunk_len * g.max_batch > 64)
     return PHYAI_ERR_UNSUPPORTED;
   if (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) return PHYAI_ERR_UNSUPPORTED;
 
@@ -165,8 +170,9 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   const size_t zero_begin = o_kc;
   const size_t o_x = lay.take((size_t)d.M * A * 4), o_h = lay.take((size_t)d.M * D * 4);
   const size_t o_ssq = lay.take((size_t)(D / 16) * d.Mst * 4);
-  const size_t o_hs = lay.take((size_t)d.M * D * c->es_act), o_q = lay.take((size_t)d.M * qd * c->es_act);
-  const size_t o_o = lay.take((size_t)d.M * qd * c->es_act), o_act = lay.take((size_t)d.M * F * c->es_act);
+  const size_t mpad = (size_t)(d.M + 15) / 16 * 16;  // swizzled activations hold whole 16-row tiles
+  const size_t o_hs = lay.take(mpad * D * c->es_act), o_q = lay.take((size_t)d.M * qd * c->es_act);
+  const size_t o_o = lay.take(mpad * qd * c->es_act), o_act = lay.take(mpad * F * c->es_act);
   // scratch for split reductions: upper bounds over every batch / prefix length
   const int nblk_max = (d.P + d.H + 31) / 32;
   const size_t attn_ws = attn_counters(d) * nblk_max * ((size_t)(d.dh / 16) * 256 + 32);
@@ -241,15 +247,19 @@ phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
   HIPCHK(c, cp(c->b.b_out, w->b_out, (size_t)A * e));
   HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * 2 * D * D * e));
   HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * 2 * D * e));
+  // expert linears: re-laid out into the fragment-native (swizzled) layout the kernels stream
   if (c->wt != W_INT4) {
-    HIPCHK(c, cp(c->b.w_qkv, w->w_qkv, wrow_bytes(c->wt, D) * d.qkv * L));
-    HIPCHK(c, cp(c->b.w_o, w->w_o, wrow_bytes(c->wt, qd) * D * L));
-    HIPCHK(c, cp(c->b.w_gu, w->w_gu, wrow_bytes(c->wt, D) * 2 * F * L));
-    HIPCHK(c, cp(c->b.w_d, w->w_d, wrow_bytes(c->wt, F) * D * L));
+    auto sw = [&](const void* dst, const void* src, int64_t rows, int cols) {
+      return enqueue_swizzle(src, const_cast<void*>(dst), rows, cols, e, c->stream);
+    };
+    HIPCHK(c, sw(c->b.w_qkv, w->w_qkv, (int64_t)L * d.qkv, D));
+    HIPCHK(c, sw(c->b.w_o, w->w_o, (int64_t)L * D, qd));
+    HIPCHK(c, sw(c->b.w_gu, w->w_gu, (int64_t)L * 2 * F, D));
+    HIPCHK(c, sw(c->b.w_d, w->w_d, (int64_t)L * D, F));
   } else {
-    auto rp = [&](const void* dst, const void* src, int64_t rows, int64_t cols) {
-      return enqueue_repack_int4(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(const_cast<void*>(dst)),
-                                 rows, cols, c->stream);
+    auto rp = [&](const void* dst, const void* src, int64_t rows, int cols) {
+      return enqueue_swizzle_int4(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(const_cast<void*>(dst)),
+                                  rows, cols, c->stream);
     };
     HIPCHK(c, rp(c->b.w_qkv, w->w_qkv, (int64_t)L * d.qkv, D));
     HIPCHK(c, rp(c->b.w_o, w->w_o, (int64_t)L * D, qd));
@@ -381,6 +391,38 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
     HIPCHK(c, enqueue_denoise(d, c->b, plan, c->wt, c->stream));
   }
   HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
+}
+
+phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int reps) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (which < 0 || which > 6 || reps < 1 || reps > 100000 || layer < 0 || layer >= c->base.L)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "enqueue_kernel_repeat: bad kernel id, layer or reps");
+  if (!c->have_weights || !c->have_prefix || !c->have_tables)
+    return fail(c, PHYAI_ERR_BAD_STATE, "enqueue_kernel_repeat: weights, prefix and tables must be set");
+  const Dims d = launch_dims(c, c->batch, c->prefix_len, c->n_steps);
+  const Plan plan = make_plan(d, c->wt);
+  auto key = std::make_tuple(which, layer, reps, c->batch, c->prefix_len, c->n_steps);
+  auto it = c->kgraphs.find(key);
+  if (it == c->kgraphs.end()) {
+    hipGraph_t graph = nullptr;
+    HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < reps && e == hipSuccess; ++i) e = enqueue_one(d, c->b, plan, c->wt, which, 0, layer, c->cap_stream);
+    hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+    if (e != hipSuccess || e2 != hipSuccess) {
+      if (graph) hipGraphDestroy(graph);
+      return fail(c, PHYAI_ERR_DEVICE, std::string("enqueue_kernel_repeat: capture failed: ") +
+                                           hipGetErrorString(e != hipSuccess ? e : e2));
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(c, PHYAI_ERR_DEVICE, std::string("enqueue_kernel_repeat: instantiate: ") + hipGetErrorString(e));
+    it = c->kgraphs.emplace(key, exec).first;
+  }
+  HIPCHK(c, hipGraphLaunch(it->second, c->stream));
   return PHYAI_OK;
 }
 

@@ -1,0 +1,282 @@
+// One-off kernels (outside the Euler loop): timestep embedding and modulation
+// tables, the norm-folded shift projections, prefix K/V installation, and the
+// offline int4 quantiser / repacker.
+//
+// Tables (PhyAI reading "PhyAI: Real-Time Physical AI at the Edge, Scalable
+// Rollouts in the Cloud", Sec. 5.1: timestep/modulation tables over the fixed
+// schedule are precomputed once) are computed in fp64 and stored as fp32.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace phyai {
+
+// Scalar weight read for the table kernels.  Expert linears are stored swizzled (see
+// common.h); the in/out projections are plain row-major.
+template <class WT, bool SW> struct WRow {
+  const WT* w;
+  const uint16_t* s;
+  int K;
+  __device__ float at(size_t n, int k) const {
+    return SW ? to_f32(w[sw_idx((int)n, k, K)]) : to_f32(w[n * K + k]);
+  }
+};
+template <bool SW> struct WRow<i4, SW> {
+  const i4* w;
+  const uint16_t* s;
+  int K;
+  __device__ float at(size_t n, int k) const {
+    const uint32_t word = reinterpret_cast<const uint32_t*>(w)[sw4_word((int)n, k, K)];
+    const int q = (int)((word >> sw4_shift(k)) & 0xFu) - 8;
+    return (float)q * bf16_bits_to_f32(s[n * (K / 128) + k / 128]);
+  }
+};
+
+// ------------------------------------------------------------------ timestep / modulation tables
+// Embedding e(t_k) in fp64: e_i = sin(2 pi t / p_i), e_{D/2+i} = cos(2 pi t / p_i),
+// p_i = 4e-3 * 1000^(i / (D/2 - 1)).
+__global__ void k_embed(const float* t, int N, int D, double* e) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * D) return;
+  const int k = idx / D, c = idx % D, half = D / 2;
+  const int i = c % half;
+  const double period = 4e-3 * pow(1000.0, (double)i / (double)(half - 1));
+  const double ang = 2.0 * M_PI * (double)t[k] / period;
+  e[idx] = c < half ? sin(ang) : cos(ang);
+}
+
+// One wave per row o of W_mod[j] (j = norm, o in [0, 2D)): m_k = W_mod[j][o] . e(t_k) + b_mod[j][o]
+// for every step k, accumulated in fp64.
+template <class IOT>
+__global__ __launch_bounds__(256) void k_modulation(const IOT* w_mod, const IOT* b_mod, const double* e,
+                                                    int N, int nmod, int D, float* mod) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nmod * 2 * D) return;
+  const int j = row / (2 * D), o = row % (2 * D);
+  const IOT* wr = w_mod + (size_t)row * D;
+  const double bias = (double)to_f32(b_mod[row]);
+  for (int k0 = 0; k0 < N; k0 += 8) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = lane; c < D; c += 64) {
+      const double wv = (double)to_f32(wr[c]);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        if (k0 + kk < N) acc[kk] += wv * e[(size_t)(k0 + kk) * D + c];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const double v = wave_sum(acc[kk]);
+      if (lane == 0 && k0 + kk < N)
+        mod[(((size_t)(k0 + kk) * nmod + j) * 2 + (o >= D ? 1 : 0)) * D + (o % D)] = (float)(v + bias);
+    }
+  }
+}
+
+// Norm-folded biases: for every step k, c = W shift_j(t_k) for the QKV rows (j = 2l),
+// the gate/up rows (j = 2l+1) and the out-projection rows (j = 2L).  One wave per row.
+template <class WT, class IOT>
+__global__ __launch_bounds__(256) void k_shift_proj(Dims d, Bufs bf, const float* mod, float* cvec) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nq = d.L * d.qkv, ng = d.L * 2 * d.F;
+  if (row >= nq + ng + d.A) return;
+  int j, off;
+  WRow<WT, true> wq{static_cast<const WT*>(bf.w_qkv), bf.s_qkv, d.D};
+  WRow<WT, true> wg{static_cast<const WT*>(bf.w_gu), bf.s_gu, d.D};
+  WRow<IOT, false> wo{static_cast<const IOT*>(bf.w_out), nullptr, d.D};
+  int which;
+  size_t n;
+  if (row < nq) {
+    which = 0; n = row; j = 2 * (row / d.qkv); off = row;
+  } else if (row < nq + ng) {
+    which = 1; n = row - nq; j = 2 * ((row - nq) / (2 * d.F)) + 1; off = bf.cv_gu_off + (row - nq);
+  } else {
+    which = 2; n = row - nq - ng; j = 2 * d.L; off = bf.cv_out_off + (row - nq - ng);
+  }
+  for (int k0 = 0; k0 < d.N; k0 += 8) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = lane; c < d.D; c += 64) {
+      const double wv = which == 0 ? wq.at(n, c) : which == 1 ? wg.at(n, c) : wo.at(n, c);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        if (k0 + kk < d.N) acc[kk] += wv * (double)mod[(((size_t)(k0 + kk) * d.nmod + j) * 2 + 1) * d.D + c];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const double v = wave_sum(acc[kk]);
+      if (lane == 0 && k0 + kk < d.N) cvec[(size_t)(k0 + kk) * bf.cv_stride + off] = (float)v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefix install
+// K [B][L][P][Hkv][dh] -> cache [b][l][r][p][dh];  V -> V^T cache [b][l][r][dh][p].
+template <class T>
+__global__ void k_install_prefix(Dims d, const T* k, const T* v, int B, int P, T* kc, T* vt) {
+  const size_t total = (size_t)B * d.L * d.Hkv * d.dh * P;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    // V^T write order: p fastest
+    size_t rem = idx;
+    const int p = rem % P; rem /= P;
+    const int dd = rem % d.dh; rem /= d.dh;
+    const int r = rem % d.Hkv; rem /= d.Hkv;
+    const int l = rem % d.L;
+    const int b = rem / d.L;
+    const size_t src = ((((size_t)b * d.L + l) * P + p) * d.Hkv + r) * d.dh + dd;
+    const size_t cb = ((size_t)b * d.L + l) * d.Hkv + r;
+    vt[(cb * d.dh + dd) * d.KS + p] = v[src];
+    // K with dh fastest: reuse the same index space transposed
+    const int dd2 = idx % d.dh;
+    size_t rem2 = idx / d.dh;
+    const int p2 = rem2 % P;
+    rem2 /= P;
+    const size_t cb2 = rem2;  // (b*L + l)*Hkv + r
+    const int r2 = cb2 % d.Hkv;
+    const size_t bl2 = cb2 / d.Hkv;
+    kc[(cb2 * d.KS + p2) * d.dh + dd2] = k[((bl2 * P + p2) * d.Hkv + r2) * d.dh + dd2];
+  }
+}
+
+// ------------------------------------------------------------------ int4 quantiser and repack
+// One wave per (row, 128-column group); lane i quantises columns 2i, 2i+1 and writes one byte.
+__global__ __launch_bounds__(256) void k_quantize_int4(const float* w, int64_t rows, int64_t cols,
+                                                       uint8_t* packed, uint16_t* scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t ng = cols / 128;
+  if (item >= rows * ng) return;
+  const int64_t row = item / ng, gi = item % ng;
+  const float* src = w + row * cols + gi * 128 + 2 * lane;
+  const float a = src[0], b = src[1];
+  float mx = fmaxf(fabsf(a), fabsf(b));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float s32 = mx / 7.0f;
+  // bf16 round to nearest even of s32
+  uint32_t u = __builtin_bit_cast(uint32_t, s32);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const float s = __builtin_bit_cast(float, u << 16);
+  int qa = 0, qb = 0;
+  if (s > 0.f) {
+    qa = (int)fminf(fmaxf(rintf(a / s), -8.f), 7.f);
+    qb = (int)fminf(fmaxf(rintf(b / s), -8.f), 7.f);
+  }
+  packed[row * (cols / 2) + gi * 64 + lane] = (uint8_t)((qa & 0xF) | ((qb & 0xF) << 4));
+  if (lane == 0) scales[row * ng + gi] = (uint16_t)u;
+}
+
+// Row-major [rows][K] -> swizzled layout (rows a multiple of 16).  One thread per element.
+template <class T>
+__global__ void k_swizzle(const T* src, T* dst, int64_t rows, int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * K) return;
+  const int64_t r = i / K;
+  const int k = (int)(i % K);
+  // rows are handled 16 at a time (r >> 4 < 2^31 for any arena that fits the device)
+  dst[(size_t)(r >> 4) * 16 * K + sw_idx((int)(r & 15), k, K)] = src[i];
+}
+
+// ABI int4 (byte j of a row: input 2j in the low nibble, 2j+1 in the high nibble, two's
+// complement) -> swizzled words (sw4_word / sw4_shift, offset binary).  One thread per word.
+__global__ void k_swizzle_int4(const uint8_t* src, uint32_t* dst, int64_t rows, int K) {
+  const int64_t words = rows * (K / 8);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= words) return;
+  // decode the word index: [row tile][quad][lane = g*16 + r16][j]
+  const int64_t per_tile = (int64_t)(K / 128) * 64 * 4;
+  const int64_t rt = i / per_tile;
+  int64_t rem = i % per_tile;
+  const int q = (int)(rem / 256);
+  rem %= 256;
+  const int lane = (int)(rem / 4), j = (int)(rem % 4);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t row = rt * 16 + r16;
+  const int k0 = q * 128 + j * 32 + g * 8;
+  const uint8_t* b = src + row * (K / 2) + k0 / 2;
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t nib = ((e & 1) ? (b[e >> 1] >> 4) : b[e >> 1]) & 0xFu;
+    out |= (nib ^ 0x8u) << sw4_shift(k0 + e);
+  }
+  dst[i] = out;
+}
+
+// ================================================================== host side
+template <class WT, class IOT>
+static hipError_t tables_impl(const Dims& d, const Bufs& b, const float* t_dev, double* e, float* mod,
+                              float* cvec, hipStream_t st) {
+  const int ne = d.N * d.D;
+  hipLaunchKernelGGL(k_embed, dim3((ne + 255) / 256), dim3(256), 0, st, t_dev, d.N, d.D, e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int rows = d.nmod * 2 * d.D;
+  hipLaunchKernelGGL((k_modulation<IOT>), dim3((rows + 3) / 4), dim3(256), 0, st,
+                     static_cast<const IOT*>(b.w_mod), static_cast<const IOT*>(b.b_mod), e, d.N, d.nmod, d.D, mod);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int rows2 = d.L * d.qkv + d.L * 2 * d.F + d.A;
+  hipLaunchKernelGGL((k_shift_proj<WT, IOT>), dim3((rows2 + 3) / 4), dim3(256), 0, st, d, b, mod, cvec);
+  return hipGetLastError();
+}
+
+hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e,
+                          float* mod, float* cvec, hipStream_t st) {
+  switch (wt) {
+    case W_F32: return tables_impl<float, float>(d, b, t_dev, e, mod, cvec, st);
+    case W_BF16: return tables_impl<bf16, bf16>(d, b, t_dev, e, mod, cvec, st);
+    case W_INT4: return tables_impl<i4, bf16>(d, b, t_dev, e, mod, cvec, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue_install_prefix(const Dims& d, const void* k, const void* v, int batch, int P, void* kc,
+                                  void* vt, size_t es, hipStream_t st) {
+  const size_t total = (size_t)batch * d.L * d.Hkv * d.dh * P;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  if (es == 4)
+    hipLaunchKernelGGL(k_install_prefix<float>, dim3(blocks), dim3(256), 0, st, d, static_cast<const float*>(k),
+                       static_cast<const float*>(v), batch, P, static_cast<float*>(kc), static_cast<float*>(vt));
+  else
+    hipLaunchKernelGGL(k_install_prefix<uint16_t>, dim3(blocks), dim3(256), 0, st, d,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), batch, P,
+                       static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vt));
+  return hipGetLastError();
+}
+
+hipError_t enqueue_quantize_int4(const float* w, int64_t rows, int64_t cols, uint8_t* packed, uint16_t* scales,
+                                 hipStream_t st) {
+  const int64_t items = rows * (cols / 128);
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_int4, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, w, rows, cols, packed,
+                     scales);
+  return hipGetLastError();
+}
+
+hipError_t enqueue_swizzle(const void* src, void* dst, int64_t rows, int K, size_t es, hipStream_t st) {
+  const int64_t n = rows * K;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (es == 4)
+    hipLaunchKernelGGL(k_swizzle<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(src),
+                       static_cast<float*>(dst), rows, K);
+  else
+    hipLaunchKernelGGL(k_swizzle<uint16_t>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                       static_cast<uint16_t*>(dst), rows, K);
+  return hipGetLastError();
+}
+
+hipError_t enqueue_swizzle_int4(const uint8_t* src, uint8_t* dst, int64_t rows, int K, hipStream_t st) {
+  const int64_t words = rows * (K / 8);
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swizzle_int4, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st, src,
+                     reinterpret_cast<uint32_t*>(dst), rows, K);
+  return hipGetLastError();
+}
+
+}  // namespace phyai

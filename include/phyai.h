@@ -66,10 +66,10 @@ typedef enum {
                            symmetric int4 with one bf16 scale per 128 consecutive inputs */
 } phyai_dtype;
 
-/* Model and capacity.  Constraints (else PHYAI_ERR_UNSUPPORTED): width, mlp_dim and
- * n_q_heads*head_dim multiples of 128; head_dim a multiple of 32 and <= 256;
- * n_q_heads a multiple of n_kv_heads; action_dim <= 256; chunk_len*max_batch <= 64
- * (the weight-streaming path; larger token counts use the tiled path when built). */
+/* Model and capacity.  Constraints (else PHYAI_ERR_UNSUPPORTED): width a multiple of 256
+ * and <= 2048; mlp_dim and n_q_heads*head_dim multiples of 128; head_dim 32, 64, 128 or
+ * 256; n_q_heads a multiple of n_kv_heads; action_dim a multiple of 8 and <= 256;
+ * chunk_len * max_batch <= 64 (the weight-streaming path for few token rows). */
 typedef struct {
   int n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim;
   int action_dim, chunk_len, max_prefix_len, max_batch;
@@ -155,6 +155,15 @@ phyai_status phyai_quantize_int4_g128(const float* w, int64_t rows, int64_t cols
 /* Copy the precomputed modulation tables out, for checking: dst dev float
  * [n_steps][2L+1][2][D] holding (scale, shift) of every norm at every step. */
 phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
+
+/* Measurement aid: enqueue on the context stream one graph replay of `reps` back-to-back
+ * launches of a single kernel of the loop, with the arguments it has at step 0 and layer
+ * `layer`.  which: 0 norm-folded QKV (+ chunk K/V into the cache), 1 attention, 2 O-projection
+ * + residual, 3 gate/up + GeGLU, 4 down-projection + residual, 5 out-projection + Euler +
+ * in-projection, 6 first in-projection.  Requires weights, prefix and tables.  The caller
+ * brackets the call with events on the same stream to time one kernel in isolation.  It
+ * overwrites the context's activations, state and chunk K/V rows (re-run phyai_denoise after). */
+phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, int reps);
 
 /* Library version string. */
 const char* phyai_version(void);

@@ -63,7 +63,9 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(n_layers=0))[0] == 1
     assert _create(lib, _cfg(rms_eps=0.0))[0] == 1
     assert _create(lib, _cfg(weight_dtype=7))[0] == 1
-    assert _create(lib, _cfg(width=200))[0] == 5          # not a multiple of 128
+    assert _create(lib, _cfg(width=200))[0] == 5          # not a multiple of 256
+    assert _create(lib, _cfg(width=384))[0] == 5
+    assert _create(lib, _cfg(action_dim=6))[0] == 5
     assert _create(lib, _cfg(head_dim=48))[0] == 5
     assert _create(lib, _cfg(n_q_heads=3, n_kv_heads=2))[0] == 5
     assert _create(lib, _cfg(chunk_len=50, max_batch=2))[0] == 5   # beyond the streaming path
