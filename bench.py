@@ -58,6 +58,18 @@ def chunk_bytes(d):
     return d.n_steps * (d.n_layers * per_layer + io + kv + tables)
 
 
+def chunk_bytes_int4(d):
+    """Per chunk: N x (int4 codes + bf16 scales of the expert linears, bf16 in/out
+    projections, prefix K/V, tables)."""
+    per_layer = d.qkv_dim * d.width + d.width * d.n_q_heads * d.head_dim + 3 * d.mlp_dim * d.width
+    codes = d.n_layers * per_layer // 2
+    scales = d.n_layers * per_layer // 128 * 2
+    io = 2 * d.action_dim * d.width * 2
+    kv = 2 * d.n_layers * d.prefix_len * d.n_kv_heads * d.head_dim * 2
+    tables = d.n_mod * 2 * d.width * 4
+    return d.n_steps * (codes + scales + io + kv + tables)
+
+
 def schedule(n):
     import numpy as np
     dt = -1.0 / n
@@ -96,6 +108,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the loop runs on a single MI355X; --gpus {args.gpus} "
@@ -165,10 +178,43 @@ def main():
     ach = abytes[dominant] / (per_launch_us[dominant] * 1e-6) / 1e9
     print(f"[bench] isolated kernels (us/launch): {per_launch_us}", file=sys.stderr, flush=True)
 
-    # parity spot check of the benchmarked output (first element against a fresh run)
     ex.denoise(noise, out)
     torch.cuda.synchronize()
     finite = bool(torch.isfinite(out).all().item())
+    ex.close()
+
+    # int4 group-128 variant of the same workload (expert linears quantised by the library)
+    variants = {}
+    if not args.no_variants:
+        d4 = synth.CONFIGS["pi05_int4"]
+        inp4 = synth.make_expert_inputs(d4, 0)
+        w4 = {}
+        for k in ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod"):
+            w4[k] = w[k]
+        for k in ("w_qkv", "w_o", "w_gu", "w_d"):
+            p_, s_ = fm.quantize_int4_g128(torch.from_numpy(inp4[k]).cuda())
+            w4[k], w4["s" + k[1:]] = p_, s_
+        del inp4
+        e4 = fm.ActionExpert.from_dims(d4)
+        e4.set_weights(w4)
+        e4.set_prefix_kv(kp, vp)
+        e4.set_timestep_tables(schedule(d.n_steps))
+        for _ in range(args.warmup):
+            e4.denoise(noise, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            e4.denoise(noise, out)
+        b.record()
+        torch.cuda.synchronize()
+        ms4 = a.elapsed_time(b) / args.steps
+        e4.close()
+        b4 = chunk_bytes_int4(d)
+        variants["int4_g128_batch1"] = {"ms_per_chunk": round(ms4, 4), "chunks_per_s": round(1000.0 / ms4, 2),
+                                        "algorithmic_bytes": b4,
+                                        "hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] int4 variant: {ms4:.4f} ms/chunk", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -204,9 +250,9 @@ def main():
                      "algorithmic_bytes_per_launch": abytes[dominant],
                      "avg_launch_us": round(per_launch_us[dominant], 3)},
         "output_finite": finite,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
-    ex.close()
     print(json.dumps(line), flush=True)
 
 

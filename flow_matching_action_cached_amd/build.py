@@ -31,15 +31,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libphyai.so next to this file."""
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    """Compile every source for gfx950 and link libphyai.so next to this file.
+
+    phase_trace=True builds libphyai_trace.so instead: the same library with per-wave phase
+    timestamps recorded by the kernels (exported reader: phyai_phase_trace)."""
     cc = hipcc()
     objs = []
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build_trace" if phase_trace else "_build")
+    lib = LIB.replace("libphyai.so", "libphyai_trace.so") if phase_trace else LIB
+    extra = ["-DPHYAI_PHASE_TRACE"] if phase_trace else []
     os.makedirs(objdir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [cc, *GPU_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [cc, *GPU_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         if verbose:
@@ -48,16 +53,16 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_trace="--phase-trace" in sys.argv))

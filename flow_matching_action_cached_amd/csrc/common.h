@@ -18,6 +18,21 @@
 
 namespace phyai {
 
+// Optional per-phase timestamps (a build with -DPHYAI_PHASE_TRACE only): each wave's lane 0
+// stores the 100 MHz real-time counter at numbered points of a kernel into
+// g_phase_trace[(workgroup * 4 + wave) * 8 + slot]; phyai_phase_trace() copies it out.
+#ifdef PHYAI_PHASE_TRACE
+extern __device__ uint64_t g_phase_trace[4096 * 4 * 8];
+#define PHASE_MARK(slot)                                                                          \
+  do {                                                                                            \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < 4096)                                             \
+      g_phase_trace[((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (slot)] =                 \
+          __builtin_amdgcn_s_memrealtime();                                                       \
+  } while (0)
+#else
+#define PHASE_MARK(slot) ((void)0)
+#endif
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -149,6 +164,18 @@ __device__ __forceinline__ void st_agent(float* p, float v) {
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte agent-scope accesses through a raw buffer resource (buffer_load/store ... sc1):
+// same coherence as the atomics above, four times the width of a 64-bit atomic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t agent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
+}
+__device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 16);
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 

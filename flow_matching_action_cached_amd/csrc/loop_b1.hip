@@ -40,6 +40,10 @@
 
 namespace phyai {
 
+#ifdef PHYAI_PHASE_TRACE
+__device__ uint64_t g_phase_trace[4096 * 4 * 8];
+#endif
+
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2 };
 
 struct GemmLaunch {
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
   nrow[0] = tile * 16;
   if (NT == 2) nrow[NT - 1] = g.n_second + tile * 16;
 
+  PHASE_MARK(0);
   // this wave's k-blocks: [kbeg, min(kbeg + KBW, kend)), contiguous
   const int KB = g.K / 32, kbs = KB / g.S;
   const int kbeg = s * kbs + w * KBW, kend = s * kbs + kbs;
@@ -152,6 +157,8 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
       for (int mtl = 0; mtl < MT; ++mtl) af[i][mtl] = load_frag(A + sw_frag(mtl, kb, g.K, lane));
     }
   }
+  // keep every load above in flight together: nothing below may be scheduled before them
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (NORM) {
     float ss = 0.f;
 #pragma unroll
@@ -174,6 +181,7 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
     if (squart == 0 && (tid >> 2) < d.M) rinv_s[tid >> 2] = 1.0f / sqrtf((((q0 + q1) + q2) + q3) / (float)d.D + d.eps);
   }
 
+  PHASE_MARK(1);
   // ---- 2. MFMA
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -220,6 +228,7 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
     }
   }
 
+  PHASE_MARK(2);
   // ---- 3. cross-wave reduction in a fixed order; wave w then owns M-tile w
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -239,21 +248,25 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
     }
   }
 
+  PHASE_MARK(3);
   // ---- 4. cross-workgroup split: the last arrival sums the partials in split order
   if (g.S > 1) {
-    const size_t part_floats = (size_t)NT * MT * 256;
-    float* base = bf.gemm_ws + (size_t)tile * g.S * part_floats;
+    const uint32_t part_bytes = (uint32_t)NT * MT * 1024;
+    const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.gemm_ws + (size_t)tile * g.S * NT * MT * 256, part_bytes * g.S);
     if (mt < MT)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) st_agent(base + s * part_floats + ((nt * MT + mt) * 64 + lane) * 4, tot[nt]);
-    if (!split_arrive_wg(bf.gemm_cnt + tile, (unsigned)g.S, &flag)) return;
+      for (int nt = 0; nt < NT; ++nt) st_agent16(ws, s * part_bytes + ((nt * MT + mt) * 64 + lane) * 16, tot[nt]);
+    PHASE_MARK(4);
+    const bool last = split_arrive_wg(bf.gemm_cnt + tile, (unsigned)g.S, &flag);
+    PHASE_MARK(5);
+    if (!last) return;
     if (mt < MT) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4 parts[8];
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
-          parts[s2] = ld_agent4(base + min(s2, g.S - 1) * part_floats + ((nt * MT + mt) * 64 + lane) * 4);
+          parts[s2] = ld_agent16(ws, min(s2, g.S - 1) * part_bytes + ((nt * MT + mt) * 64 + lane) * 16);
         f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
@@ -262,6 +275,7 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
       }
     }
   }
+  PHASE_MARK(6);
   if (mt >= MT) return;
 
   // ---- 5. epilogues.  tot[nt][i] is row mt*16 + 4*grp + i, column nrow[nt] + r16.
@@ -317,33 +331,39 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
       act[sw_idx(m, f, d.F)] = to_elem<AT>(gelu_tanh(yg) * yu);
     }
   }
+  PHASE_MARK(7);
 }
 
 // ------------------------------------------------------------------ attention
 // Split-key flash decode.  The query rows of one KV head r are the g*H pairs
 // (query head r*g + j, chunk token t), row j*H + t, in 16-row tiles; the keys are
 // the P cached prefix rows followed by the H chunk rows (no mask among them).
-// A workgroup owns (sample, KV head, 4 query tiles, key split); its 256 threads
-// stage each 32-key block of K and V^T in LDS (the next block is loaded into
-// registers while the current one is used), and each wave runs one query tile:
-// S^T = K q^T and O^T += V^T P^T on MFMA, so the softmax probabilities come out
-// of the first product already laid out as the second product's B operand.  V is
-// kept transposed in the cache for the same reason.  Splits are merged with
-// log-sum-exp weights in split order by the last wave to finish.
+// A workgroup owns (sample, KV head, 4 query tiles, key split).  Its 256 threads stage
+// the split's keys -- up to NB blocks of 32 at once -- as K and V^T tiles in LDS with one
+// burst of loads, and each wave runs one query tile over them: S^T = K q^T on MFMA, a
+// direct softmax over the staged keys (online rescaling only between groups of NB
+// blocks), then O^T += V^T P^T on MFMA.  The probabilities come out of the first product
+// already laid out as the second product's B operand, which is why V is kept transposed
+// in the cache.  Splits are merged with log-sum-exp weights in split order by the last
+// wave to finish.
 template <class AT, int DH>
 __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
   typedef typename FragOf<AT>::type Frag;
+  constexpr int NB = DH * sizeof(AT) <= 512 ? 4 : 2;  // 32-key blocks staged per group (LDS <= 160 KB)
+  constexpr int NK = NB * 32;
   constexpr int ES = sizeof(AT);
-  constexpr int PK = 16 / ES;                       // K row pad (16 B)
-  constexpr int PV = 4;                             // V^T row pad (4 elements)
-  constexpr int KROW = DH + PK, VROW = 32 + PV;
-  constexpr int KCH = 32 * DH * ES / 16;            // 16-byte chunks of one K block
-  constexpr int CPT = 2 * KCH / 256;                // chunks per thread (K and V)
-  static_assert(CPT >= 1 && (2 * KCH) % 256 == 0, "block size");
-  __shared__ __attribute__((aligned(16))) AT ks[32 * KROW];
+  constexpr int KROW = DH + 16 / ES;                 // K row: DH + 16 B pad
+  constexpr int VROW = NK + 16 / ES;                 // V^T row: NK keys + 16 B pad
+  constexpr int KCPR = DH * ES / 16;                 // 16-byte chunks per K row
+  constexpr int VCPR = NK * ES / 16;                 // 16-byte chunks per staged V^T row
+  constexpr int KCH = NK * KCPR, VCH = DH * VCPR;    // chunks of one group
+  constexpr int CPT = (KCH + VCH) / 256;             // chunks per thread
+  static_assert((KCH + VCH) % 256 == 0, "group size");
+  __shared__ __attribute__((aligned(16))) AT ks[NK * KROW];
   __shared__ __attribute__((aligned(16))) AT vs[DH * VROW];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = d.Hq / d.Hkv;
   const int QT = (gq * d.H + 15) / 16, QG = (QT + 3) / 4;
   int idx = blockIdx.x;
@@ -358,6 +378,7 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   const int T = d.P + d.H;
   const int nblk = (T + 31) / 32;
   const int blk0 = s * bps, blk1 = min(nblk, blk0 + bps);
+  const int kend = min(T, blk1 * 32);                // keys of this split: [blk0*32, kend)
 
   const int qrow = qt * 16 + r16;
   const bool qvalid = active && qrow < gq * d.H;
@@ -370,51 +391,13 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   const AT* Kc = static_cast<const AT*>(bf.kc) + kvbase * d.KS * DH;
   const AT* Vt = static_cast<const AT*>(bf.vt) + kvbase * DH * d.KS;
 
-  // staged copy of one block: chunk c < KCH is K (row c / (DH*ES/16)), else V^T (row (c-KCH) / 4)
-  u32x4 stage[CPT];
-  auto fetch = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const char* src;
-      if (c < KCH) {
-        constexpr int CPR = DH * ES / 16;  // chunks per K row
-        src = reinterpret_cast<const char*>(Kc + (size_t)(blk * 32 + c / CPR) * DH) + (c % CPR) * 16;
-      } else {
-        const int cv = c - KCH;
-        constexpr int CPRV = 32 * ES / 16;  // chunks per V^T row of one block
-        src = reinterpret_cast<const char*>(Vt + (size_t)(cv / CPRV) * d.KS + blk * 32) + (cv % CPRV) * 16;
-      }
-      stage[i] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      char* dst;
-      if (c < KCH) {
-        constexpr int CPR = DH * ES / 16;
-        dst = reinterpret_cast<char*>(ks + (c / CPR) * KROW) + (c % CPR) * 16;
-      } else {
-        const int cv = c - KCH;
-        constexpr int CPRV = 32 * ES / 16;
-        dst = reinterpret_cast<char*>(vs + (cv / CPRV) * VROW) + (cv % CPRV) * 16;
-      }
-      // V^T rows are 8-byte aligned only (pad of 4 elements): store as two halves
-      const u32x4 v = stage[i];
-      reinterpret_cast<u32x2*>(dst)[0] = u32x2{v[0], v[1]};
-      reinterpret_cast<u32x2*>(dst)[1] = u32x2{v[2], v[3]};
-    }
-  };
-
+  PHASE_MARK(0);
   Frag qf[DH / 32];
   {
     const AT* qp = static_cast<const AT*>(bf.q) + (size_t)m * qd + head * DH + grp * 8;
 #pragma unroll
-    for (int j = 0; j < DH / 32; ++j) qf[j] = qvalid ? load_frag(qp + 32 * j) : zero_frag<AT>();
+    for (int j = 0; j < DH / 32; ++j) qf[j] = load_frag(qp + 32 * j);
   }
-  fetch(blk0);
 
   const float sc = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
   float m_run = -INFINITY, l_part = 0.f;
@@ -422,51 +405,86 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
 #pragma unroll
   for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int blk = blk0; blk < blk1; ++blk) {
+  for (int g0 = blk0; g0 < blk1; g0 += NB) {
+    const int glast = min(blk1, g0 + NB) - 1;          // last block of this group
+    // ---- one burst of loads for the whole group (blocks past the split are clamped to
+    // its last block: their keys are masked below), then into LDS
+    u32x4 stage[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const char* src;
+      if (c < KCH) {
+        const int row = c / KCPR;                        // staged key row 0..NK-1
+        const int blk = min(g0 + row / 32, glast);
+        src = reinterpret_cast<const char*>(Kc + (size_t)(blk * 32 + row % 32) * DH) + (c % KCPR) * 16;
+      } else {
+        const int cv = c - KCH;
+        const int row = cv / VCPR;                       // dh row
+        const int kofs = (cv % VCPR) * (16 / ES);        // staged key offset 0..NK-1
+        const int blk = min(g0 + kofs / 32, glast);
+        src = reinterpret_cast<const char*>(Vt + (size_t)row * d.KS + blk * 32 + kofs % 32);
+      }
+      stage[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    __syncthreads();                                     // previous group's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      AT* dst = c < KCH ? ks + (c / KCPR) * KROW + (c % KCPR) * (16 / ES)
+                        : vs + ((c - KCH) / VCPR) * VROW + ((c - KCH) % VCPR) * (16 / ES);
+      *reinterpret_cast<u32x4*>(dst) = stage[i];
+    }
     __syncthreads();
-    commit();
-    __syncthreads();
-    if (blk + 1 < blk1) fetch(blk + 1);
+    if (g0 == blk0) PHASE_MARK(1);
     if (!active) continue;
-    const int kb = blk * 32;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- scores of the group, masked past the split
+    float sv[NB][8];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < DH / 32; ++j) {
-      s0 = mma(load_frag(ks + r16 * KROW + 32 * j + grp * 8), qf[j], s0);
-      s1 = mma(load_frag(ks + (16 + r16) * KROW + 32 * j + grp * 8), qf[j], s1);
+    for (int j = 0; j < NB; ++j) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      if (g0 + j <= glast) {
+#pragma unroll
+        for (int jj = 0; jj < DH / 32; ++jj) {
+          s0 = mma(load_frag(ks + (j * 32 + r16) * KROW + 32 * jj + grp * 8), qf[jj], s0);
+          s1 = mma(load_frag(ks + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8), qf[jj], s1);
+        }
+      }
+      const int kb = (g0 + j) * 32 + grp * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[j][i] = kb + i < kend ? s0[i] * sc : -INFINITY;
+        sv[j][4 + i] = kb + 16 + i < kend ? s1[i] * sc : -INFINITY;
+        mx = fmaxf(mx, fmaxf(sv[j][i], sv[j][4 + i]));
+      }
     }
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + grp * 4 + i;
-      v[i] = key < T ? s0[i] * sc : -INFINITY;
-      v[4 + i] = key + 16 < T ? s1[i] * sc : -INFINITY;
-    }
-    float mx = v[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, v[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = exp2f(m_run - m_new);
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(v[e] - m_new);
-      ps += p[e];
-    }
-    l_part = l_part * alpha + ps;
+    l_part *= alpha;
     m_run = m_new;
-    Frag pf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = to_elem<AT>(p[e]);
+    for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t) {
-      o[t] *= alpha;
-      const AT* vp = vs + (t * 16 + r16) * VROW + grp * 4;
-      o[t] = mma(load_frag_split4(vp, vp + 16), pf, o[t]);
+    for (int j = 0; j < NB; ++j) {
+      if (g0 + j > glast) break;
+      Frag pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(sv[j][e] - m_new);
+        l_part += p;
+        pf[e] = to_elem<AT>(p);
+      }
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t) {
+        const AT* vp = vs + (t * 16 + r16) * VROW + j * 32 + grp * 4;
+        o[t] = mma(load_frag_split4(vp, vp + 16), pf, o[t]);
+      }
     }
   }
+  PHASE_MARK(2);
   if (!active) return;
   float l_row = l_part;
   l_row += __shfl_xor(l_row, 16, 64);
@@ -474,37 +492,41 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
 
   if (S > 1) {
     // Partial of this split: (m, l) in fp32 and O / l in the activation type (bf16 halves
-    // the hand-off; fp32 workloads keep fp32).  Every split, the merging one included,
-    // enters the merge through the stored (rounded) value, so the result does not depend
-    // on which split finishes last.
-    constexpr int PW = (DH / 16) * 64 * (ES == 2 ? 2 : 4);  // payload floats
+    // the hand-off; fp32 workloads keep fp32), as 16-byte lane slots.  Every split, the
+    // merging one included, enters the merge through the stored (rounded) value, so the
+    // result does not depend on which split finishes last.
+    constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;   // 16-byte slots per lane
+    constexpr uint32_t STRIDE = PAY * 1024 + 128;      // bytes per split partial
     const size_t item = ((size_t)(b * d.Hkv + r) * QT + qt);
-    const size_t stride = (size_t)PW + 32;
-    float* base = bf.attn_ws + item * S * stride;
-    float* mine = base + s * stride;
+    const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
     const float inv_l = 1.0f / l_row;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t) {
-      const f32x4 v = o[t] * inv_l;
+    for (int u = 0; u < PAY; ++u) {
+      f32x4 v;
       if constexpr (ES == 2) {
-        const bf16x4 pk = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-        __hip_atomic_store(reinterpret_cast<uint64_t*>(mine) + t * 64 + lane, __builtin_bit_cast(uint64_t, pk),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const f32x4 a = o[2 * u] * inv_l, c = o[2 * u + 1] * inv_l;
+        const bf16x8 pk = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+        v = __builtin_bit_cast(f32x4, pk);
       } else {
-        st_agent(mine + (t * 64 + lane) * 4, v);
+        v = o[u] * inv_l;
       }
+      st_agent16(ws, s * STRIDE + (u * 64 + lane) * 16, v);
     }
     if (grp == 0) {
-      st_agent(mine + PW + r16, m_run);
-      st_agent(mine + PW + 16 + r16, l_row);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0, 16);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, l_row), ws, s * STRIDE + PAY * 1024 + 64 + r16 * 4,
+                                            0, 16);
     }
-    if (!split_arrive_wave(bf.attn_cnt + item, (unsigned)S)) return;
+    PHASE_MARK(3);
+    const bool last = split_arrive_wave(bf.attn_cnt + item, (unsigned)S);
+    PHASE_MARK(4);
+    if (!last) return;
     float ms[8], ls[8];
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) {
-      const float* p2 = base + min(s2, S - 1) * stride;
-      ms[s2] = ld_agent(p2 + PW + r16);
-      ls[s2] = ld_agent(p2 + PW + 16 + r16);
+      const uint32_t off = min(s2, S - 1) * STRIDE + PAY * 1024;
+      ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + r16 * 4, 0, 16));
+      ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + 64 + r16 * 4, 0, 16));
     }
     float M = -INFINITY;
 #pragma unroll
@@ -521,24 +543,23 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
 #pragma unroll
     for (int h2 = 0; h2 < 8; h2 += 4) {
       if (h2 >= S) break;
+      f32x4 v[4][PAY];
 #pragma unroll
-      for (int t = 0; t < DH / 16; ++t) {
-        f32x4 v[4];
+      for (int u4 = 0; u4 < 4; ++u4)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float* p2 = base + min(h2 + u, S - 1) * stride;
+        for (int u = 0; u < PAY; ++u) v[u4][u] = ld_agent16(ws, min(h2 + u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4)
+#pragma unroll
+        for (int u = 0; u < PAY; ++u) {
           if constexpr (ES == 2) {
-            const bf16x4 pk = __builtin_bit_cast(
-                bf16x4, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p2) + t * 64 + lane, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT));
-            v[u] = f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+            const bf16x8 pk = __builtin_bit_cast(bf16x8, v[u4][u]);
+            o[2 * u] += wgt[h2 + u4] * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+            o[2 * u + 1] += wgt[h2 + u4] * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
           } else {
-            v[u] = ld_agent4(p2 + (t * 64 + lane) * 4);
+            o[u] += wgt[h2 + u4] * v[u4][u];
           }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o[t] += wgt[h2 + u] * v[u];
-      }
     }
     l_row = den;
   }
@@ -553,6 +574,7 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(o[t][i] * inv);
   }
+  PHASE_MARK(7);
 }
 
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
@@ -705,9 +727,11 @@ Plan make_plan(const Dims& d, WDtype wt) {
   p.s_o = pick_split(d.Hq * d.dh, d.D / 16);
   p.s_gu = pick_split(d.D, d.F / 16);
   p.s_d = pick_split(d.F, d.D / 16);
-  // about four 32-key blocks per split
+  // about four 32-key blocks per split, and at most 8 splits (the merge width)
   const int T = d.P + d.H, nblk = (T + 31) / 32;
-  p.attn_bps = nblk < 4 ? nblk : 4;
+  int bps = nblk < 4 ? nblk : 4;
+  if ((nblk + bps - 1) / bps > 8) bps = (nblk + 7) / 8;
+  p.attn_bps = bps;
   return p;
 }
 
@@ -843,3 +867,16 @@ hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype w
 }
 
 }  // namespace phyai
+
+#ifdef PHYAI_PHASE_TRACE
+// Phase-trace build only: copy the per-wave timestamps out (host dst of 4096*4*8 uint64),
+// then clear them.
+extern "C" int phyai_phase_trace(void* host_dst) {
+  static uint64_t zeros[4096 * 4 * 8];
+  if (hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(phyai::g_phase_trace), sizeof(zeros), 0, hipMemcpyDeviceToHost) !=
+          hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(phyai::g_phase_trace), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) != hipSuccess)
+    return 4;
+  return 0;
+}
+#endif

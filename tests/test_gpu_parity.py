@@ -136,3 +136,69 @@ def test_pi05_graph_replay_bitwise():
     e.sync()
     e.close()
     assert all(torch.equal(eager, o) for o in outs)
+
+
+def test_tiny_long_prefix_uses_bounded_splits():
+    """A prefix long enough that four-block splits would exceed the merge width
+    (prefix 1200 -> 38 key blocks)."""
+    d = dataclasses.replace(TINY, prefix_len=1200)
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    assert rel_err(got, ex.denoise(inp, d)) <= 1e-4
+
+
+# ---------------------------------------------------------------- int4 (group-128) variant
+PI05_I4 = synth.CONFIGS["pi05_int4"]
+
+
+def test_int4_quantiser_bit_exact():
+    """The library's GPU quantiser produces exactly the oracle's codes and scales
+    (integer work: bit-exact), including an all-zero group and a ragged row count."""
+    import flow_matching_action_cached_amd as fm
+    from oracle import int4 as q4
+    w = synth.normal(0, "w_qkv", (37, 1024), 0.02)
+    w[3, 128:256] = 0.0
+    w[5, :8] = [2.5e-3, 3.5e-3, -2.5e-3, 7e-3, -7e-3, 0.5e-3, 1.5e-3, -1e-3]
+    packed, scales = fm.quantize_int4_g128(torch.from_numpy(w).cuda())
+    ref_p, ref_s = q4.quantize(w)
+    assert np.array_equal(packed.cpu().numpy(), ref_p)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_s)
+
+
+def test_tiny_int4_matches_oracle():
+    """int4 path at tiny shapes (bf16 activations, int4 expert linears)."""
+    from oracle import int4 as q4
+    d = dataclasses.replace(TINY, weight_dtype="int4")
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    deq = {k: q4.dequantize_stack(*q4.quantize_stack(inp[k])) for k in ("w_qkv", "w_o", "w_gu", "w_d")}
+    ref = ex.denoise(inp, d, linears=deq)
+    err = rel_err(got, ref)
+    _say(f"tiny int4 rel err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_pi05_int4_matches_oracle():
+    _say("case: pi05 int4 g128 batch 1, seed 0")
+    from oracle import int4 as q4
+    inp = synth.make_expert_inputs(PI05_I4, 0)
+    got = _run(PI05_I4, inp)
+    deq = {k: q4.dequantize_stack(*q4.quantize_stack(inp[k])) for k in ("w_qkv", "w_o", "w_gu", "w_d")}
+    ref = ex.denoise(inp, PI05_I4, linears=deq)
+    err = rel_err(got, ref)
+    _say(f"pi05 int4 rel err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_int4_lossless_weights_match_bf16_path():
+    """When W is exactly q*s, quantisation is lossless, so the int4 path must match
+    the bf16 path fed the dequantised weights (same activations, fp32 accumulation)."""
+    from oracle import int4 as q4
+    d4 = dataclasses.replace(TINY, weight_dtype="int4")
+    db = dataclasses.replace(TINY, weight_dtype="bf16")
+    inp = synth.make_expert_inputs(d4, 0)
+    for k in ("w_qkv", "w_o", "w_gu", "w_d"):
+        inp[k] = q4.dequantize_stack(*q4.quantize_stack(inp[k])).astype(np.float32)
+    got4 = _run(d4, inp)
+    gotb = _run(db, inp)
+    assert rel_err(got4, gotb) <= 1e-3
