@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ms per action chunk (10 Euler steps) at batch 1; chunks/sec at batch 32"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 KERNELS = ["qkv", "attention", "o_proj", "gate_up", "down", "out_euler"]
 
 
@@ -70,6 +71,46 @@ def chunk_bytes_int4(d):
     return d.n_steps * (codes + scales + io + kv + tables)
 
 
+def batch_flops(d):
+    """Algorithmic MFMA flops of one chunk for the whole batch: the four expert linears
+    (2 * rows * params per layer) plus attention (QK^T and PV over prefix + chunk keys),
+    times layers and steps.  In/out projections and element-wise work are not counted."""
+    rows = d.batch * d.chunk_len
+    per_layer = d.qkv_dim * d.width + d.width * d.n_q_heads * d.head_dim + 3 * d.mlp_dim * d.width
+    lin = 2 * rows * per_layer
+    keys = d.prefix_len + d.chunk_len
+    attn = 4 * rows * d.n_q_heads * keys * d.head_dim
+    return d.n_steps * d.n_layers * (lin + attn)
+
+
+def time_chunks(ex, noise, out, steps, warmup, torch):
+    for _ in range(warmup):
+        ex.denoise(noise, out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        ex.denoise(noise, out)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def kernel_times(ex, reps, torch):
+    """Mean duration of each loop kernel, one graph replay of `reps` launches each."""
+    res = {}
+    for which, name in enumerate(KERNELS):
+        ex.enqueue_kernel_repeat(which, 0, reps)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ex.enqueue_kernel_repeat(which, 0, reps)
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1000.0 / reps
+    return res
+
+
 def schedule(n):
     import numpy as np
     dt = -1.0 / n
@@ -109,6 +150,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
+                         "known traffic for calibrating hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the loop runs on a single MI355X; --gpus {args.gpus} "
@@ -129,6 +173,13 @@ def main():
     ex.set_timestep_tables(schedule(d.n_steps))
     out = torch.empty_like(noise)
     print(f"[bench] setup done: {d}", file=sys.stderr, flush=True)
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         ex.denoise(noise, out)
@@ -215,6 +266,38 @@ def main():
                                         "algorithmic_bytes": b4,
                                         "hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] int4 variant: {ms4:.4f} ms/chunk", file=sys.stderr, flush=True)
+
+        # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs
+        d32 = synth.CONFIGS["pi05_b32"]
+        inp32 = synth.make_expert_inputs(d32, 0)
+        k32 = torch.from_numpy(inp32["k_pre"]).cuda().to(torch.bfloat16).contiguous()
+        v32 = torch.from_numpy(inp32["v_pre"]).cuda().to(torch.bfloat16).contiguous()
+        n32 = torch.from_numpy(inp32["noise"]).cuda().contiguous()
+        del inp32
+        e32 = fm.ActionExpert.from_dims(d32)
+        e32.set_weights(w)
+        e32.set_prefix_kv(k32, v32)
+        e32.set_timestep_tables(schedule(d.n_steps))
+        o32 = torch.empty_like(n32)
+        ms32 = time_chunks(e32, n32, o32, max(5, args.steps // 5), max(2, args.warmup // 5), torch)
+        kt32 = kernel_times(e32, max(10, args.kernel_reps // 10), torch)
+        e32.close()
+        fl = batch_flops(d32)
+        gemm_fl = {"qkv": 2 * 1600 * d32.qkv_dim * d32.width, "o_proj": 2 * 1600 * d32.width * d32.n_q_heads * d32.head_dim,
+                   "gate_up": 2 * 1600 * 2 * d32.mlp_dim * d32.width, "down": 2 * 1600 * d32.mlp_dim * d32.width}
+        dom32 = max(gemm_fl, key=lambda k: kt32[k])
+        variants["bf16_batch32"] = {
+            "ms_per_batch_chunk": round(ms32, 4), "chunks_per_s": round(32 * 1000.0 / ms32, 2),
+            "algorithmic_tflop": round(fl / 1e12, 3),
+            "mfma_frac": round(fl / (ms32 * 1e-3) / MFMA_PEAK_TFLOPS / 1e12, 4),
+            "kernel_us": {k: round(v, 2) for k, v in kt32.items()},
+            "roofline": {"kernel": dom32, "bound": "mfma", "unit": "TFLOP/s",
+                         "achieved": round(gemm_fl[dom32] / (kt32[dom32] * 1e-6) / 1e12, 1),
+                         "peak": MFMA_PEAK_TFLOPS,
+                         "frac": round(gemm_fl[dom32] / (kt32[dom32] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
+        }
+        print(f"[bench] batch-32 variant: {ms32:.3f} ms per batch chunk, {32000.0 / ms32:.1f} chunks/s",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,62 @@
+// Launch record and per-element epilogues shared by the two GEMM families (the
+// weight-streaming kernels for few token rows and the LDS-tiled kernels for many).
+//
+// Norm folding.  adaRMS(h) W^T = rinv * ((h * (1 + scale)) W^T) + W shift, with
+// rinv = 1/sqrt(mean(h^2) + eps) per token row: the GEMM input is hs = h * (1 + scale)
+// (written by the producer of h), the accumulator is multiplied by rinv and the per-step
+// vector W shift (precomputed with the timestep tables) is added.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace phyai {
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2 };
+
+struct GemmLaunch {
+  const void* A;             // activations, swizzled [Mpad][K]
+  int lda, K;
+  const void* W;             // weights of this layer, swizzled [N][K] (int4: swizzled codes)
+  const uint16_t* Ws;        // int4 scales of this layer [N][K/128]
+  int n_second;              // row offset of the second weight tile (gate/up: F)
+  int S;                     // k-splits across workgroups
+  int layer;
+  const float* cvec;         // norm-folded bias of this step/layer (QKV, GEGLU)
+  const float* scale_next;   // raw scale of the norm that consumes h (RESID)
+};
+
+// QKV output y of token row m, column col: q rows go to q [M][Hq*dh]; the chunk's own
+// K and V go straight into the cache after the prefix rows (V transposed).
+template <class AT>
+__device__ __forceinline__ void qkv_store(const Dims& d, const Bufs& bf, int layer, int m, int col, float y) {
+  const int qd = d.Hq * d.dh, kd = d.Hkv * d.dh;
+  const int b = m / d.H, t = m % d.H;
+  if (col < qd) {
+    static_cast<AT*>(bf.q)[(size_t)m * qd + col] = to_elem<AT>(y);
+  } else if (col < qd + kd) {
+    const int r = (col - qd) / d.dh, dd = (col - qd) % d.dh;
+    static_cast<AT*>(bf.kc)[((((size_t)b * d.L + layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
+  } else {
+    const int r = (col - qd - kd) / d.dh, dd = (col - qd - kd) % d.dh;
+    static_cast<AT*>(bf.vt)[((((size_t)b * d.L + layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
+  }
+}
+
+// Residual update of token row m, column col: h += delta; hs = h * (1 + scale of the next
+// norm) in the GEMM input type (swizzled).  Returns the new h (for the row statistics).
+template <class AT>
+__device__ __forceinline__ float resid_store(const Dims& d, const Bufs& bf, int m, int col, float h_old, float delta,
+                                             float sc1) {
+  const float hn = h_old + delta;
+  bf.h[(size_t)m * d.D + col] = hn;
+  static_cast<AT*>(bf.hs)[sw_idx(m, col, d.D)] = to_elem<AT>(hn * sc1);
+  return hn;
+}
+
+// LDS-tiled GEMM family (gemm_tiled.hip) for more than 64 token rows, bf16 only.
+// n_cols: output columns (gate/up: 2F); epi: Epi.
+hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, int epi, int n_cols,
+                             hipStream_t stream);
+
+}  // namespace phyai

@@ -31,8 +31,7 @@
 // operands.  Partial sums across waves meet in LDS; across workgroups they meet
 // through agent-scope stores and the last workgroup to arrive adds them in split
 // order, so results never depend on arrival order.
-#include "common.h"
-#include "kernels.h"
+#include "epilogue.h"
 
 #include <math.h>
 
@@ -43,20 +42,6 @@ namespace phyai {
 #ifdef PHYAI_PHASE_TRACE
 __device__ uint64_t g_phase_trace[4096 * 4 * 8];
 #endif
-
-enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2 };
-
-struct GemmLaunch {
-  const void* A;             // activations [M][K] (row stride lda)
-  int lda, K;
-  const void* W;             // weights of this layer, [N][K] (int4: repacked codes)
-  const uint16_t* Ws;        // int4 scales of this layer [N][K/128]
-  int n_second;              // row offset of the second weight tile (gate/up: F)
-  int S;                     // k-splits across workgroups
-  int layer;
-  const float* cvec;         // norm-folded bias of this step/layer (QKV, GEGLU)
-  const float* scale_next;   // raw scale of the norm that consumes h (RESID)
-};
 
 // ------------------------------------------------------------------ int4 fragments
 // Swizzled int4 word (8 codes of one lane for one k-block, see sw4_word in common.h):
@@ -698,7 +683,7 @@ size_t gemm_counters(const Dims& d) {
   return n;
 }
 size_t gemm_ws_floats(const Dims& d, const Plan& p) {
-  const int MT = (d.M + 15) / 16;
+  const int MT = std::min((d.M + 15) / 16, 4);  // the split scratch serves the streaming path only
   size_t n = 0;
   auto upd = [&](size_t tiles, int S, int NT) {
     if (S > 1) n = std::max(n, tiles * S * NT * MT * 256);
@@ -727,10 +712,15 @@ Plan make_plan(const Dims& d, WDtype wt) {
   p.s_o = pick_split(d.Hq * d.dh, d.D / 16);
   p.s_gu = pick_split(d.D, d.F / 16);
   p.s_d = pick_split(d.F, d.D / 16);
-  // about four 32-key blocks per split, and at most 8 splits (the merge width)
+  // Key splits only as far as needed to give the chip ~256 workgroups (a batch of many
+  // samples needs none), at least four 32-key blocks per split, at most 8 splits (the
+  // merge width).
   const int T = d.P + d.H, nblk = (T + 31) / 32;
-  int bps = nblk < 4 ? nblk : 4;
-  if ((nblk + bps - 1) / bps > 8) bps = (nblk + 7) / 8;
+  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16, QG = (QT + 3) / 4;
+  const int base = d.B * d.Hkv * QG;
+  int S = std::max(1, 256 / base);
+  S = std::min(S, std::min(8, (nblk + 3) / 4));
+  int bps = (nblk + S - 1) / S;
   p.attn_bps = bps;
   return p;
 }
@@ -756,6 +746,9 @@ static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& 
 
 template <class AT, class WT, int EPI, int NT>
 static hipError_t launch_gemm(const Dims& d, const Bufs& b, const GemmLaunch& g, int tiles, hipStream_t st) {
+  if constexpr (!__is_same(AT, bf16) || !__is_same(WT, bf16)) {
+    if (d.M > 64) return hipErrorInvalidValue;  // many rows: bf16 only (tiled family)
+  }
   switch ((d.M + 15) / 16) {
     case 1: return launch_gemm_q<AT, WT, EPI, NT, 1>(d, b, g, tiles, st);
     case 2: return launch_gemm_q<AT, WT, EPI, NT, 2>(d, b, g, tiles, st);
@@ -802,6 +795,7 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       g.W = static_cast<const char*>(b.w_qkv) + wbytes_row<WT>(d.D) * d.qkv * l;
       g.Ws = b.s_qkv ? b.s_qkv + (size_t)l * d.qkv * (d.D / 128) : nullptr;
       g.S = p.s_qkv; g.cvec = cv + (size_t)l * d.qkv;
+      if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_QKV, d.qkv, st);
       return launch_gemm<AT, WT, EPI_QKV, 1>(d, b, g, d.qkv / 16, st);
     case 1:
       return launch_attn<AT>(d, b, p, l, st);
@@ -810,12 +804,14 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       g.W = static_cast<const char*>(b.w_o) + wbytes_row<WT>(qd) * d.D * l;
       g.Ws = b.s_o ? b.s_o + (size_t)l * d.D * (qd / 128) : nullptr;
       g.S = p.s_o; g.scale_next = b.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D;
+      if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
       return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
     case 3:
       g.A = b.hs; g.lda = d.D; g.K = d.D;
       g.W = static_cast<const char*>(b.w_gu) + wbytes_row<WT>(d.D) * 2 * d.F * l;
       g.Ws = b.s_gu ? b.s_gu + (size_t)l * 2 * d.F * (d.D / 128) : nullptr;
       g.n_second = d.F; g.S = p.s_gu; g.cvec = cv + b.cv_gu_off + (size_t)l * 2 * d.F;
+      if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_GEGLU, 2 * d.F, st);
       return launch_gemm<AT, WT, EPI_GEGLU, 2>(d, b, g, d.F / 16, st);
     case 4: {  // consumer of h is norm 2(l+1), or the final norm 2L
       g.A = b.act; g.lda = d.F; g.K = d.F;
@@ -824,6 +820,7 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       g.S = p.s_d;
       const int jn = (l + 1 < d.L) ? 2 * (l + 1) : 2 * d.L;
       g.scale_next = b.mod + (((size_t)k * d.nmod + jn) * 2) * d.D;
+      if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
       return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
     }
     case 5:

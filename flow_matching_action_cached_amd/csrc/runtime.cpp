@@ -122,7 +122,11 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
     return PHYAI_ERR_INVALID_ARG;
   if (g.width % 256 || g.width > 2048 || g.mlp_dim % 128 || (g.n_q_heads * g.head_dim) % 128 ||
       g.head_dim % 32 || g.head_dim > 256 || g.n_q_heads % g.n_kv_heads || g.action_dim > 256 ||
-      g.action_dim % 8 || g.chunk_len * g.max_batch > 64)
+      g.action_dim % 8)
+    return PHYAI_ERR_UNSUPPORTED;
+  // more than 64 token rows run on the LDS-tiled MFMA GEMMs: bf16 weights, 128-wide tiles
+  if (g.chunk_len * g.max_batch > 64 &&
+      (g.weight_dtype != PHYAI_BF16 || ((g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim) % 128))
     return PHYAI_ERR_UNSUPPORTED;
   if (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) return PHYAI_ERR_UNSUPPORTED;
 

@@ -68,8 +68,10 @@ typedef enum {
 
 /* Model and capacity.  Constraints (else PHYAI_ERR_UNSUPPORTED): width a multiple of 256
  * and <= 2048; mlp_dim and n_q_heads*head_dim multiples of 128; head_dim 32, 64, 128 or
- * 256; n_q_heads a multiple of n_kv_heads; action_dim a multiple of 8 and <= 256;
- * chunk_len * max_batch <= 64 (the weight-streaming path for few token rows). */
+ * 256; n_q_heads a multiple of n_kv_heads; action_dim a multiple of 8 and <= 256.  Up to
+ * 64 token rows (batch x chunk_len) run on weight-streaming kernels (any weight dtype);
+ * more rows run on LDS-tiled MFMA GEMMs, which need PHYAI_BF16 and (Hq+2Hkv)*head_dim a
+ * multiple of 128. */
 typedef struct {
   int n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim;
   int action_dim, chunk_len, max_prefix_len, max_batch;

@@ -68,7 +68,7 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(action_dim=6))[0] == 5
     assert _create(lib, _cfg(head_dim=48))[0] == 5
     assert _create(lib, _cfg(n_q_heads=3, n_kv_heads=2))[0] == 5
-    assert _create(lib, _cfg(chunk_len=50, max_batch=2))[0] == 5   # beyond the streaming path
+    assert _create(lib, _cfg(chunk_len=50, max_batch=2))[0] == 5   # many rows need bf16 weights
     st, h = _create(lib, _cfg(n_layers=0))
     assert h.value is None
 
