@@ -17,6 +17,7 @@ Modules
             reproduce).
 ``int4``    offline round-to-nearest group-128 int4 quantiser and its
             dequantiser.
+``wam``     the joint video/action denoiser with classifier-free guidance.
 
 Every function cites the passage of the pages it follows.  The pages (three
 web pages about PhyAI / FlashRT-PAI) describe the loop in prose only and print
@@ -25,4 +26,4 @@ named where it is used.  Pinning (tests marked ``not gpu``): every function here
 is checked against closed forms, invariants, brute force or library routines.
 No function of this package is "parity unpinned".
 """
-from . import expert, int4, joint  # noqa: F401
+from . import expert, int4, joint, wam  # noqa: F401

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "ExpertDims", "CONFIGS", "TENSOR_IDS", "normal", "bf16_bits", "bf16_values",
-    "make_expert_inputs", "expert_param_shapes",
+    "make_expert_inputs", "expert_param_shapes", "WamDims", "WAM_CONFIGS", "make_wam_inputs",
 ]
 
 # one fixed id per tensor; never reorder (changing an id changes every draw)
@@ -148,4 +148,66 @@ def make_expert_inputs(d: ExpertDims, seed: int = 0, batch: int | None = None,
     out["k_pre"], out["v_pre"] = k, v
     out["noise"] = np.stack([normal(seed, "noise", (d.chunk_len, d.action_dim), 1.0, sample=s)
                              for s in samples])
+    return out
+
+
+# ---------------------------------------------------------------- joint video/action (WAM)
+@dataclasses.dataclass(frozen=True)
+class WamDims:
+    """Joint video/action denoiser: latent and action tokens evolve together in one
+    sequence under full self-attention; a conditional and an unconditional branch are
+    combined by classifier-free guidance."""
+    n_layers: int
+    width: int
+    n_heads: int
+    head_dim: int
+    mlp_dim: int
+    latent_tokens: int
+    latent_dim: int
+    action_tokens: int
+    action_dim: int
+    n_steps: int
+    guidance: float
+    rms_eps: float = 1e-6
+    weight_std: float = 0.02
+
+    @property
+    def tokens(self) -> int:
+        return self.latent_tokens + self.action_tokens
+
+    @property
+    def n_mod(self) -> int:
+        return 2 * self.n_layers + 1
+
+
+WAM_CONFIGS = {
+    # full workload: 28 layers, width 2048, 16 heads of 128, MLP 8192, 4096 latents x 16 + 32 actions x 32
+    "wam": WamDims(28, 2048, 16, 128, 8192, 4096, 16, 32, 32, 8, 3.0),
+    # reduced shapes the CPU oracle finishes in seconds (several tiles, a ragged last tile)
+    "wam_tiny": WamDims(2, 256, 4, 64, 1024, 200, 16, 24, 32, 3, 3.0),
+}
+
+
+def wam_param_shapes(d: WamDims) -> dict:
+    L, D, F = d.n_layers, d.width, d.mlp_dim
+    hd = d.n_heads * d.head_dim
+    return {
+        "w_in_lat": (D, d.latent_dim), "b_in_lat": (D,), "w_in_act": (D, d.action_dim), "b_in_act": (D,),
+        "w_out_lat": (d.latent_dim, D), "b_out_lat": (d.latent_dim,),
+        "w_out_act": (d.action_dim, D), "b_out_act": (d.action_dim,),
+        "w_mod": (d.n_mod, 2 * D, D), "b_mod": (d.n_mod, 2 * D),
+        "w_qkv": (L, 3 * hd, D), "w_o": (L, D, hd), "w_gu": (L, 2 * F, D), "w_d": (L, D, F),
+    }
+
+
+def make_wam_inputs(d: WamDims, seed: int = 0) -> dict:
+    """bf16-valued weights (RNE of float32 N(0, std^2) draws), float32 latents/actions
+    N(0, 1), bf16-valued condition vector N(0, 1) (the unconditional branch uses 0)."""
+    out = {}
+    for name, shape in wam_param_shapes(d).items():
+        out[name] = bf16_values(normal(seed, "wam_" + name, shape, d.weight_std))
+    out["z_lat"] = normal(seed, "wam_z_lat", (d.latent_tokens, d.latent_dim))
+    out["z_act"] = normal(seed, "wam_z_act", (d.action_tokens, d.action_dim))
+    out["c_cond"] = bf16_values(normal(seed, "wam_cond", (d.width,)))
+    out["c_uncond"] = np.zeros(d.width, np.float32)
     return out
