@@ -28,7 +28,8 @@ EXPORTED = (
     "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_timestep_tables",
     "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
-    "phyai_enqueue_kernel_repeat",
+    "phyai_enqueue_kernel_repeat", "phyai_wam_create", "phyai_wam_set_weights", "phyai_wam_set_conditions",
+    "phyai_wam_denoise",
 )
 
 
@@ -52,6 +53,21 @@ _WFIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WFIELDS]
+
+
+class WamConfig(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("width", ctypes.c_int), ("n_heads", ctypes.c_int),
+                ("head_dim", ctypes.c_int), ("mlp_dim", ctypes.c_int), ("latent_tokens", ctypes.c_int),
+                ("latent_dim", ctypes.c_int), ("action_tokens", ctypes.c_int), ("action_dim", ctypes.c_int),
+                ("rms_eps", ctypes.c_float), ("max_arena_bytes", ctypes.c_size_t)]
+
+
+_WAM_WFIELDS = ("w_in_lat", "b_in_lat", "w_in_act", "b_in_act", "w_out_lat", "b_out_lat", "w_out_act",
+                "b_out_act", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d")
+
+
+class WamWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WAM_WFIELDS]
 
 
 _lib = None
@@ -82,6 +98,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_quantize_int4_g128.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
     lib.phyai_get_modulation.argtypes = [vp, vp]
     lib.phyai_enqueue_kernel_repeat.argtypes = [vp, ci, ci, ci]
+    lib.phyai_wam_create.argtypes = [ctypes.POINTER(WamConfig), vp, ctypes.POINTER(vp)]
+    lib.phyai_wam_set_weights.argtypes = [vp, ctypes.POINTER(WamWeights)]
+    lib.phyai_wam_set_conditions.argtypes = [vp, vp, vp, cf]
+    lib.phyai_wam_denoise.argtypes = [vp, vp, vp, ci, vp, vp]
     lib.phyai_version.restype = ctypes.c_char_p
     for name in EXPORTED:
         if name not in ("phyai_last_error", "phyai_status_string", "phyai_destroy", "phyai_version"):
@@ -100,7 +120,50 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-class ActionExpert:
+class _Context:
+    """Calls shared by both context kinds (see include/phyai.h)."""
+
+    _h = None
+
+    def _check(self, st):
+        if st != 0:
+            raise PhyaiError(st, self._lib.phyai_last_error(self._h).decode())
+
+    def set_timestep_tables(self, t):
+        arr = (ctypes.c_float * len(t))(*[float(x) for x in t])
+        self._check(self._lib.phyai_set_timestep_tables(self._h, arr, len(t)))
+        self.n_steps = len(t)
+
+    def set_graph_mode(self, use_graph: bool):
+        self._check(self._lib.phyai_set_graph_mode(self._h, int(bool(use_graph))))
+
+    def enqueue_kernel_repeat(self, which: int, layer: int, reps: int):
+        """One graph replay of `reps` launches of a single loop kernel (see phyai.h)."""
+        self._check(self._lib.phyai_enqueue_kernel_repeat(self._h, which, layer, reps))
+
+    def _modulation(self, shape):
+        import torch
+        out = torch.empty(shape, dtype=torch.float32, device="cuda")
+        self._check(self._lib.phyai_get_modulation(self._h, _ptr(out)))
+        self.sync()
+        return out
+
+    def sync(self):
+        self._check(self._lib.phyai_sync(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.phyai_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class ActionExpert(_Context):
     """One runner context: owns the device arena, the prefix KV cache, the tables
     and the captured denoise graphs (see include/phyai.h)."""
 
@@ -128,10 +191,6 @@ class ActionExpert:
                    max_prefix_len=kw.pop("max_prefix_len", d.prefix_len), max_batch=kw.pop("max_batch", d.batch),
                    weight_dtype=d.weight_dtype, rms_eps=d.rms_eps, **kw)
 
-    def _check(self, st):
-        if st != 0:
-            raise PhyaiError(st, self._lib.phyai_last_error(self._h).decode())
-
     def set_weights(self, w: dict):
         """w: dict of contiguous cuda tensors named as in phyai_weights."""
         for k, t in w.items():
@@ -148,14 +207,6 @@ class ActionExpert:
         self._batch = int(k.shape[0])
         self.sync()
 
-    def set_timestep_tables(self, t):
-        arr = (ctypes.c_float * len(t))(*[float(x) for x in t])
-        self._check(self._lib.phyai_set_timestep_tables(self._h, arr, len(t)))
-        self.n_steps = len(t)
-
-    def set_graph_mode(self, use_graph: bool):
-        self._check(self._lib.phyai_set_graph_mode(self._h, int(bool(use_graph))))
-
     def denoise(self, noise, out=None):
         """noise: cuda float32 [B][H][A]; returns x at t=0 (asynchronous on the stream)."""
         import torch
@@ -165,31 +216,60 @@ class ActionExpert:
         self._check(self._lib.phyai_denoise(self._h, _ptr(noise), int(noise.shape[0]), self.n_steps, _ptr(out)))
         return out
 
-    def enqueue_kernel_repeat(self, which: int, layer: int, reps: int):
-        """One graph replay of `reps` launches of a single loop kernel (see phyai.h)."""
-        self._check(self._lib.phyai_enqueue_kernel_repeat(self._h, which, layer, reps))
+    def get_modulation(self):
+        c = self.cfg
+        return self._modulation((self.n_steps, 2 * c.n_layers + 1, 2, c.width))
+
+
+class JointDenoiser(_Context):
+    """Joint video/action denoiser context with a guided branch pair (see include/phyai.h)."""
+
+    def __init__(self, *, n_layers, width, n_heads, head_dim, mlp_dim, latent_tokens, latent_dim,
+                 action_tokens, action_dim, rms_eps=1e-6, max_arena_bytes=0, stream=None):
+        self._lib = load_library()
+        cfg = WamConfig(n_layers, width, n_heads, head_dim, mlp_dim, latent_tokens, latent_dim, action_tokens,
+                        action_dim, rms_eps, max_arena_bytes)
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        st = self._lib.phyai_wam_create(ctypes.byref(cfg), _stream_handle(stream), ctypes.byref(h))
+        if st != 0:
+            raise PhyaiError(st, "phyai_wam_create failed")
+        self._h = h
+
+    @classmethod
+    def from_dims(cls, d, **kw):
+        """Build from a ``synth.WamDims``-like object."""
+        return cls(n_layers=d.n_layers, width=d.width, n_heads=d.n_heads, head_dim=d.head_dim, mlp_dim=d.mlp_dim,
+                   latent_tokens=d.latent_tokens, latent_dim=d.latent_dim, action_tokens=d.action_tokens,
+                   action_dim=d.action_dim, rms_eps=d.rms_eps, **kw)
+
+    def set_weights(self, w: dict):
+        """w: dict of contiguous bf16 cuda tensors named as in phyai_wam_weights."""
+        for k in _WAM_WFIELDS:
+            if not w[k].is_contiguous():
+                raise ValueError(f"{k} must be contiguous")
+        ws = WamWeights(*[_ptr(w[n]) for n in _WAM_WFIELDS])
+        self._check(self._lib.phyai_wam_set_weights(self._h, ctypes.byref(ws)))
+
+    def set_conditions(self, c_cond, c_uncond, guidance: float):
+        """c_cond, c_uncond: bf16 cuda [D]."""
+        assert c_cond.is_contiguous() and c_uncond.is_contiguous()
+        self._check(self._lib.phyai_wam_set_conditions(self._h, _ptr(c_cond), _ptr(c_uncond), float(guidance)))
+
+    def denoise(self, z_lat, z_act, out_lat=None, out_act=None):
+        """z_lat float32 cuda [Tl][Cl], z_act float32 cuda [Ta][A] -> (z_lat, z_act) at t = 0."""
+        import torch
+        for z in (z_lat, z_act):
+            assert z.dtype == torch.float32 and z.is_contiguous()
+        out_lat = torch.empty_like(z_lat) if out_lat is None else out_lat
+        out_act = torch.empty_like(z_act) if out_act is None else out_act
+        self._check(self._lib.phyai_wam_denoise(self._h, _ptr(z_lat), _ptr(z_act), self.n_steps, _ptr(out_lat),
+                                                _ptr(out_act)))
+        return out_lat, out_act
 
     def get_modulation(self):
-        import torch
         c = self.cfg
-        out = torch.empty((self.n_steps, 2 * c.n_layers + 1, 2, c.width), dtype=torch.float32, device="cuda")
-        self._check(self._lib.phyai_get_modulation(self._h, _ptr(out)))
-        self.sync()
-        return out
-
-    def sync(self):
-        self._check(self._lib.phyai_sync(self._h))
-
-    def close(self):
-        if getattr(self, "_h", None):
-            self._lib.phyai_destroy(self._h)
-            self._h = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        return self._modulation((self.n_steps, 2, 2 * c.n_layers + 1, 2, c.width))
 
 
 def quantize_int4_g128(w, stream=None):

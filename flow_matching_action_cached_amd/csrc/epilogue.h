@@ -36,10 +36,10 @@ __device__ __forceinline__ void qkv_store(const Dims& d, const Bufs& bf, int lay
     static_cast<AT*>(bf.q)[(size_t)m * qd + col] = to_elem<AT>(y);
   } else if (col < qd + kd) {
     const int r = (col - qd) / d.dh, dd = (col - qd) % d.dh;
-    static_cast<AT*>(bf.kc)[((((size_t)b * d.L + layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
+    static_cast<AT*>(bf.kc)[((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
   } else {
     const int r = (col - qd - kd) / d.dh, dd = (col - qd - kd) % d.dh;
-    static_cast<AT*>(bf.vt)[((((size_t)b * d.L + layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
+    static_cast<AT*>(bf.vt)[((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
   }
 }
 

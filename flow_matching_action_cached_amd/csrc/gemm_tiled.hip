@@ -105,9 +105,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
     }
   }
 
-  // ---- epilogues: acc[i][j][e] is row rowbase + 16 i + 4 grp + e, virtual column tile vt0 + j
+  // ---- epilogues: acc[i][j][e] is row rowbase + 16 i + 4 grp + e, virtual column tile vt0 + j.
+  // Rows may belong to different modulation tables (a guided pair: one table per branch):
+  // the per-step vectors of table tb sit tb * cv_stride (W shift) or tb * nmod * 2 * D
+  // (scale) after table 0's.
   const int rowbase = tm * BM + wm * WMT * 16;
   const int vt0 = tn * BNT + wn * WNT;
+  const size_t scale_tab = (size_t)d.nmod * 2 * d.D;
 #pragma unroll
   for (int i = 0; i < WMT; ++i) {
     const int m0 = rowbase + i * 16 + grp * 4;
@@ -115,23 +119,26 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const int col = (vt0 + j) * 16 + r16;
-        const float c = g.cvec[col];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + e;
-          if (m < d.M) qkv_store<AT>(d, bf, g.layer, m, col, rinv_s[m - tm * BM] * acc[i][j][e] + c);
+          if (m >= d.M) continue;
+          const float c = g.cvec[(size_t)(m / d.rows_per_tab) * bf.cv_stride + col];
+          qkv_store<AT>(d, bf, g.layer, m, col, rinv_s[m - tm * BM] * acc[i][j][e] + c);
         }
       }
     } else if constexpr (EPI == EPI_RESID) {
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const int col = (vt0 + j) * 16 + r16;
-        const float sc1 = 1.0f + g.scale_next[col];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + e;
           float hn = 0.f;
-          if (m < d.M) hn = resid_store<AT>(d, bf, m, col, bf.h[(size_t)m * d.D + col], acc[i][j][e], sc1);
+          if (m < d.M) {
+            const float sc1 = 1.0f + g.scale_next[(size_t)(m / d.rows_per_tab) * scale_tab + col];
+            hn = resid_store<AT>(d, bf, m, col, bf.h[(size_t)m * d.D + col], acc[i][j][e], sc1);
+          }
           const float sq = sum16(hn * hn);
           if (r16 == 0 && m < d.M) bf.ssq[(size_t)m * (d.D / 16) + vt0 + j] = sq;
         }
@@ -140,11 +147,12 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
 #pragma unroll
       for (int j = 0; j < WNT; j += 2) {
         const int f = ((vt0 + j) >> 1) * 16 + r16;
-        const float cg = g.cvec[f], cu = g.cvec[g.n_second + f];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + e;
           if (m >= d.M) continue;
+          const float* cv = g.cvec + (size_t)(m / d.rows_per_tab) * bf.cv_stride;
+          const float cg = cv[f], cu = cv[g.n_second + f];
           const float ri = rinv_s[m - tm * BM];
           const float yg = ri * acc[i][j][e] + cg;
           const float yu = ri * acc[i][j + 1][e] + cu;

@@ -18,21 +18,29 @@ struct Dims {
   int qkv, nmod;                   // (Hq + 2 Hkv) * dh, 2L + 1
   int N;                           // Euler steps
   float eps;
+  int Lc;                          // layers held by the KV cache (L; 1 when no cache is kept)
+  int ntab, rows_per_tab;          // modulation tables (1; 2 for a guided pair), token rows per table
+  int joint;                       // 1: joint video/action denoiser (no prefix, guided branch pair)
+  int Tl, Cl;                      // joint denoiser: latent tokens and their channels (0 otherwise)
+  float gamma;                     // joint denoiser: guidance scale
 };
 
 // Device pointers of one context.  Element types depend on the weight dtype:
 // "io" = fp32 (F32) or bf16 (BF16, INT4); "act" = fp32 (F32) or bf16 (BF16, INT4);
 // expert linears: fp32 / bf16 / repacked int4 codes + bf16 scales.
 struct Bufs {
-  const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;  // io
+  const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;  // io (joint denoiser: latent projections)
+  const void *w_in2, *b_in2, *w_out2, *b_out2;              // joint denoiser: action projections
+  const void* cond;                                         // [ntab][D] io: added to the embedding
   const void *w_qkv, *w_o, *w_gu, *w_d;                     // expert linears
   const uint16_t *s_qkv, *s_o, *s_gu, *s_d;                 // int4 scales (bf16 bits)
   void *kc, *vt;          // K cache [Bmax][L][Hkv][KS][dh], V^T cache [Bmax][L][Hkv][dh][KS] (act)
-  const float* mod;       // [N][nmod][2][D] (scale, shift)
-  const float* cvec;      // [N][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
+  const float* mod;       // [N][ntab][nmod][2][D] (scale, shift)
+  const float* cvec;      // [N][ntab][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
   const float* dt;        // [N]
   int cv_stride, cv_gu_off, cv_out_off;
   float *x, *h, *ssq;     // state [M][A], residual [M][D], row sum-of-squares partials [Mst][D/16]
+  float* x2;              // joint denoiser: action state [Ta][A] (x holds the latents [Tl][Cl])
   void *hs, *q, *o, *act; // act-typed: hs [Mpad][D], o [Mpad][Hq dh], act [Mpad][F] swizzled; q [M][Hq dh]
   float* attn_ws; unsigned* attn_cnt;
   float* gemm_ws; unsigned* gemm_cnt;
@@ -58,6 +66,11 @@ hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype w
 // 5 out/Euler/in-projection, 6 first in-projection) with the arguments of step k, layer l.
 hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, int which, int k, int l,
                        hipStream_t stream);
+
+// Joint video/action denoiser (bf16): whole guided loop, and one launch of a loop kernel.
+hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipStream_t stream);
+hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
+                           hipStream_t stream);
 
 // One-off kernels.
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,

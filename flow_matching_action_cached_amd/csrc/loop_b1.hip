@@ -281,10 +281,10 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
         q[(size_t)m * qd + col] = to_elem<AT>(y);
       } else if (col < qd + kd) {
         const int r = (col - qd) / d.dh, dd = (col - qd) % d.dh;
-        kc[((((size_t)b * d.L + g.layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
+        kc[((((size_t)b * d.Lc + g.layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
       } else {
         const int r = (col - qd - kd) / d.dh, dd = (col - qd - kd) % d.dh;
-        vt[((((size_t)b * d.L + g.layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
+        vt[((((size_t)b * d.Lc + g.layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
       }
     }
   } else if constexpr (EPI == EPI_RESID) {
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   const int m = b * d.H + tok;
   const int qd = d.Hq * DH;
 
-  const size_t kvbase = ((size_t)b * d.L + layer) * d.Hkv + r;
+  const size_t kvbase = ((size_t)b * d.Lc + layer) * d.Hkv + r;
   const AT* Kc = static_cast<const AT*>(bf.kc) + kvbase * d.KS * DH;
   const AT* Vt = static_cast<const AT*>(bf.vt) + kvbase * DH * d.KS;
 
@@ -666,6 +666,100 @@ __global__ __launch_bounds__(256) void k_out_euler(Dims d, Bufs bf, int k_prev, 
   }
 }
 
+// ------------------------------------------------------------------ joint denoiser: guidance + Euler
+// Joint video/action denoiser (PhyAI reading, Figure 4: conditional and unconditional
+// branches combined by the guidance scale, then every rank advances its video/action
+// state).  Rows [0, H) of every activation hold the conditional branch (modulation
+// table 0), rows [H, 2H) the unconditional one (table 1); token t < Tl is a latent
+// token (Cl channels, latent projections), the rest action tokens (A dims).
+// One workgroup per token t.  k_prev >= 0: both branches' final norm and out-projection,
+// v = v_u + gamma (v_c - v_u), z += dt v.  k_next >= 0: in-projection of z (identical for
+// both branches), hs of each branch with its own first-norm scale, row statistics.
+template <class AT, class IOT>
+__global__ __launch_bounds__(256) void k_wam_out(Dims d, Bufs bf, int k_prev, int k_next) {
+  typedef typename FragOf<AT>::type AF;
+  typedef typename FragOf<IOT>::type WF;
+  __shared__ float xs[256];
+  __shared__ float vres[2][256];
+  __shared__ float wred[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.x;
+  const bool lat = t < d.Tl;
+  const int dim = lat ? d.Cl : d.A;
+  const IOT* wo = static_cast<const IOT*>(lat ? bf.w_out : bf.w_out2);
+  const IOT* bo = static_cast<const IOT*>(lat ? bf.b_out : bf.b_out2);
+  const IOT* wi = static_cast<const IOT*>(lat ? bf.w_in : bf.w_in2);
+  const IOT* bi = static_cast<const IOT*>(lat ? bf.b_in : bf.b_in2);
+  float* z = lat ? bf.x + (size_t)t * d.Cl : bf.x2 + (size_t)(t - d.Tl) * d.A;
+  const int rows[2] = {t, d.H + t};
+  if (k_prev >= 0) {
+    const int n16 = d.D / 16;
+    if (w < 2) {  // wave b: row statistics of branch b
+      const int m = rows[w];
+      float ss = 0.f;
+      for (int j = lane; j < n16; j += 64) ss += bf.ssq[(size_t)m * n16 + j];
+      ss = wave_sum(ss);
+      if (lane == 0) wred[w] = ss;
+    }
+    const AT* hsb = static_cast<const AT*>(bf.hs);
+    for (int o0 = w; o0 < 2 * dim; o0 += 4) {  // output o: branch o / dim, channel o % dim
+      const int br = o0 / dim, a = o0 % dim;
+      const int m = rows[br];
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = lane * 8 + 512 * j;
+        const int kc = min(k, d.D - 8);
+        const AF hv = load_frag(hsb + sw_idx(m, kc, d.D));
+        const WF wv = load_frag(wo + (size_t)a * d.D + kc);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += to_f32(hv[e]) * to_f32(wv[e]);
+        acc += k < d.D ? part : 0.f;
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) vres[br][a] = acc;
+    }
+    __syncthreads();
+    for (int a = tid; a < dim; a += 256) {
+      const int ooff = bf.cv_out_off + (lat ? 0 : d.Cl) + a;
+      float v[2];
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        const float rinv = 1.0f / sqrtf(wred[br] / (float)d.D + d.eps);
+        const float* cv = bf.cvec + ((size_t)k_prev * d.ntab + br) * bf.cv_stride;
+        v[br] = rinv * vres[br][a] + cv[ooff] + to_f32(bo[a]);
+      }
+      const float vg = v[1] + d.gamma * (v[0] - v[1]);
+      const float zn = z[a] + bf.dt[k_prev] * vg;
+      z[a] = zn;
+      xs[a] = zn;
+    }
+    __syncthreads();
+  } else {
+    for (int a = tid; a < dim; a += 256) xs[a] = z[a];
+    __syncthreads();
+  }
+  if (k_next < 0) return;
+  AT* hs = static_cast<AT*>(bf.hs);
+  const size_t stab = (size_t)d.nmod * 2 * d.D;
+  const float* scl = bf.mod + (size_t)k_next * d.ntab * stab;  // table 0, norm 0, scale row
+  for (int n0 = 0; n0 < d.D; n0 += 256) {
+    const int n = n0 + tid;
+    float hn = to_f32(bi[n]);
+    for (int a = 0; a < dim; ++a) hn += xs[a] * to_f32(wi[(size_t)n * dim + a]);
+    const float sq = sum16(hn * hn);
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      const int m = rows[br];
+      bf.h[(size_t)m * d.D + n] = hn;
+      hs[sw_idx(m, n, d.D)] = to_elem<AT>(hn * (1.0f + scl[br * stab + n]));
+      if ((tid & 15) == 0) bf.ssq[(size_t)m * (d.D / 16) + n / 16] = sq;
+    }
+  }
+}
+
 // ================================================================== host side
 size_t attn_counters(const Dims& d) {
   const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
@@ -852,6 +946,63 @@ hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, i
     case W_INT4: return launch_one<bf16, i4, bf16>(d, b, p, which, k, l, st);
   }
   return hipErrorInvalidValue;
+}
+
+// Joint denoiser: one launch of kernel `which` (0 QKV, 1 attention, 2 O, 3 gate/up, 4 down,
+// 5 guidance/Euler/in-projection, 6 first in-projection) for step k, layer l.  No K/V is
+// kept across layers (one cache layer, no prefix); every linear runs on the tiled GEMMs
+// with one modulation table per branch.
+static hipError_t launch_one_wam(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
+                                 hipStream_t st) {
+  const int qd = d.Hq * d.dh;
+  const float* cv = b.cvec + (size_t)k * d.ntab * b.cv_stride;
+  const float* md = b.mod + (size_t)k * d.ntab * d.nmod * 2 * d.D;
+  GemmLaunch g{};
+  g.layer = 0;  // cache layer
+  g.S = 1;
+  switch (which) {
+    case 0:
+      g.A = b.hs; g.K = d.D; g.W = static_cast<const bf16*>(b.w_qkv) + (size_t)l * d.qkv * d.D;
+      g.cvec = cv + (size_t)l * d.qkv;
+      return launch_gemm_tiled(d, b, g, EPI_QKV, d.qkv, st);
+    case 1:
+      return launch_attn<bf16>(d, b, p, 0, st);
+    case 2:
+      g.A = b.o; g.K = qd; g.W = static_cast<const bf16*>(b.w_o) + (size_t)l * d.D * qd;
+      g.scale_next = md + (size_t)(2 * l + 1) * 2 * d.D;
+      return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
+    case 3:
+      g.A = b.hs; g.K = d.D; g.W = static_cast<const bf16*>(b.w_gu) + (size_t)l * 2 * d.F * d.D;
+      g.n_second = d.F; g.cvec = cv + b.cv_gu_off + (size_t)l * 2 * d.F;
+      return launch_gemm_tiled(d, b, g, EPI_GEGLU, 2 * d.F, st);
+    case 4: {
+      g.A = b.act; g.K = d.F; g.W = static_cast<const bf16*>(b.w_d) + (size_t)l * d.D * d.F;
+      const int jn = (l + 1 < d.L) ? 2 * (l + 1) : 2 * d.L;
+      g.scale_next = md + (size_t)jn * 2 * d.D;
+      return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
+    }
+    case 5:
+      hipLaunchKernelGGL((k_wam_out<bf16, bf16>), dim3(d.H), dim3(256), 0, st, d, b, k, k + 1 < d.N ? k + 1 : -1);
+      return hipGetLastError();
+    case 6:
+      hipLaunchKernelGGL((k_wam_out<bf16, bf16>), dim3(d.H), dim3(256), 0, st, d, b, -1, 0);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l, hipStream_t st) {
+  return launch_one_wam(d, b, p, which, k, l, st);
+}
+
+hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipStream_t st) {
+  hipError_t e = launch_one_wam(d, b, p, 6, 0, 0, st);
+  for (int k = 0; k < d.N && e == hipSuccess; ++k) {
+    for (int l = 0; l < d.L && e == hipSuccess; ++l)
+      for (int which = 0; which < 5 && e == hipSuccess; ++which) e = launch_one_wam(d, b, p, which, k, l, st);
+    if (e == hipSuccess) e = launch_one_wam(d, b, p, 5, k, 0, st);
+  }
+  return e;
 }
 
 hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t st) {

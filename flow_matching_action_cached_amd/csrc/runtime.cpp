@@ -39,7 +39,8 @@ struct phyai_ctx {
   float* t_dev = nullptr;
   double* e_dev = nullptr;
 
-  bool have_weights = false, have_prefix = false, have_tables = false;
+  int joint = 0;                     // 1: joint video/action denoiser context
+  bool have_weights = false, have_prefix = false, have_tables = false, have_cond = false;
   int batch = 0, prefix_len = 0, n_steps = 0;
   int use_graph = 1;
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
@@ -83,11 +84,48 @@ void drop_graphs(phyai_ctx* c) {
 
 Dims launch_dims(const phyai_ctx* c, int batch, int prefix_len, int n_steps) {
   Dims d = c->base;
+  if (c->joint) {  // fixed shape: the branch pair over all tokens, no prefix
+    d.N = n_steps;
+    return d;
+  }
   d.B = batch;
   d.M = batch * d.H;
   d.P = prefix_len;
   d.N = n_steps;
   return d;
+}
+
+// Enqueue the whole loop on the context stream: one graph launch (captured on first use for
+// this (batch, prefix_len, n_steps)) or the same kernels launched eagerly.
+phyai_status run_loop(phyai_ctx* c, const Dims& d, const Plan& plan, const char* who) {
+  auto enqueue = [&](hipStream_t st) {
+    return c->joint ? enqueue_wam_denoise(d, c->b, plan, st) : enqueue_denoise(d, c->b, plan, c->wt, st);
+  };
+  if (!c->use_graph) {
+    HIPCHK(c, enqueue(c->stream));
+    return PHYAI_OK;
+  }
+  auto key = std::make_tuple(d.B, d.P, d.N);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipError_t e = enqueue(c->cap_stream);
+    hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+    if (e != hipSuccess || e2 != hipSuccess) {
+      if (graph) hipGraphDestroy(graph);
+      return fail(c, PHYAI_ERR_DEVICE,
+                  std::string(who) + ": graph capture failed: " + hipGetErrorString(e != hipSuccess ? e : e2));
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess)
+      return fail(c, PHYAI_ERR_DEVICE, std::string(who) + ": graph instantiate: " + hipGetErrorString(e));
+    it = c->graphs.emplace(key, exec).first;
+  }
+  HIPCHK(c, hipGraphLaunch(it->second, c->stream));
+  return PHYAI_OK;
 }
 
 }  // namespace
@@ -151,6 +189,13 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   d.nmod = 2 * g.n_layers + 1;
   d.N = 1;
   d.eps = g.rms_eps;
+  d.Lc = d.L;
+  d.joint = 0;
+  d.ntab = 1;
+  d.rows_per_tab = 1 << 30;
+  d.Tl = 0;
+  d.Cl = 0;
+  d.gamma = 0.f;
 
   const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
   Layout lay;
@@ -234,6 +279,7 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
 phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "set_weights: joint denoiser context (use phyai_wam_set_weights)");
   if (!w || !w->w_in || !w->b_in || !w->w_out || !w->b_out || !w->w_mod || !w->b_mod || !w->w_qkv || !w->w_o ||
       !w->w_gu || !w->w_d)
     return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: null weight pointer");
@@ -283,6 +329,7 @@ phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
 phyai_status phyai_set_prefix_kv(phyai_ctx* c, const void* k, const void* v, int batch, int prefix_len) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "set_prefix_kv: a joint denoiser context has no cached prefix");
   if (!k || !v) return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefix_kv: null pointer");
   if (batch < 1 || batch > c->cfg.max_batch)
     return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefix_kv: batch out of range [1, max_batch]");
@@ -300,13 +347,16 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   c->err.clear();
   if (!t_host || n_steps < 1) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: need n_steps >= 1 times");
   if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "set_timestep_tables: weights not set");
+  if (c->joint && !c->have_cond)
+    return fail(c, PHYAI_ERR_BAD_STATE, "set_timestep_tables: branch conditions not set");
   for (int i = 0; i < n_steps; ++i)
     if (!std::isfinite(t_host[i])) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: non-finite time");
   Dims d = c->base;
   d.N = n_steps;
-  const size_t mod_f = (size_t)n_steps * d.nmod * 2 * d.D;
-  const int cv_stride = d.L * d.qkv + d.L * 2 * d.F + d.A;
-  const size_t cv_f = (size_t)n_steps * cv_stride;
+  const size_t mod_f = (size_t)n_steps * d.ntab * d.nmod * 2 * d.D;
+  // per table: W_qkv shifts | W_gu shifts | out-projection shifts (expert A; joint Cl + A)
+  const int cv_stride = d.L * d.qkv + d.L * 2 * d.F + (d.joint ? d.Cl + d.A : d.A);
+  const size_t cv_f = (size_t)n_steps * d.ntab * cv_stride;
   if (n_steps > c->tab_cap) {
     HIPCHK(c, hipStreamSynchronize(c->stream));
     drop_graphs(c);
@@ -322,9 +372,9 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   const int cap = c->tab_cap;
   char* p = static_cast<char*>(c->tab);
   float* mod = reinterpret_cast<float*>(p);
-  p += align256((size_t)cap * d.nmod * 2 * d.D * 4);
+  p += align256((size_t)cap * d.ntab * d.nmod * 2 * d.D * 4);
   float* cvec = reinterpret_cast<float*>(p);
-  p += align256((size_t)cap * cv_stride * 4);
+  p += align256((size_t)cap * d.ntab * cv_stride * 4);
   float* dt = reinterpret_cast<float*>(p);
   p += align256((size_t)cap * 4);
   c->t_dev = reinterpret_cast<float*>(p);
@@ -361,6 +411,7 @@ phyai_status phyai_set_graph_mode(phyai_ctx* c, int use_graph) {
 phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_steps, float* out) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: joint denoiser context (use phyai_wam_denoise)");
   if (!noise || !out) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: null pointer");
   if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: weights not set");
   if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: prefix KV not set");
@@ -371,29 +422,8 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
   const Plan plan = make_plan(d, c->wt);
   const size_t xbytes = (size_t)d.M * d.A * 4;
   HIPCHK(c, hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream));
-  if (c->use_graph) {
-    auto key = std::make_tuple(batch, c->prefix_len, n_steps);
-    auto it = c->graphs.find(key);
-    if (it == c->graphs.end()) {
-      hipGraph_t graph = nullptr;
-      HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-      hipError_t e = enqueue_denoise(d, c->b, plan, c->wt, c->cap_stream);
-      hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
-      if (e != hipSuccess || e2 != hipSuccess) {
-        if (graph) hipGraphDestroy(graph);
-        return fail(c, PHYAI_ERR_DEVICE,
-                    std::string("denoise: graph capture failed: ") + hipGetErrorString(e != hipSuccess ? e : e2));
-      }
-      hipGraphExec_t exec = nullptr;
-      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-      hipGraphDestroy(graph);
-      if (e != hipSuccess) return fail(c, PHYAI_ERR_DEVICE, std::string("denoise: graph instantiate: ") + hipGetErrorString(e));
-      it = c->graphs.emplace(key, exec).first;
-    }
-    HIPCHK(c, hipGraphLaunch(it->second, c->stream));
-  } else {
-    HIPCHK(c, enqueue_denoise(d, c->b, plan, c->wt, c->stream));
-  }
+  const phyai_status st = run_loop(c, d, plan, "denoise");
+  if (st != PHYAI_OK) return st;
   HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
   return PHYAI_OK;
 }
@@ -403,7 +433,7 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
   c->err.clear();
   if (which < 0 || which > 6 || reps < 1 || reps > 100000 || layer < 0 || layer >= c->base.L)
     return fail(c, PHYAI_ERR_INVALID_ARG, "enqueue_kernel_repeat: bad kernel id, layer or reps");
-  if (!c->have_weights || !c->have_prefix || !c->have_tables)
+  if (!c->have_weights || !(c->have_prefix || c->joint) || !c->have_tables)
     return fail(c, PHYAI_ERR_BAD_STATE, "enqueue_kernel_repeat: weights, prefix and tables must be set");
   const Dims d = launch_dims(c, c->batch, c->prefix_len, c->n_steps);
   const Plan plan = make_plan(d, c->wt);
@@ -413,7 +443,9 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
     hipGraph_t graph = nullptr;
     HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
     hipError_t e = hipSuccess;
-    for (int i = 0; i < reps && e == hipSuccess; ++i) e = enqueue_one(d, c->b, plan, c->wt, which, 0, layer, c->cap_stream);
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+      e = c->joint ? enqueue_wam_one(d, c->b, plan, which, 0, layer, c->cap_stream)
+                   : enqueue_one(d, c->b, plan, c->wt, which, 0, layer, c->cap_stream);
     hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
     if (e != hipSuccess || e2 != hipSuccess) {
       if (graph) hipGraphDestroy(graph);
@@ -442,7 +474,7 @@ phyai_status phyai_get_modulation(phyai_ctx* c, float* dst) {
   c->err.clear();
   if (!dst) return fail(c, PHYAI_ERR_INVALID_ARG, "get_modulation: null pointer");
   if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "get_modulation: tables not set");
-  const size_t bytes = (size_t)c->n_steps * c->base.nmod * 2 * c->base.D * 4;
+  const size_t bytes = (size_t)c->n_steps * c->base.ntab * c->base.nmod * 2 * c->base.D * 4;
   HIPCHK(c, hipMemcpyAsync(dst, c->b.mod, bytes, hipMemcpyDeviceToDevice, c->stream));
   return PHYAI_OK;
 }
@@ -455,6 +487,200 @@ void phyai_destroy(phyai_ctx* c) {
   if (c->arena) hipFree(c->arena);
   if (c->cap_stream) hipStreamDestroy(c->cap_stream);
   delete c;
+}
+
+// ---------------------------------------------------------------- joint video/action denoiser
+// PhyAI reading, Figure 4 and Sec. 5.5 third item: the conditional and unconditional branches
+// run as a batch of two over one joint latent/action sequence with full self-attention.
+phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phyai_ctx** out) {
+  if (!out) return PHYAI_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!cfg) return PHYAI_ERR_INVALID_ARG;
+  const phyai_wam_config& g = *cfg;
+  if (g.n_layers < 1 || g.width < 1 || g.n_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 || g.latent_tokens < 0 ||
+      g.action_tokens < 0 || g.latent_tokens + g.action_tokens < 1 || g.latent_dim < 1 || g.action_dim < 1 ||
+      !(g.rms_eps > 0.f))
+    return PHYAI_ERR_INVALID_ARG;
+  if (g.width % 256 || g.width > 2048 || g.mlp_dim % 128 || (g.n_heads * g.head_dim) % 128 ||
+      (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) || g.latent_dim > 256 ||
+      g.action_dim > 256)
+    return PHYAI_ERR_UNSUPPORTED;
+
+  phyai_ctx* c = new phyai_ctx();
+  c->joint = 1;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->wt = W_BF16;
+  c->es_io = 2;
+  c->es_act = 2;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+  Dims& d = c->base;
+  d.L = g.n_layers; d.D = g.width; d.Hq = g.n_heads; d.Hkv = g.n_heads; d.dh = g.head_dim;
+  d.F = g.mlp_dim; d.A = g.action_dim;
+  d.H = g.latent_tokens + g.action_tokens;  // tokens of one branch
+  d.B = 2; d.M = 2 * d.H; d.Mst = d.M;       // rows [0, H): conditional, [H, 2H): unconditional
+  d.P = 0;
+  d.KS = (d.H + 31) / 32 * 32;
+  d.qkv = 3 * g.n_heads * g.head_dim;
+  d.nmod = 2 * g.n_layers + 1;
+  d.N = 1;
+  d.eps = g.rms_eps;
+  d.Lc = 1;                // K/V of the current layer only
+  d.joint = 1;
+  d.ntab = 2;
+  d.rows_per_tab = d.H;
+  d.Tl = g.latent_tokens;
+  d.Cl = g.latent_dim;
+  d.gamma = 0.f;
+  // mirror into cfg the fields the shared calls read
+  c->cfg.n_layers = g.n_layers; c->cfg.width = g.width; c->cfg.n_q_heads = g.n_heads; c->cfg.n_kv_heads = g.n_heads;
+  c->cfg.head_dim = g.head_dim; c->cfg.mlp_dim = g.mlp_dim; c->cfg.action_dim = g.action_dim;
+  c->cfg.chunk_len = d.H; c->cfg.max_prefix_len = 0; c->cfg.max_batch = 2; c->cfg.weight_dtype = PHYAI_BF16;
+  c->cfg.rms_eps = g.rms_eps; c->cfg.max_arena_bytes = g.max_arena_bytes;
+
+  const int L = d.L, D = d.D, F = d.F, A = d.A, Cl = d.Cl, qd = d.Hq * d.dh;
+  Layout lay;
+  const size_t o_w_in = lay.take((size_t)D * Cl * 2), o_b_in = lay.take((size_t)D * 2);
+  const size_t o_w_in2 = lay.take((size_t)D * A * 2), o_b_in2 = lay.take((size_t)D * 2);
+  const size_t o_w_out = lay.take((size_t)Cl * D * 2), o_b_out = lay.take((size_t)Cl * 2);
+  const size_t o_w_out2 = lay.take((size_t)A * D * 2), o_b_out2 = lay.take((size_t)A * 2);
+  const size_t o_w_mod = lay.take((size_t)d.nmod * 2 * D * D * 2), o_b_mod = lay.take((size_t)d.nmod * 2 * D * 2);
+  const size_t o_cond = lay.take((size_t)2 * D * 2);
+  const size_t o_w_qkv = lay.take((size_t)L * d.qkv * D * 2), o_w_o = lay.take((size_t)L * D * qd * 2);
+  const size_t o_w_gu = lay.take((size_t)L * 2 * F * D * 2), o_w_d = lay.take((size_t)L * D * F * 2);
+  const size_t kv_elems = (size_t)d.B * d.Lc * d.Hkv * d.KS * d.dh;
+  const size_t o_kc = lay.take(kv_elems * 2), o_vt = lay.take(kv_elems * 2);
+  const size_t zero_begin = o_kc;
+  const size_t o_x = lay.take(std::max<size_t>((size_t)d.Tl * Cl, 1) * 4);
+  const size_t o_x2 = lay.take(std::max<size_t>((size_t)(d.H - d.Tl) * A, 1) * 4);
+  const size_t o_h = lay.take((size_t)d.M * D * 4), o_ssq = lay.take((size_t)(D / 16) * d.Mst * 4);
+  const size_t mpad = (size_t)(d.M + 15) / 16 * 16;
+  const size_t o_hs = lay.take(mpad * D * 2), o_q = lay.take((size_t)d.M * qd * 2);
+  const size_t o_o = lay.take(mpad * qd * 2), o_act = lay.take(mpad * F * 2);
+  const Plan plan = make_plan(d, c->wt);
+  const int nblk = (d.H + 31) / 32;
+  const size_t attn_ws = (nblk + plan.attn_bps - 1) / plan.attn_bps > 1 ? attn_ws_floats(d, plan) : 1;
+  const size_t o_attn_ws = lay.take(attn_ws * 4), o_attn_cnt = lay.take(attn_counters(d) * 4);
+  const size_t o_gemm_cnt = lay.take(gemm_counters(d) * 4);
+  c->arena_bytes = lay.off;
+  if (g.max_arena_bytes && c->arena_bytes > g.max_arena_bytes) {
+    delete c;
+    return PHYAI_ERR_OOM;
+  }
+  if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+  if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+    hipStreamDestroy(c->cap_stream);
+    delete c;
+    return PHYAI_ERR_OOM;
+  }
+  char* base = static_cast<char*>(c->arena);
+  Bufs& b = c->b;
+  b.w_in = base + o_w_in; b.b_in = base + o_b_in; b.w_in2 = base + o_w_in2; b.b_in2 = base + o_b_in2;
+  b.w_out = base + o_w_out; b.b_out = base + o_b_out; b.w_out2 = base + o_w_out2; b.b_out2 = base + o_b_out2;
+  b.w_mod = base + o_w_mod; b.b_mod = base + o_b_mod; b.cond = base + o_cond;
+  b.w_qkv = base + o_w_qkv; b.w_o = base + o_w_o; b.w_gu = base + o_w_gu; b.w_d = base + o_w_d;
+  b.kc = base + o_kc; b.vt = base + o_vt;
+  b.x = reinterpret_cast<float*>(base + o_x);
+  b.x2 = reinterpret_cast<float*>(base + o_x2);
+  b.h = reinterpret_cast<float*>(base + o_h);
+  b.ssq = reinterpret_cast<float*>(base + o_ssq);
+  b.hs = base + o_hs; b.q = base + o_q; b.o = base + o_o; b.act = base + o_act;
+  b.attn_ws = reinterpret_cast<float*>(base + o_attn_ws);
+  b.attn_cnt = reinterpret_cast<unsigned*>(base + o_attn_cnt);
+  b.gemm_ws = nullptr;  // the tiled GEMMs reduce inside the workgroup
+  b.gemm_cnt = reinterpret_cast<unsigned*>(base + o_gemm_cnt);
+  // keys past the live rows must read as finite; activations and counters start at 0
+  if (hipMemsetAsync(base + zero_begin, 0, c->arena_bytes - zero_begin, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess) {
+    hipFree(c->arena);
+    hipStreamDestroy(c->cap_stream);
+    delete c;
+    return PHYAI_ERR_DEVICE;
+  }
+  *out = c;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_wam_set_weights(phyai_ctx* c, const phyai_wam_weights* w) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "wam_set_weights: not a joint denoiser context");
+  if (!w || !w->w_in_lat || !w->b_in_lat || !w->w_in_act || !w->b_in_act || !w->w_out_lat || !w->b_out_lat ||
+      !w->w_out_act || !w->b_out_act || !w->w_mod || !w->b_mod || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_d)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "wam_set_weights: null weight pointer");
+  const Dims& d = c->base;
+  const int L = d.L, D = d.D, F = d.F, A = d.A, Cl = d.Cl, qd = d.Hq * d.dh;
+  auto cp = [&](const void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(const_cast<void*>(dst), src, bytes, hipMemcpyDeviceToDevice, c->stream);
+  };
+  auto sw = [&](const void* dst, const void* src, int64_t rows, int cols) {
+    return enqueue_swizzle(src, const_cast<void*>(dst), rows, cols, 2, c->stream);
+  };
+  HIPCHK(c, cp(c->b.w_in, w->w_in_lat, (size_t)D * Cl * 2));
+  HIPCHK(c, cp(c->b.b_in, w->b_in_lat, (size_t)D * 2));
+  HIPCHK(c, cp(c->b.w_in2, w->w_in_act, (size_t)D * A * 2));
+  HIPCHK(c, cp(c->b.b_in2, w->b_in_act, (size_t)D * 2));
+  HIPCHK(c, cp(c->b.w_out, w->w_out_lat, (size_t)Cl * D * 2));
+  HIPCHK(c, cp(c->b.b_out, w->b_out_lat, (size_t)Cl * 2));
+  HIPCHK(c, cp(c->b.w_out2, w->w_out_act, (size_t)A * D * 2));
+  HIPCHK(c, cp(c->b.b_out2, w->b_out_act, (size_t)A * 2));
+  HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * 2 * D * D * 2));
+  HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * 2 * D * 2));
+  HIPCHK(c, sw(c->b.w_qkv, w->w_qkv, (int64_t)L * d.qkv, D));
+  HIPCHK(c, sw(c->b.w_o, w->w_o, (int64_t)L * D, qd));
+  HIPCHK(c, sw(c->b.w_gu, w->w_gu, (int64_t)L * 2 * F, D));
+  HIPCHK(c, sw(c->b.w_d, w->w_d, (int64_t)L * D, F));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->have_weights = true;
+  c->have_tables = false;
+  drop_graphs(c);
+  return PHYAI_OK;
+}
+
+phyai_status phyai_wam_set_conditions(phyai_ctx* c, const void* c_cond, const void* c_uncond, float guidance) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "wam_set_conditions: not a joint denoiser context");
+  if (!c_cond || !c_uncond) return fail(c, PHYAI_ERR_INVALID_ARG, "wam_set_conditions: null pointer");
+  if (!std::isfinite(guidance)) return fail(c, PHYAI_ERR_INVALID_ARG, "wam_set_conditions: non-finite guidance");
+  const size_t bytes = (size_t)c->base.D * 2;
+  char* dst = static_cast<char*>(const_cast<void*>(c->b.cond));
+  HIPCHK(c, hipMemcpyAsync(dst, c_cond, bytes, hipMemcpyDeviceToDevice, c->stream));
+  HIPCHK(c, hipMemcpyAsync(dst + bytes, c_uncond, bytes, hipMemcpyDeviceToDevice, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->base.gamma = guidance;
+  c->have_cond = true;
+  c->have_tables = false;  // the modulation tables fold the conditions in
+  drop_graphs(c);          // the guidance scale is a launch argument
+  return PHYAI_OK;
+}
+
+phyai_status phyai_wam_denoise(phyai_ctx* c, const float* z_lat, const float* z_act, int n_steps, float* z_lat_out,
+                               float* z_act_out) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "wam_denoise: not a joint denoiser context");
+  const Dims& bd = c->base;
+  const size_t lat_bytes = (size_t)bd.Tl * bd.Cl * 4, act_bytes = (size_t)(bd.H - bd.Tl) * bd.A * 4;
+  if ((lat_bytes && (!z_lat || !z_lat_out)) || (act_bytes && (!z_act || !z_act_out)))
+    return fail(c, PHYAI_ERR_INVALID_ARG, "wam_denoise: null pointer");
+  if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "wam_denoise: weights not set");
+  if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "wam_denoise: timestep tables not set");
+  if (n_steps != c->n_steps) return fail(c, PHYAI_ERR_INVALID_ARG, "wam_denoise: n_steps differs from the tables");
+  const Dims d = launch_dims(c, 2, 0, n_steps);
+  const Plan plan = make_plan(d, c->wt);
+  if (lat_bytes) HIPCHK(c, hipMemcpyAsync(c->b.x, z_lat, lat_bytes, hipMemcpyDeviceToDevice, c->stream));
+  if (act_bytes) HIPCHK(c, hipMemcpyAsync(c->b.x2, z_act, act_bytes, hipMemcpyDeviceToDevice, c->stream));
+  const phyai_status st = run_loop(c, d, plan, "wam_denoise");
+  if (st != PHYAI_OK) return st;
+  if (lat_bytes) HIPCHK(c, hipMemcpyAsync(z_lat_out, c->b.x, lat_bytes, hipMemcpyDeviceToDevice, c->stream));
+  if (act_bytes) HIPCHK(c, hipMemcpyAsync(z_act_out, c->b.x2, act_bytes, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
 }
 
 phyai_status phyai_quantize_int4_g128(const float* w, int64_t rows, int64_t cols, uint8_t* packed,

@@ -48,67 +48,77 @@ __global__ void k_embed(const float* t, int N, int D, double* e) {
   e[idx] = c < half ? sin(ang) : cos(ang);
 }
 
-// One wave per row o of W_mod[j] (j = norm, o in [0, 2D)): m_k = W_mod[j][o] . e(t_k) + b_mod[j][o]
-// for every step k, accumulated in fp64.
+// One wave per (table tb, row o of W_mod[j]) (j = norm, o in [0, 2D)):
+// m_k = W_mod[j][o] . (e(t_k) + cond_tb) + b_mod[j][o] for every step k, accumulated in fp64.
+// cond (io [ntab][D]) may be null (no condition: a single table).
 template <class IOT>
-__global__ __launch_bounds__(256) void k_modulation(const IOT* w_mod, const IOT* b_mod, const double* e,
-                                                    int N, int nmod, int D, float* mod) {
+__global__ __launch_bounds__(256) void k_modulation(const IOT* w_mod, const IOT* b_mod, const IOT* cond,
+                                                    const double* e, int N, int nmod, int D, int ntab, float* mod) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= nmod * 2 * D) return;
-  const int j = row / (2 * D), o = row % (2 * D);
-  const IOT* wr = w_mod + (size_t)row * D;
-  const double bias = (double)to_f32(b_mod[row]);
+  if (row >= ntab * nmod * 2 * D) return;
+  const int tb = row / (nmod * 2 * D), wrow = row % (nmod * 2 * D);
+  const int j = wrow / (2 * D), o = wrow % (2 * D);
+  const IOT* wr = w_mod + (size_t)wrow * D;
+  const double bias = (double)to_f32(b_mod[wrow]);
   for (int k0 = 0; k0 < N; k0 += 8) {
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int c = lane; c < D; c += 64) {
       const double wv = (double)to_f32(wr[c]);
+      const double cv = cond ? (double)to_f32(cond[(size_t)tb * D + c]) : 0.0;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        if (k0 + kk < N) acc[kk] += wv * e[(size_t)(k0 + kk) * D + c];
+        if (k0 + kk < N) acc[kk] += wv * (e[(size_t)(k0 + kk) * D + c] + cv);
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const double v = wave_sum(acc[kk]);
       if (lane == 0 && k0 + kk < N)
-        mod[(((size_t)(k0 + kk) * nmod + j) * 2 + (o >= D ? 1 : 0)) * D + (o % D)] = (float)(v + bias);
+        mod[((((size_t)(k0 + kk) * ntab + tb) * nmod + j) * 2 + (o >= D ? 1 : 0)) * D + (o % D)] = (float)(v + bias);
     }
   }
 }
 
-// Norm-folded biases: for every step k, c = W shift_j(t_k) for the QKV rows (j = 2l),
-// the gate/up rows (j = 2l+1) and the out-projection rows (j = 2L).  One wave per row.
+// Norm-folded biases: for every step k and table tb, c = W shift_j(t_k) for the QKV rows
+// (j = 2l), the gate/up rows (j = 2l+1) and the out-projection rows (j = 2L; the joint
+// denoiser has latent then action out-projection rows).  One wave per (table, row).
 template <class WT, class IOT>
-__global__ __launch_bounds__(256) void k_shift_proj(Dims d, Bufs bf, const float* mod, float* cvec) {
+__global__ __launch_bounds__(256) void k_shift_proj(Dims d, Bufs bf, const float* mod, float* cvec, int n_out1,
+                                                    int n_out2) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nq = d.L * d.qkv, ng = d.L * 2 * d.F;
-  if (row >= nq + ng + d.A) return;
-  int j, off;
+  const int per_tab = nq + ng + n_out1 + n_out2;
+  const int row0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row0 >= d.ntab * per_tab) return;
+  const int tb = row0 / per_tab, row = row0 % per_tab;
   WRow<WT, true> wq{static_cast<const WT*>(bf.w_qkv), bf.s_qkv, d.D};
   WRow<WT, true> wg{static_cast<const WT*>(bf.w_gu), bf.s_gu, d.D};
   WRow<IOT, false> wo{static_cast<const IOT*>(bf.w_out), nullptr, d.D};
-  int which;
+  WRow<IOT, false> wo2{static_cast<const IOT*>(bf.w_out2), nullptr, d.D};
+  int which, j, off;
   size_t n;
   if (row < nq) {
     which = 0; n = row; j = 2 * (row / d.qkv); off = row;
   } else if (row < nq + ng) {
     which = 1; n = row - nq; j = 2 * ((row - nq) / (2 * d.F)) + 1; off = bf.cv_gu_off + (row - nq);
-  } else {
+  } else if (row < nq + ng + n_out1) {
     which = 2; n = row - nq - ng; j = 2 * d.L; off = bf.cv_out_off + (row - nq - ng);
+  } else {
+    which = 3; n = row - nq - ng - n_out1; j = 2 * d.L; off = bf.cv_out_off + (row - nq - ng);
   }
   for (int k0 = 0; k0 < d.N; k0 += 8) {
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int c = lane; c < d.D; c += 64) {
-      const double wv = which == 0 ? wq.at(n, c) : which == 1 ? wg.at(n, c) : wo.at(n, c);
+      const double wv = which == 0 ? wq.at(n, c) : which == 1 ? wg.at(n, c) : which == 2 ? wo.at(n, c) : wo2.at(n, c);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        if (k0 + kk < d.N) acc[kk] += wv * (double)mod[(((size_t)(k0 + kk) * d.nmod + j) * 2 + 1) * d.D + c];
+        if (k0 + kk < d.N)
+          acc[kk] += wv * (double)mod[((((size_t)(k0 + kk) * d.ntab + tb) * d.nmod + j) * 2 + 1) * d.D + c];
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const double v = wave_sum(acc[kk]);
-      if (lane == 0 && k0 + kk < d.N) cvec[(size_t)(k0 + kk) * bf.cv_stride + off] = (float)v;
+      if (lane == 0 && k0 + kk < d.N) cvec[((size_t)(k0 + kk) * d.ntab + tb) * bf.cv_stride + off] = (float)v;
     }
   }
 }
@@ -215,13 +225,17 @@ static hipError_t tables_impl(const Dims& d, const Bufs& b, const float* t_dev, 
   hipLaunchKernelGGL(k_embed, dim3((ne + 255) / 256), dim3(256), 0, st, t_dev, d.N, d.D, e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int rows = d.nmod * 2 * d.D;
-  hipLaunchKernelGGL((k_modulation<IOT>), dim3((rows + 3) / 4), dim3(256), 0, st,
-                     static_cast<const IOT*>(b.w_mod), static_cast<const IOT*>(b.b_mod), e, d.N, d.nmod, d.D, mod);
+  const int rows = d.ntab * d.nmod * 2 * d.D;
+  hipLaunchKernelGGL((k_modulation<IOT>), dim3((rows + 3) / 4), dim3(256), 0, st, static_cast<const IOT*>(b.w_mod),
+                     static_cast<const IOT*>(b.b_mod), static_cast<const IOT*>(b.cond), e, d.N, d.nmod, d.D, d.ntab,
+                     mod);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int rows2 = d.L * d.qkv + d.L * 2 * d.F + d.A;
-  hipLaunchKernelGGL((k_shift_proj<WT, IOT>), dim3((rows2 + 3) / 4), dim3(256), 0, st, d, b, mod, cvec);
+  // out-projection rows: the expert has A; the joint denoiser has Cl latent + A action rows
+  const int n_out1 = d.joint ? d.Cl : d.A, n_out2 = d.joint ? d.A : 0;
+  const int rows2 = d.ntab * (d.L * d.qkv + d.L * 2 * d.F + n_out1 + n_out2);
+  hipLaunchKernelGGL((k_shift_proj<WT, IOT>), dim3((rows2 + 3) / 4), dim3(256), 0, st, d, b, mod, cvec, n_out1,
+                     n_out2);
   return hipGetLastError();
 }
 

@@ -167,6 +167,66 @@ phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
  * overwrites the context's activations, state and chunk K/V rows (re-run phyai_denoise after). */
 phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, int reps);
 
+/* ---------------------------------------------------------------- joint video/action denoiser
+ * (PhyAI reading, Figure 4 and Sec. 5.5 third item; Sec. 5.4): latent video tokens and action
+ * tokens evolve together in one sequence under full self-attention (no cached prefix, no
+ * mask, nothing kept across steps); a conditional and an unconditional branch run as a
+ * batch of two and are combined before the update:
+ *   h  = [z_lat W_in_lat^T + b_in_lat ; z_act W_in_act^T + b_in_act]      (T = Tl + Ta rows)
+ *   per branch b (condition c_b) the layer stack of the action expert with Hq = Hkv heads,
+ *   modulation [scale_j; shift_j](t) = W_mod[j] (e(t) + c_b) + b_mod[j], keys = the T tokens;
+ *   v_b = adaRMS(h; 2L) W_out_type^T + b_out_type  (latent rows: *_lat, action rows: *_act)
+ *   v  = v_u + gamma (v_c - v_u),   z += dt_k v
+ * The same context calls apply: phyai_set_timestep_tables, phyai_set_graph_mode, phyai_sync,
+ * phyai_last_error, phyai_get_modulation ([n_steps][2][2L+1][2][D], branch-major: cond then
+ * uncond), phyai_enqueue_kernel_repeat (which 0..4 as for the expert, 5 out-projections +
+ * guidance + Euler + in-projections, 6 first in-projections) and phyai_destroy.
+ * phyai_set_prefix_kv and phyai_denoise refuse a joint context (PHYAI_ERR_BAD_STATE), and the
+ * phyai_wam_* calls refuse an action-expert context. */
+
+/* bf16 weights, fp32 accumulation, residual stream, statistics, softmax and state.
+ * Constraints (else PHYAI_ERR_UNSUPPORTED): width a multiple of 256 and <= 2048; mlp_dim and
+ * n_heads*head_dim multiples of 128; head_dim 32, 64, 128 or 256; latent_dim and action_dim
+ * in [1, 256]; latent_tokens, action_tokens >= 0 with at least one token. */
+typedef struct {
+  int n_layers, width, n_heads, head_dim, mlp_dim;
+  int latent_tokens, latent_dim, action_tokens, action_dim;
+  float rms_eps;              /* > 0 */
+  size_t max_arena_bytes;     /* 0 = no limit */
+} phyai_wam_config;
+
+/* bf16 dev pointers, row-major [out][in]:
+ *   w_in_lat [D][Cl], b_in_lat [D], w_in_act [D][A], b_in_act [D],
+ *   w_out_lat [Cl][D], b_out_lat [Cl], w_out_act [A][D], b_out_act [A],
+ *   w_mod [2L+1][2D][D], b_mod [2L+1][2D]  (as in phyai_weights),
+ *   w_qkv [L][3 H dh][D] (q heads, k heads, v heads), w_o [L][D][H dh],
+ *   w_gu [L][2F][D] (gate rows, then up rows), w_d [L][D][F]. */
+typedef struct {
+  const void *w_in_lat, *b_in_lat, *w_in_act, *b_in_act;
+  const void *w_out_lat, *b_out_lat, *w_out_act, *b_out_act;
+  const void *w_mod, *b_mod, *w_qkv, *w_o, *w_gu, *w_d;
+} phyai_wam_weights;
+
+/* Create a joint-denoiser context on the current HIP device (arena for the weights, the two
+ * branches' activations and one layer of K/V).  Same stream and error rules as phyai_create. */
+phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phyai_ctx** out);
+
+/* Copy the weights (layouts above) into the arena; invalidates tables and graphs. */
+phyai_status phyai_wam_set_weights(phyai_ctx* ctx, const phyai_wam_weights* w);
+
+/* Branch conditions and guidance scale: c_cond, c_uncond dev bf16 [D] (added to the timestep
+ * embedding of the conditional / unconditional branch), guidance gamma finite.  Must precede
+ * phyai_set_timestep_tables (the tables fold the conditions in); invalidates tables and graphs. */
+phyai_status phyai_wam_set_conditions(phyai_ctx* ctx, const void* c_cond, const void* c_uncond,
+                                      float guidance);
+
+/* Run the guided Euler loop from z = (z_lat, z_act) at t_0 to t = 0.  z_lat, z_lat_out: dev
+ * float [latent_tokens][latent_dim]; z_act, z_act_out: dev float [action_tokens][action_dim]
+ * (a pointer may be NULL when its token count is 0).  n_steps must equal the table length.
+ * Asynchronous on the context stream, one hipGraph launch (captured once per n_steps). */
+phyai_status phyai_wam_denoise(phyai_ctx* ctx, const float* z_lat, const float* z_act, int n_steps,
+                               float* z_lat_out, float* z_act_out);
+
 /* Library version string. */
 const char* phyai_version(void);
 

@@ -31,6 +31,7 @@ import numpy as np
 __all__ = [
     "ExpertDims", "CONFIGS", "TENSOR_IDS", "normal", "bf16_bits", "bf16_values",
     "make_expert_inputs", "expert_param_shapes", "WamDims", "WAM_CONFIGS", "make_wam_inputs",
+    "wam_device_inputs",
 ]
 
 # one fixed id per tensor; never reorder (changing an id changes every draw)
@@ -210,4 +211,30 @@ def make_wam_inputs(d: WamDims, seed: int = 0) -> dict:
     out["z_act"] = normal(seed, "wam_z_act", (d.action_tokens, d.action_dim))
     out["c_cond"] = bf16_values(normal(seed, "wam_cond", (d.width,)))
     out["c_uncond"] = np.zeros(d.width, np.float32)
+    return out
+
+
+def wam_device_inputs(d: WamDims, seed: int = 0, device: str = "cuda") -> dict:
+    """Full-size joint-denoiser inputs drawn directly on the device (1.9 B weights are too
+    many to draw on the host in a test): torch's seeded device generator, one stream per
+    tensor (seed * 1000 + tensor id), same distributions as ``make_wam_inputs`` (weights
+    N(0, std^2) rounded to bf16, latents/actions N(0, 1) fp32, condition N(0, 1) bf16, zero
+    unconditional vector).  Not comparable draw-for-draw with ``make_wam_inputs``."""
+    import torch
+    out = {}
+
+    def draw(name, shape, std, dtype):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed) * 1000 + TENSOR_IDS["wam_" + name if "wam_" + name in TENSOR_IDS else name])
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(dtype).contiguous()
+
+    for name, shape in wam_param_shapes(d).items():
+        out[name] = draw(name, shape, d.weight_std, torch.bfloat16)
+    out["z_lat"] = draw("z_lat", (d.latent_tokens, d.latent_dim), 1.0, torch.float32)
+    out["z_act"] = draw("z_act", (d.action_tokens, d.action_dim), 1.0, torch.float32)
+    out["c_cond"] = draw("cond", (d.width,), 1.0, torch.bfloat16)
+    out["c_uncond"] = torch.zeros(d.width, dtype=torch.bfloat16, device=device)
     return out

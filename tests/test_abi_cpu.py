@@ -89,3 +89,37 @@ def test_quantizer_argument_checks(lib):
     assert lib.phyai_quantize_int4_g128(None, -1, 128, None, None, None) == 1
     assert lib.phyai_quantize_int4_g128(None, 0, 128, None, None, None) == 0    # empty: nothing to do
     assert lib.phyai_quantize_int4_g128(None, 4, 128, None, None, None) == 1   # null pointers
+
+
+def _wcfg(**kw):
+    base = dict(n_layers=2, width=256, n_heads=4, head_dim=64, mlp_dim=1024, latent_tokens=200, latent_dim=16,
+                action_tokens=24, action_dim=32, rms_eps=1e-6, max_arena_bytes=0)
+    base.update(kw)
+    return fm.WamConfig(**base)
+
+
+def _wcreate(lib, cfg):
+    h = ctypes.c_void_p()
+    return lib.phyai_wam_create(ctypes.byref(cfg) if cfg is not None else None, None, ctypes.byref(h)), h
+
+
+def test_joint_create_rejects_bad_config_without_a_device(lib):
+    assert _wcreate(lib, None)[0] == 1
+    assert _wcreate(lib, _wcfg(n_layers=0))[0] == 1
+    assert _wcreate(lib, _wcfg(latent_tokens=0, action_tokens=0))[0] == 1   # no tokens at all
+    assert _wcreate(lib, _wcfg(latent_tokens=-1))[0] == 1
+    assert _wcreate(lib, _wcfg(rms_eps=-1.0))[0] == 1
+    assert _wcreate(lib, _wcfg(width=200))[0] == 5
+    assert _wcreate(lib, _wcfg(width=4096))[0] == 5
+    assert _wcreate(lib, _wcfg(head_dim=48))[0] == 5
+    assert _wcreate(lib, _wcfg(n_heads=3))[0] == 5                         # 3 x 64 not a multiple of 128
+    assert _wcreate(lib, _wcfg(latent_dim=300))[0] == 5
+    assert _wcreate(lib, _wcfg(mlp_dim=1000))[0] == 5
+    st, h = _wcreate(lib, _wcfg(n_layers=0))
+    assert h.value is None
+
+
+def test_joint_null_context_calls_fail_cleanly(lib):
+    assert lib.phyai_wam_set_weights(None, None) == 1
+    assert lib.phyai_wam_set_conditions(None, None, None, 3.0) == 1
+    assert lib.phyai_wam_denoise(None, None, None, 1, None, None) == 1

@@ -1,0 +1,173 @@
+"""GPU parity of the joint video/action denoiser (guided branch pair) through the C ABI.
+
+Reduced shapes against the float64 oracle (bf16 weights and GEMM inputs, fp32
+accumulation: max error / max |ref| <= 2e-2); the full 28-layer, 4128-token shape through
+properties that hold at any size (equal branch conditions make the guidance scale
+irrelevant, bitwise; graph replay equals eager launches, bitwise; the state stays finite).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import expert as ex
+from oracle import wam as owam
+
+from gpu_util import rel_err
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WAM_CONFIGS["wam_tiny"]
+FULL = synth.WAM_CONFIGS["wam"]
+TOL = 2e-2
+
+
+def _dev(inputs):
+    import torch
+    out = {}
+    for k, v in inputs.items():
+        t = torch.from_numpy(np.ascontiguousarray(v)).cuda()
+        out[k] = t if k in ("z_lat", "z_act") else t.to(torch.bfloat16).contiguous()
+    return out
+
+
+def _make(d, dev, t, guidance=None, graph=True):
+    import flow_matching_action_cached_amd as fm
+    jd = fm.JointDenoiser.from_dims(d)
+    jd.set_weights(dev)
+    jd.set_conditions(dev["c_cond"], dev["c_uncond"], d.guidance if guidance is None else guidance)
+    jd.set_timestep_tables(t)
+    jd.set_graph_mode(graph)
+    return jd
+
+
+def _run(jd, dev):
+    zl, za = jd.denoise(dev["z_lat"], dev["z_act"])
+    jd.sync()
+    return zl.cpu().numpy(), za.cpu().numpy()
+
+
+def _check_vs_oracle(d, seed=0):
+    inp = synth.make_wam_inputs(d, seed)
+    t = ex.schedule(d.n_steps)
+    jd = _make(d, _dev(inp), t)
+    zl, za = _run(jd, _dev(inp))
+    rl, ra = owam.denoise(inp, d, t)
+    got = np.concatenate([zl.ravel(), za.ravel()])
+    ref = np.concatenate([rl.ravel(), ra.ravel()])
+    err = rel_err(got, ref)
+    print(f"joint {d.latent_tokens}+{d.action_tokens} tokens L={d.n_layers} N={d.n_steps}: rel err {err:.3e}",
+          flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL
+    return jd
+
+
+def test_joint_tiny_matches_oracle():
+    _check_vs_oracle(TINY)
+
+
+@pytest.mark.parametrize("lat,act", [(0, 24), (37, 0), (5, 3)])
+def test_joint_ragged_token_mixes_match_oracle(lat, act):
+    """Only actions, only latents, and a token count far from a tile multiple."""
+    _check_vs_oracle(dataclasses.replace(TINY, latent_tokens=lat, action_tokens=act, n_steps=2))
+
+
+def test_joint_modulation_tables_match_oracle():
+    d = dataclasses.replace(TINY, n_steps=3)
+    inp = synth.make_wam_inputs(d, 1)
+    t = ex.schedule(d.n_steps)
+    jd = _make(d, _dev(inp), t)
+    got = jd.get_modulation().cpu().numpy()           # [N][branch][nmod][2][D]
+    for k in range(d.n_steps):
+        for b, c in enumerate((inp["c_cond"], inp["c_uncond"])):
+            ref = owam.modulation(t[k], c, inp["w_mod"], inp["b_mod"])
+            np.testing.assert_allclose(got[k, b], ref, rtol=1e-5, atol=1e-5)
+
+
+def test_joint_graph_equals_eager_and_replays_bitwise():
+    d = TINY
+    inp = synth.make_wam_inputs(d, 2)
+    dev = _dev(inp)
+    t = ex.schedule(d.n_steps)
+    g = _make(d, dev, t, graph=True)
+    a1 = _run(g, dev)
+    a2 = _run(g, dev)
+    g.set_graph_mode(False)
+    e1 = _run(g, dev)
+    for x, y in ((a1, a2), (a1, e1)):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+
+
+def test_joint_guidance_change_recaptures():
+    """A new guidance scale is a new launch argument: the loop must follow it."""
+    d = dataclasses.replace(TINY, n_steps=2)
+    inp = synth.make_wam_inputs(d, 3)
+    dev = _dev(inp)
+    t = ex.schedule(d.n_steps)
+    jd = _make(d, dev, t, guidance=1.0)
+    _run(jd, dev)
+    jd.set_conditions(dev["c_cond"], dev["c_uncond"], 5.0)
+    jd.set_timestep_tables(t)
+    zl, za = _run(jd, dev)
+    rl, ra = owam.denoise(inp, d, t, guidance=5.0)
+    assert rel_err(np.concatenate([zl.ravel(), za.ravel()]), np.concatenate([rl.ravel(), ra.ravel()])) <= TOL
+
+
+def test_joint_call_order_and_kind_errors():
+    import torch
+    import flow_matching_action_cached_amd as fm
+    d = TINY
+    jd = fm.JointDenoiser.from_dims(d)
+    z = torch.zeros((d.latent_tokens, d.latent_dim), device="cuda")
+    a = torch.zeros((d.action_tokens, d.action_dim), device="cuda")
+    with pytest.raises(fm.PhyaiError) as e:
+        jd.set_timestep_tables([1.0, 0.5])            # weights not set
+    assert e.value.status == 2
+    lib = fm.load_library()
+    assert lib.phyai_set_prefix_kv(jd._h, z.data_ptr(), z.data_ptr(), 1, 1) == 2
+    assert lib.phyai_denoise(jd._h, z.data_ptr(), 1, 1, z.data_ptr()) == 2
+    assert lib.phyai_wam_denoise(jd._h, z.data_ptr(), a.data_ptr(), 1, z.data_ptr(), a.data_ptr()) == 2
+    inp = _dev(synth.make_wam_inputs(d, 0))
+    jd.set_weights(inp)
+    with pytest.raises(fm.PhyaiError) as e:
+        jd.set_timestep_tables([1.0, 0.5])            # conditions not set
+    assert e.value.status == 2
+    assert lib.phyai_wam_set_conditions(jd._h, inp["c_cond"].data_ptr(), inp["c_uncond"].data_ptr(),
+                                        float("nan")) == 1
+    # an action-expert context refuses the joint calls
+    e_ctx = fm.ActionExpert.from_dims(synth.CONFIGS["tiny"])
+    assert lib.phyai_wam_denoise(e_ctx._h, z.data_ptr(), a.data_ptr(), 1, z.data_ptr(), a.data_ptr()) == 2
+    e_ctx.close()
+    jd.close()
+
+
+@pytest.mark.slow
+def test_joint_full_shape_properties():
+    """28 layers, width 2048, 4096 + 32 tokens, 8 steps, device-drawn inputs.  With both
+    branches on the same condition the two halves of every GEMM and attention launch see
+    identical rows, so v_c == v_u bitwise and the guidance scale must not change one bit."""
+    import torch
+    d = FULL
+    dev = synth.wam_device_inputs(d, 0)
+    dev["c_uncond"] = dev["c_cond"].clone()
+    t = ex.schedule(d.n_steps)
+    jd = _make(d, dev, t, guidance=0.0)
+    a = _run(jd, dev)
+    jd.set_conditions(dev["c_cond"], dev["c_uncond"], 7.0)
+    jd.set_timestep_tables(t)
+    b = _run(jd, dev)
+    assert np.isfinite(a[0]).all() and np.isfinite(a[1]).all()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # distinct conditions: guidance now matters, state finite, eager == graph
+    c_unc = torch.zeros_like(dev["c_cond"])
+    jd.set_conditions(dev["c_cond"], c_unc, 3.0)
+    jd.set_timestep_tables(t)
+    g = _run(jd, dev)
+    jd.set_graph_mode(False)
+    e = _run(jd, dev)
+    assert np.isfinite(g[0]).all() and np.isfinite(g[1]).all()
+    assert not np.array_equal(g[0], a[0])
+    assert np.array_equal(g[0], e[0]) and np.array_equal(g[1], e[1])
+    jd.close()
