@@ -83,6 +83,25 @@ def batch_flops(d):
     return d.n_steps * d.n_layers * (lin + attn)
 
 
+def wam_flops(d):
+    """Algorithmic MFMA flops of one joint chunk: both guidance branches (2 x T token rows)
+    through the four linears of every layer plus full self-attention over the T tokens,
+    times layers and steps (in/out projections and element-wise work not counted)."""
+    T = d.latent_tokens + d.action_tokens
+    rows = 2 * T
+    hd = d.n_heads * d.head_dim
+    per_layer = 3 * hd * d.width + d.width * hd + 3 * d.mlp_dim * d.width
+    return d.n_steps * d.n_layers * (2 * rows * per_layer + 4 * rows * T * hd)
+
+
+def wam_kernel_flops(d):
+    T = d.latent_tokens + d.action_tokens
+    rows = 2 * T
+    hd = d.n_heads * d.head_dim
+    return {"qkv": 2 * rows * 3 * hd * d.width, "attention": 4 * rows * T * hd, "o_proj": 2 * rows * d.width * hd,
+            "gate_up": 2 * rows * 2 * d.mlp_dim * d.width, "down": 2 * rows * d.mlp_dim * d.width}
+
+
 def time_chunks(ex, noise, out, steps, warmup, torch):
     for _ in range(warmup):
         ex.denoise(noise, out)
@@ -298,6 +317,47 @@ def main():
         }
         print(f"[bench] batch-32 variant: {ms32:.3f} ms per batch chunk, {32000.0 / ms32:.1f} chunks/s",
               file=sys.stderr, flush=True)
+
+        # joint video/action denoiser, guided pair: 28 layers, width 2048, 4096 + 32 tokens, 8 steps
+        dw = synth.WAM_CONFIGS["wam"]
+        wdev = synth.wam_device_inputs(dw, 0)
+        jd = fm.JointDenoiser.from_dims(dw)
+        jd.set_weights(wdev)
+        jd.set_conditions(wdev["c_cond"], wdev["c_uncond"], dw.guidance)
+        jd.set_timestep_tables(schedule(dw.n_steps))
+        ol, oa = torch.empty_like(wdev["z_lat"]), torch.empty_like(wdev["z_act"])
+        for _ in range(2):
+            jd.denoise(wdev["z_lat"], wdev["z_act"], ol, oa)
+        torch.cuda.synchronize()
+        nw = max(3, args.steps // 10)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(nw):
+            jd.denoise(wdev["z_lat"], wdev["z_act"], ol, oa)
+        b.record()
+        torch.cuda.synchronize()
+        msw = a.elapsed_time(b) / nw
+        ktw = kernel_times(jd, 5, torch)
+        jd.close()
+        del wdev
+        flw = wam_flops(dw)
+        kfl = wam_kernel_flops(dw)
+        domw = max(kfl, key=lambda k: ktw[k])
+        variants["wam_joint_cfg_pair"] = {
+            "ms_per_chunk": round(msw, 3), "chunks_per_s": round(1000.0 / msw, 3),
+            "algorithmic_tflop": round(flw / 1e12, 2),
+            "mfma_frac": round(flw / (msw * 1e-3) / MFMA_PEAK_TFLOPS / 1e12, 4),
+            "kernel_us": {k: round(v, 1) for k, v in ktw.items()},
+            "kernel_mfma_frac": {k: round(kfl[k] / (ktw[k] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4) for k in kfl},
+            "roofline": {"kernel": domw, "bound": "mfma", "unit": "TFLOP/s",
+                         "achieved": round(kfl[domw] / (ktw[domw] * 1e-6) / 1e12, 1), "peak": MFMA_PEAK_TFLOPS,
+                         "frac": round(kfl[domw] / (ktw[domw] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
+            "config": {"layers": dw.n_layers, "width": dw.width, "heads": f"{dw.n_heads} x {dw.head_dim}",
+                       "mlp": dw.mlp_dim, "tokens": f"{dw.latent_tokens}x{dw.latent_dim} latent + "
+                                                    f"{dw.action_tokens}x{dw.action_dim} action",
+                       "branches": 2, "guidance": dw.guidance, "euler_steps": dw.n_steps},
+        }
+        print(f"[bench] joint variant: {msw:.2f} ms per chunk", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
