@@ -179,6 +179,15 @@ __device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t by
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding (loads
+// complete in issue order), leaving the LDS and export counters alone.  gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Arrival of one workgroup (all threads call it) at a split reduction with n_parts
 // participants.  True for exactly the last arrival; that workgroup resets the counter.
 __device__ __forceinline__ bool split_arrive_wg(unsigned* counter, unsigned n_parts, unsigned* lds_flag) {

@@ -20,22 +20,47 @@ namespace phyai {
 #define PHYAI_GLOBAL_AS __attribute__((address_space(1)))
 #define PHYAI_LDS_AS __attribute__((address_space(3)))
 
-template <int WMT, int WNT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch g, int tilesN) {
+// Waits of the pipeline: stage ks has landed once at most `after` later stages (LPW loads
+// each) are still in flight.
+template <int LPW, int NSTG>
+__device__ __forceinline__ void wait_stage(int after) {
+  if constexpr (NSTG >= 4) {
+    if (after >= 2) { wait_vmem_le<2 * LPW>(); return; }
+  }
+  if constexpr (NSTG >= 3) {
+    if (after >= 1) { wait_vmem_le<LPW>(); return; }
+  }
+  wait_vmem_le<0>();
+}
+
+// WGM x WGN waves, each owning a 16*WMT x 16*WNT sub-tile; NSTG stages of 32*BKB
+// k-columns in LDS, up to NSTG-1 of them in flight while one feeds the MFMAs.
+template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch g, int tilesN,
+                                                               int tilesM) {
   typedef bf16 AT;
-  constexpr int BMT = 2 * WMT, BNT = 2 * WNT;  // 16-row / 16-column tiles per workgroup
-  constexpr int BKB = 2;                       // 32-wide k-blocks per stage
+  constexpr int NW = WGM * WGN;
+  constexpr int BMT = WGM * WMT, BNT = WGN * WNT;  // 16-row / 16-column tiles per workgroup
+  constexpr int LA = BMT * BKB, LB = BNT * BKB;    // 1 KB fragment blocks per stage
+  constexpr int LPW = (LA + LB) / NW;              // direct-to-LDS loads per wave per stage
   constexpr int BM = 16 * BMT;
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_GEGLU);
+  static_assert((LA + LB) % NW == 0, "stage loads split evenly over the waves");
+  static_assert(NSTG >= 2 && NSTG <= 4, "pipeline depth");
   static_assert(EPI != EPI_GEGLU || WNT % 2 == 0, "gate/up tiles come in pairs");
-  __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][BMT * BKB][64];
-  __shared__ __attribute__((aligned(16))) u32x4 lds_b[2][BNT * BKB][64];
+  static_assert(BM <= 64 * NW, "one thread per tile row for the row statistics");
+  __shared__ __attribute__((aligned(16))) u32x4 lds[NSTG][LA + LB][64];
   __shared__ float rinv_s[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
-  const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
+  const int wm = w / WGN, wn = w % WGN;
+  // XCD-aware tile order: consecutive workgroups go to different XCDs (round robin over 8),
+  // so give each XCD a contiguous run of tiles (shared operand rows/columns stay in its L2).
+  const int ntiles = tilesM * tilesN;
+  int tile = blockIdx.x;
+  if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int tn = tile % tilesN, tm = tile / tilesN;
   const int nstage = g.K / 32 / BKB;
   const int mtiles = (d.M + 15) / 16;  // 16-row tiles present in the activation buffer
   const AT* A = static_cast<const AT*>(g.A);
@@ -47,23 +72,26 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
     if constexpr (EPI == EPI_GEGLU) return (vt & 1) ? (g.n_second >> 4) + (vt >> 1) : (vt >> 1);
     return vt;
   };
-  // one stage: BMT*BKB activation blocks and BNT*BKB weight blocks, wave w copies every 4th
+  // one stage: LA activation blocks then LB weight blocks; wave w copies blocks w, w+NW, ...
   auto issue = [&](int ks, int buf) {
 #pragma unroll
-    for (int blk = w; blk < BMT * BKB; blk += 4) {
-      const int rt = min(tm * BMT + blk / BKB, mtiles - 1);  // past the last rows: any valid tile
-      const AT* src = A + sw_frag(rt, ks * BKB + blk % BKB, g.K, lane);
-      __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&lds_a[buf][blk][0], 16,
-                                       0, 0);
-    }
-#pragma unroll
-    for (int blk = w; blk < BNT * BKB; blk += 4) {
-      const AT* src = W + sw_frag(wtile(tn * BNT + blk / BKB), ks * BKB + blk % BKB, g.K, lane);
-      __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&lds_b[buf][blk][0], 16,
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = w + i * NW;
+      const AT* src;
+      if (blk < LA) {
+        const int rt = min(tm * BMT + blk / BKB, mtiles - 1);  // past the last rows: any valid tile
+        src = A + sw_frag(rt, ks * BKB + blk % BKB, g.K, lane);
+      } else {
+        const int b2 = blk - LA;
+        src = W + sw_frag(wtile(tn * BNT + b2 / BKB), ks * BKB + b2 % BKB, g.K, lane);
+      }
+      __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&lds[buf][blk][0], 16,
                                        0, 0);
     }
   };
-  issue(0, 0);
+#pragma unroll
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < nstage) issue(s, s);
 
   if (NORM && tid < BM) {
     // row statistics of this tile's rows: D/16 partial sums per row, in column order
@@ -86,22 +114,33 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
 #pragma unroll
     for (int j = 0; j < WNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < nstage; ++ks) {
-    wait_all_mem();   // this wave's copies of stage ks have landed
-    __syncthreads();  // ... and everyone's; everyone is also done reading stage ks-1
-    if (ks + 1 < nstage) issue(ks + 1, (ks + 1) & 1);
-    const int buf = ks & 1;
+  // main loop, unrolled by the pipeline depth so every LDS buffer index is a constant
+  for (int ks0 = 0; ks0 < nstage; ks0 += NSTG) {
 #pragma unroll
-    for (int kb = 0; kb < BKB; ++kb) {
-      bf16x8 af[WMT], bw[WNT];
+    for (int j = 0; j < NSTG; ++j) {
+      const int ks = ks0 + j;
+      if (ks < nstage) {
+        wait_stage<LPW, NSTG>(min(NSTG - 2, nstage - 1 - ks));  // this wave's copies of stage ks landed
+        // ... and everyone's; everyone is also done reading stage ks-1.  A bare barrier: the
+        // fences of __syncthreads would wait for the later stages' copies as well.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (ks + NSTG - 1 < nstage) issue(ks + NSTG - 1, (j + NSTG - 1) % NSTG);
 #pragma unroll
-      for (int i = 0; i < WMT; ++i) af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][(wm * WMT + i) * BKB + kb][lane]);
+        for (int kb = 0; kb < BKB; ++kb) {
+          bf16x8 af[WMT], bw[WNT];
 #pragma unroll
-      for (int j = 0; j < WNT; ++j) bw[j] = __builtin_bit_cast(bf16x8, lds_b[buf][(wn * WNT + j) * BKB + kb][lane]);
+          for (int i = 0; i < WMT; ++i) af[i] = __builtin_bit_cast(bf16x8, lds[j][(wm * WMT + i) * BKB + kb][lane]);
 #pragma unroll
-      for (int i = 0; i < WMT; ++i)
+          for (int t = 0; t < WNT; ++t)
+            bw[t] = __builtin_bit_cast(bf16x8, lds[j][LA + (wn * WNT + t) * BKB + kb][lane]);
 #pragma unroll
-        for (int j = 0; j < WNT; ++j) acc[i][j] = mma(af[i], bw[j], acc[i][j]);
+          for (int i = 0; i < WMT; ++i)
+#pragma unroll
+            for (int t = 0; t < WNT; ++t) acc[i][t] = mma(af[i], bw[t], acc[i][t]);
+        }
+      }
     }
   }
 
@@ -163,33 +202,38 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch 
   }
 }
 
-// Host launch for the tiled family.  n_cols = output columns (gate/up: 2F).  Chooses a
-// 128x128 tile, or 64x128 when that leaves fewer than 256 workgroups.
+// Host launch for the tiled family.  n_cols = output columns (gate/up: 2F).
+//
+// On gfx950 the load rate of a workgroup grows with its wave count much more than with
+// its pipeline depth, so every shape runs 16 waves per workgroup with two LDS stages
+// (two workgroups fit a CU), and the tile shape follows the output size:
+//   gate/up (2F columns)        256 x 256, each wave 64 x 64
+//   QKV, and O / down when there are >= 512 tiles of 128 x 128: 128 x 128, waves 32 x 32
+//   O / down otherwise (few output tiles): 64 x 128 with 128-wide stages, waves 16 x 32
+template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
+static hipError_t launch_cfg(const Dims& d, const Bufs& b, const GemmLaunch& g, int n_cols, hipStream_t st) {
+  constexpr int BM = 16 * WGM * WMT, BN = 16 * WGN * WNT;
+  if (n_cols % BN || g.K % (32 * BKB)) return hipErrorInvalidValue;
+  const int tilesN = n_cols / BN, tilesM = (d.M + BM - 1) / BM;
+  hipLaunchKernelGGL((k_gemm_tiled<WMT, WNT, WGM, WGN, NSTG, BKB, EPI>), dim3(tilesM * tilesN), dim3(64 * WGM * WGN),
+                     0, st, d, b, g, tilesN, tilesM);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, int epi, int n_cols,
                              hipStream_t st) {
-  if (n_cols % 128 || g.K % 64) return hipErrorInvalidValue;
-  const int tilesN = n_cols / 128;
-  const int big = (d.M + 127) / 128 * tilesN;
-  const bool small_m = big < 256;
-  const int tilesM = small_m ? (d.M + 63) / 64 : (d.M + 127) / 128;
-  dim3 grid(tilesM * tilesN), block(256);
-#define PHYAI_TILED(WM, E) \
-  hipLaunchKernelGGL((k_gemm_tiled<WM, 4, E>), grid, block, 0, st, d, b, g, tilesN)
   switch (epi) {
     case EPI_QKV:
-      if (small_m) PHYAI_TILED(2, EPI_QKV); else PHYAI_TILED(4, EPI_QKV);
-      break;
-    case EPI_RESID:
-      if (small_m) PHYAI_TILED(2, EPI_RESID); else PHYAI_TILED(4, EPI_RESID);
-      break;
+      return launch_cfg<2, 2, 4, 4, 2, 2, EPI_QKV>(d, b, g, n_cols, st);
+    case EPI_RESID: {
+      const int tiles128 = (d.M + 127) / 128 * (n_cols / 128);
+      if (tiles128 >= 512) return launch_cfg<2, 2, 4, 4, 2, 2, EPI_RESID>(d, b, g, n_cols, st);
+      return launch_cfg<1, 2, 4, 4, 3, 4, EPI_RESID>(d, b, g, n_cols, st);
+    }
     case EPI_GEGLU:
-      if (small_m) PHYAI_TILED(2, EPI_GEGLU); else PHYAI_TILED(4, EPI_GEGLU);
-      break;
-    default:
-      return hipErrorInvalidValue;
+      return launch_cfg<4, 4, 4, 4, 2, 2, EPI_GEGLU>(d, b, g, n_cols, st);
   }
-#undef PHYAI_TILED
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace phyai
