@@ -50,6 +50,7 @@ struct Bufs {
 struct Plan {
   int s_qkv, s_o, s_gu, s_d;  // k-splits across workgroups per linear
   int attn_bps;               // 32-key blocks per attention split
+  int attn_wide;              // 1: many query tiles, shared-staging attention kernel
 };
 
 // Scratch sizes the plan needs (floats / counters).

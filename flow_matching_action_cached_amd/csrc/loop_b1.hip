@@ -320,6 +320,107 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
 }
 
 // ------------------------------------------------------------------ attention
+// End of one query tile's attention (one wave): with S > 1 key splits, publish this split's
+// partial, and the last split to arrive merges all S partials in split order with
+// log-sum-exp weights; then the normalised output goes to o (swizzled [Mpad][Hq*dh], the A
+// operand of the output projection).  o holds O^T of the tile (lane: column r16, rows
+// 4 grp + i of 16-column tile t), m_run / l_part the running max (log2 units) and this
+// lane's part of the row sums.  item indexes the tile's split workspace and counter.
+template <class AT, int DH>
+__device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4 (&o)[DH / 16], float m_run,
+                                            float l_part, int S, int s, size_t item, bool qvalid, int m, int head) {
+  constexpr int ES = sizeof(AT);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const int qd = d.Hq * DH;
+  float l_row = l_part;
+  l_row += __shfl_xor(l_row, 16, 64);
+  l_row += __shfl_xor(l_row, 32, 64);
+
+  if (S > 1) {
+    // Partial of this split: (m, l) in fp32 and O / l in the activation type (bf16 halves
+    // the hand-off; fp32 workloads keep fp32), as 16-byte lane slots.  Every split, the
+    // merging one included, enters the merge through the stored (rounded) value, so the
+    // result does not depend on which split finishes last.
+    constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;   // 16-byte slots per lane
+    constexpr uint32_t STRIDE = PAY * 1024 + 128;      // bytes per split partial
+    const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
+    const float inv_l = 1.0f / l_row;
+#pragma unroll
+    for (int u = 0; u < PAY; ++u) {
+      f32x4 v;
+      if constexpr (ES == 2) {
+        const f32x4 a = o[2 * u] * inv_l, c = o[2 * u + 1] * inv_l;
+        const bf16x8 pk = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+        v = __builtin_bit_cast(f32x4, pk);
+      } else {
+        v = o[u] * inv_l;
+      }
+      st_agent16(ws, s * STRIDE + (u * 64 + lane) * 16, v);
+    }
+    if (grp == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0, 16);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, l_row), ws, s * STRIDE + PAY * 1024 + 64 + r16 * 4,
+                                            0, 16);
+    }
+    PHASE_MARK(3);
+    const bool last = split_arrive_wave(bf.attn_cnt + item, (unsigned)S);
+    PHASE_MARK(4);
+    if (!last) return;
+    float ms[8], ls[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const uint32_t off = min(s2, S - 1) * STRIDE + PAY * 1024;
+      ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + r16 * 4, 0, 16));
+      ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + 64 + r16 * 4, 0, 16));
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if (s2 < S) M = fmaxf(M, ms[s2]);
+    float wgt[8], den = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      wgt[s2] = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+      den += wgt[s2];
+    }
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h2 = 0; h2 < 8; h2 += 4) {
+      if (h2 >= S) break;
+      f32x4 v[4][PAY];
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4)
+#pragma unroll
+        for (int u = 0; u < PAY; ++u) v[u4][u] = ld_agent16(ws, min(h2 + u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4)
+#pragma unroll
+        for (int u = 0; u < PAY; ++u) {
+          if constexpr (ES == 2) {
+            const bf16x8 pk = __builtin_bit_cast(bf16x8, v[u4][u]);
+            o[2 * u] += wgt[h2 + u4] * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+            o[2 * u + 1] += wgt[h2 + u4] * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
+          } else {
+            o[u] += wgt[h2 + u4] * v[u4][u];
+          }
+        }
+    }
+    l_row = den;
+  }
+  if (!qvalid) return;
+  const float inv = 1.0f / l_row;
+  // o is the A operand of the output projection: swizzled [Mpad][Hq*dh].  The four values
+  // of (t, i = 0..3) are consecutive columns inside one 8-wide lane slot.
+  AT* op = static_cast<AT*>(bf.o);
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) {
+    AT* dst = op + sw_idx(m, head * DH + t * 16 + grp * 4, qd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(o[t][i] * inv);
+  }
+}
+
 // Split-key flash decode.  The query rows of one KV head r are the g*H pairs
 // (query head r*g + j, chunk token t), row j*H + t, in 16-row tiles; the keys are
 // the P cached prefix rows followed by the H chunk rows (no mask among them).
@@ -471,95 +572,196 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   }
   PHASE_MARK(2);
   if (!active) return;
-  float l_row = l_part;
-  l_row += __shfl_xor(l_row, 16, 64);
-  l_row += __shfl_xor(l_row, 32, 64);
+  attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head);
+  PHASE_MARK(7);
+}
 
-  if (S > 1) {
-    // Partial of this split: (m, l) in fp32 and O / l in the activation type (bf16 halves
-    // the hand-off; fp32 workloads keep fp32), as 16-byte lane slots.  Every split, the
-    // merging one included, enters the merge through the stored (rounded) value, so the
-    // result does not depend on which split finishes last.
-    constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;   // 16-byte slots per lane
-    constexpr uint32_t STRIDE = PAY * 1024 + 128;      // bytes per split partial
-    const size_t item = ((size_t)(b * d.Hkv + r) * QT + qt);
-    const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
-    const float inv_l = 1.0f / l_row;
+// ------------------------------------------------------------------ attention, many query rows
+// The same split-key attention for batches and long joint sequences (hundreds to thousands
+// of query rows per KV head): NW waves each own QPW query tiles and all of them share the
+// staged key groups, so every staged K/V byte feeds NW*QPW tiles, and the group loads are
+// spread over NW waves (the load rate of a workgroup grows with its wave count).  Groups
+// are double-buffered: the loads of group g+1 are in flight (in registers) while group g
+// is used, and land in the other LDS buffer afterwards.  bf16 only.
+template <int DH, int NW, int QPW>
+__global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int layer, int S, int bps) {
+  typedef bf16 AT;
+  typedef typename FragOf<AT>::type Frag;
+  constexpr int NB = DH <= 64 ? 4 : 2;   // 32-key blocks per group (registers: 2 waves per SIMD)
+  constexpr int NK = NB * 32;
+  constexpr int KROW = DH + 8;           // K row: DH + 16 B pad
+  constexpr int VROW = NK + 8;           // V^T row: NK keys + 16 B pad
+  constexpr int KCPR = DH / 8, VCPR = NK / 8;
+  constexpr int KCH = NK * KCPR, VCH = DH * VCPR;
+  constexpr int CPT = (KCH + VCH) / (64 * NW);
+  static_assert((KCH + VCH) % (64 * NW) == 0, "group chunks split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) AT ks[2][NK * KROW];
+  __shared__ __attribute__((aligned(16))) AT vs[2][DH * VROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = d.Hq / d.Hkv;
+  const int QT = (gq * d.H + 15) / 16, QG = (QT + NW * QPW - 1) / (NW * QPW);
+  int idx = blockIdx.x;
+  const int s = idx % S;
+  idx /= S;
+  const int qg = idx % QG;
+  idx /= QG;
+  const int r = idx % d.Hkv;
+  const int b = idx / d.Hkv;
+  const int T = d.P + d.H;
+  const int nblk = (T + 31) / 32;
+  const int blk0 = s * bps, blk1 = min(nblk, blk0 + bps);
+  const int kend = min(T, blk1 * 32);
+  const int qd = d.Hq * DH;
+
+  const size_t kvbase = ((size_t)b * d.Lc + layer) * d.Hkv + r;
+  const AT* Kc = static_cast<const AT*>(bf.kc) + kvbase * d.KS * DH;
+  const AT* Vt = static_cast<const AT*>(bf.vt) + kvbase * DH * d.KS;
+
+  int qt[QPW], head[QPW], mrow[QPW];
+  bool active[QPW], qvalid[QPW];
+  Frag qf[QPW][DH / 32];
 #pragma unroll
-    for (int u = 0; u < PAY; ++u) {
-      f32x4 v;
-      if constexpr (ES == 2) {
-        const f32x4 a = o[2 * u] * inv_l, c = o[2 * u + 1] * inv_l;
-        const bf16x8 pk = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
-        v = __builtin_bit_cast(f32x4, pk);
+  for (int p = 0; p < QPW; ++p) {
+    qt[p] = (qg * NW + w) * QPW + p;
+    active[p] = qt[p] < QT;
+    const int qrow = qt[p] * 16 + r16;
+    qvalid[p] = active[p] && qrow < gq * d.H;
+    head[p] = r * gq + (qvalid[p] ? qrow / d.H : 0);
+    const int tok = qvalid[p] ? qrow % d.H : 0;
+    mrow[p] = b * d.H + tok;
+    const AT* qp = static_cast<const AT*>(bf.q) + (size_t)mrow[p] * qd + head[p] * DH + grp * 8;
+#pragma unroll
+    for (int j = 0; j < DH / 32; ++j) qf[p][j] = load_frag(qp + 32 * j);
+  }
+
+  // group g0.. (blocks past the split are clamped to its last block: masked below)
+  auto load_group = [&](int g0, u32x4 (&stage)[CPT]) {
+    const int glast = min(blk1, g0 + NB) - 1;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 64 * NW * i;
+      const char* src;
+      if (c < KCH) {
+        const int row = c / KCPR;
+        const int blk = min(g0 + row / 32, glast);
+        src = reinterpret_cast<const char*>(Kc + (size_t)(blk * 32 + row % 32) * DH) + (c % KCPR) * 16;
       } else {
-        v = o[u] * inv_l;
+        const int cv = c - KCH;
+        const int row = cv / VCPR;
+        const int kofs = (cv % VCPR) * 8;
+        const int blk = min(g0 + kofs / 32, glast);
+        src = reinterpret_cast<const char*>(Vt + (size_t)row * d.KS + blk * 32 + kofs % 32);
       }
-      st_agent16(ws, s * STRIDE + (u * 64 + lane) * 16, v);
+      stage[i] = *reinterpret_cast<const u32x4*>(src);
     }
-    if (grp == 0) {
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0, 16);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, l_row), ws, s * STRIDE + PAY * 1024 + 64 + r16 * 4,
-                                            0, 16);
+  };
+  auto store_group = [&](const u32x4 (&stage)[CPT], int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 64 * NW * i;
+      AT* dst = c < KCH ? ks[buf] + (c / KCPR) * KROW + (c % KCPR) * 8
+                        : vs[buf] + ((c - KCH) / VCPR) * VROW + ((c - KCH) % VCPR) * 8;
+      *reinterpret_cast<u32x4*>(dst) = stage[i];
     }
-    PHASE_MARK(3);
-    const bool last = split_arrive_wave(bf.attn_cnt + item, (unsigned)S);
-    PHASE_MARK(4);
-    if (!last) return;
-    float ms[8], ls[8];
+  };
+
+  const float sc = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+  float m_run[QPW], l_part[QPW];
+  f32x4 o[QPW][DH / 16];
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const uint32_t off = min(s2, S - 1) * STRIDE + PAY * 1024;
-      ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + r16 * 4, 0, 16));
-      ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + 64 + r16 * 4, 0, 16));
-    }
-    float M = -INFINITY;
+  for (int p = 0; p < QPW; ++p) {
+    m_run[p] = -INFINITY;
+    l_part[p] = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
-      if (s2 < S) M = fmaxf(M, ms[s2]);
-    float wgt[8], den = 0.f;
+    for (int t = 0; t < DH / 16; ++t) o[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  u32x4 stage[CPT];
+  load_group(blk0, stage);
+  store_group(stage, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int g0 = blk0; g0 < blk1; g0 += NB) {
+    const int glast = min(blk1, g0 + NB) - 1;
+    const bool has_next = g0 + NB < blk1;
+    if (has_next) load_group(g0 + NB, stage);
+    const AT* kb_ = ks[buf];
+    const AT* vb_ = vs[buf];
+    // ---- scores of the group for every tile of the wave (K fragments shared)
+    float sv[QPW][NB][8];
+    float mx[QPW];
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      wgt[s2] = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
-      den += wgt[s2];
-    }
+    for (int p = 0; p < QPW; ++p) mx[p] = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) {
+      f32x4 s0[QPW], s1[QPW];
 #pragma unroll
-    for (int h2 = 0; h2 < 8; h2 += 4) {
-      if (h2 >= S) break;
-      f32x4 v[4][PAY];
+      for (int p = 0; p < QPW; ++p) s0[p] = s1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g0 + j <= glast) {
 #pragma unroll
-      for (int u4 = 0; u4 < 4; ++u4)
+        for (int jj = 0; jj < DH / 32; ++jj) {
+          const Frag k0 = load_frag(kb_ + (j * 32 + r16) * KROW + 32 * jj + grp * 8);
+          const Frag k1 = load_frag(kb_ + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8);
 #pragma unroll
-        for (int u = 0; u < PAY; ++u) v[u4][u] = ld_agent16(ws, min(h2 + u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
-#pragma unroll
-      for (int u4 = 0; u4 < 4; ++u4)
-#pragma unroll
-        for (int u = 0; u < PAY; ++u) {
-          if constexpr (ES == 2) {
-            const bf16x8 pk = __builtin_bit_cast(bf16x8, v[u4][u]);
-            o[2 * u] += wgt[h2 + u4] * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
-            o[2 * u + 1] += wgt[h2 + u4] * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
-          } else {
-            o[u] += wgt[h2 + u4] * v[u4][u];
+          for (int p = 0; p < QPW; ++p) {
+            s0[p] = mma(k0, qf[p][jj], s0[p]);
+            s1[p] = mma(k1, qf[p][jj], s1[p]);
           }
         }
+      }
+      const int kb = (g0 + j) * 32 + grp * 4;
+#pragma unroll
+      for (int p = 0; p < QPW; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[p][j][i] = kb + i < kend ? s0[p][i] * sc : -INFINITY;
+          sv[p][j][4 + i] = kb + 16 + i < kend ? s1[p][i] * sc : -INFINITY;
+          mx[p] = fmaxf(mx[p], fmaxf(sv[p][j][i], sv[p][j][4 + i]));
+        }
     }
-    l_row = den;
-  }
-  if (!qvalid) return;
-  const float inv = 1.0f / l_row;
-  // o is the A operand of the output projection: swizzled [Mpad][Hq*dh].  The four values
-  // of (t, i = 0..3) are consecutive columns inside one 8-wide lane slot.
-  AT* op = static_cast<AT*>(bf.o);
 #pragma unroll
-  for (int t = 0; t < DH / 16; ++t) {
-    AT* dst = op + sw_idx(m, head * DH + t * 16 + grp * 4, qd);
+    for (int p = 0; p < QPW; ++p) {
+      mx[p] = fmaxf(mx[p], __shfl_xor(mx[p], 16, 64));
+      mx[p] = fmaxf(mx[p], __shfl_xor(mx[p], 32, 64));
+      const float m_new = fmaxf(m_run[p], mx[p]);
+      const float alpha = exp2f(m_run[p] - m_new);
+      l_part[p] *= alpha;
+      m_run[p] = m_new;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(o[t][i] * inv);
+      for (int t = 0; t < DH / 16; ++t) o[p][t] *= alpha;
+    }
+    // ---- per key block: probabilities, then O^T += V^T P^T (V fragments shared)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (g0 + j > glast) break;
+      Frag pf[QPW];
+#pragma unroll
+      for (int p = 0; p < QPW; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = exp2f(sv[p][j][e] - m_run[p]);
+          l_part[p] += pv;
+          pf[p][e] = to_elem<AT>(pv);
+        }
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t) {
+        const AT* vp = vb_ + (t * 16 + r16) * VROW + j * 32 + grp * 4;
+        const Frag vf = load_frag_split4(vp, vp + 16);
+#pragma unroll
+        for (int p = 0; p < QPW; ++p) o[p][t] = mma(vf, pf[p], o[p][t]);
+      }
+    }
+    if (has_next) store_group(stage, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
-  PHASE_MARK(7);
+#pragma unroll
+  for (int p = 0; p < QPW; ++p)
+    if (active[p])
+      attn_finish<AT, DH>(d, bf, o[p], m_run[p], l_part[p], S, s, (size_t)(b * d.Hkv + r) * QT + qt[p], qvalid[p],
+                          mrow[p], head[p]);
 }
 
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
@@ -799,8 +1001,10 @@ static int pick_split(int K, int tiles) {
   return S;
 }
 
+// Query tiles per workgroup of the many-row attention kernel (8 waves x tiles per wave).
+static int attn_wide_tiles(int dh) { return dh <= 128 ? 16 : 8; }
+
 Plan make_plan(const Dims& d, WDtype wt) {
-  (void)wt;
   Plan p;
   p.s_qkv = pick_split(d.D, d.qkv / 16);
   p.s_o = pick_split(d.Hq * d.dh, d.D / 16);
@@ -814,6 +1018,15 @@ Plan make_plan(const Dims& d, WDtype wt) {
   const int base = d.B * d.Hkv * QG;
   int S = std::max(1, 256 / base);
   S = std::min(S, std::min(8, (nblk + 3) / 4));
+  // Many query tiles (bf16): the shared-staging kernel, with key splits only up to ~256
+  // workgroups and at least one whole key group per split.
+  p.attn_wide = wt != W_F32 && d.B * d.Hkv * QT >= 64;
+  if (p.attn_wide) {
+    const int tpw = attn_wide_tiles(d.dh), nbg = d.dh <= 64 ? 4 : 2;
+    const int wbase = d.B * d.Hkv * ((QT + tpw - 1) / tpw);
+    S = std::max(1, (256 + wbase - 1) / wbase);
+    S = std::min(S, std::min(8, (nblk + nbg - 1) / nbg));
+  }
   int bps = (nblk + S - 1) / S;
   p.attn_bps = bps;
   return p;
@@ -856,7 +1069,22 @@ template <class AT>
 static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int layer, hipStream_t st) {
   const int T = d.P + d.H, nblk = (T + 31) / 32;
   const int S = (nblk + p.attn_bps - 1) / p.attn_bps;
-  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16, QG = (QT + 3) / 4;
+  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
+  if constexpr (sizeof(AT) == 2) {
+    if (p.attn_wide) {
+      const int tpw = attn_wide_tiles(d.dh);
+      dim3 grid(d.B * d.Hkv * ((QT + tpw - 1) / tpw) * S), block(512);
+      switch (d.dh) {
+        case 32: hipLaunchKernelGGL((k_attn_wide<32, 8, 2>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+        case 64: hipLaunchKernelGGL((k_attn_wide<64, 8, 2>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+        case 128: hipLaunchKernelGGL((k_attn_wide<128, 8, 2>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+        case 256: hipLaunchKernelGGL((k_attn_wide<256, 8, 1>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+  }
+  const int QG = (QT + 3) / 4;
   dim3 grid(d.B * d.Hkv * QG * S), block(256);
   switch (d.dh) {
     case 32: hipLaunchKernelGGL((k_attn<AT, 32>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
