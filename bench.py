@@ -169,6 +169,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--variants", default="int4,b32,wam",
+                    help="comma-separated variants to measure after the batch-1 line: int4, b32, wam")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -255,7 +257,8 @@ def main():
 
     # int4 group-128 variant of the same workload (expert linears quantised by the library)
     variants = {}
-    if not args.no_variants:
+    todo = set() if args.no_variants else {v.strip() for v in args.variants.split(",") if v.strip()}
+    if "int4" in todo:
         d4 = synth.CONFIGS["pi05_int4"]
         inp4 = synth.make_expert_inputs(d4, 0)
         w4 = {}
@@ -286,6 +289,7 @@ def main():
                                         "hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] int4 variant: {ms4:.4f} ms/chunk", file=sys.stderr, flush=True)
 
+    if "b32" in todo:
         # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs
         d32 = synth.CONFIGS["pi05_b32"]
         inp32 = synth.make_expert_inputs(d32, 0)
@@ -318,6 +322,7 @@ def main():
         print(f"[bench] batch-32 variant: {ms32:.3f} ms per batch chunk, {32000.0 / ms32:.1f} chunks/s",
               file=sys.stderr, flush=True)
 
+    if "wam" in todo:
         # joint video/action denoiser, guided pair: 28 layers, width 2048, 4096 + 32 tokens, 8 steps
         dw = synth.WAM_CONFIGS["wam"]
         wdev = synth.wam_device_inputs(dw, 0)

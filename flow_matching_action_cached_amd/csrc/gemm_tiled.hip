@@ -55,12 +55,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WGN, wn = w % WGN;
-  // XCD-aware tile order: consecutive workgroups go to different XCDs (round robin over 8),
-  // so give each XCD a contiguous run of tiles (shared operand rows/columns stay in its L2).
+  // Tile order.  Consecutive workgroups go to different XCDs (round robin over 8), so each
+  // XCD gets a contiguous run of the ordinal order; the ordinal order walks groups of GM
+  // row tiles column by column, so the workgroups resident on one XCD at a time cover a
+  // GM x (resident / GM) block and share operand panels in that XCD's L2.
+  constexpr int GM = 8;
   const int ntiles = tilesM * tilesN;
-  int tile = blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
-  const int tn = tile % tilesN, tm = tile / tilesN;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int gi = t / (GM * tilesN), rows_g = min(GM, tilesM - gi * GM), within = t - gi * GM * tilesN;
+  const int tm = gi * GM + within % rows_g, tn = within / rows_g;
   const int nstage = g.K / 32 / BKB;
   const int mtiles = (d.M + 15) / 16;  // 16-row tiles present in the activation buffer
   const AT* A = static_cast<const AT*>(g.A);
@@ -208,8 +212,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
 // its pipeline depth, so every shape runs 16 waves per workgroup with two LDS stages
 // (two workgroups fit a CU), and the tile shape follows the output size:
 //   gate/up (2F columns)        256 x 256, each wave 64 x 64
-//   QKV, and O / down when there are >= 512 tiles of 128 x 128: 128 x 128, waves 32 x 32
-//   O / down otherwise (few output tiles): 64 x 128 with 128-wide stages, waves 16 x 32
+//   QKV, O and down when there are >= 512 tiles of 128 x 128: 128 x 128, waves 32 x 32
+//   otherwise (few output tiles) QKV: 64 x 128 with 8 waves and three stages; O / down:
+//   64 x 128 with 16 waves and 128-wide stages
 template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
 static hipError_t launch_cfg(const Dims& d, const Bufs& b, const GemmLaunch& g, int n_cols, hipStream_t st) {
   constexpr int BM = 16 * WGM * WMT, BN = 16 * WGN * WNT;
@@ -224,7 +229,8 @@ hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, 
                              hipStream_t st) {
   switch (epi) {
     case EPI_QKV:
-      return launch_cfg<2, 2, 4, 4, 2, 2, EPI_QKV>(d, b, g, n_cols, st);
+      if ((d.M + 127) / 128 * (n_cols / 128) >= 512) return launch_cfg<2, 2, 4, 4, 2, 2, EPI_QKV>(d, b, g, n_cols, st);
+      return launch_cfg<2, 2, 2, 4, 3, 2, EPI_QKV>(d, b, g, n_cols, st);
     case EPI_RESID: {
       const int tiles128 = (d.M + 127) / 128 * (n_cols / 128);
       if (tiles128 >= 512) return launch_cfg<2, 2, 4, 4, 2, 2, EPI_RESID>(d, b, g, n_cols, st);
