@@ -20,13 +20,13 @@ namespace phyai {
 
 // Optional per-phase timestamps (a build with -DPHYAI_PHASE_TRACE only): each wave's lane 0
 // stores the 100 MHz real-time counter at numbered points of a kernel into
-// g_phase_trace[(workgroup * 4 + wave) * 8 + slot]; phyai_phase_trace() copies it out.
+// g_phase_trace[(workgroup * 8 + wave) * 8 + slot] (workgroups < 2048, waves < 8); phyai_phase_trace() copies it out.
 #ifdef PHYAI_PHASE_TRACE
 extern __device__ uint64_t g_phase_trace[4096 * 4 * 8];
 #define PHASE_MARK(slot)                                                                          \
   do {                                                                                            \
-    if ((threadIdx.x & 63) == 0 && blockIdx.x < 4096)                                             \
-      g_phase_trace[((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (slot)] =                 \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < 2048 && (threadIdx.x >> 6) < 8)                   \
+      g_phase_trace[((size_t)blockIdx.x * 8 + (threadIdx.x >> 6)) * 8 + (slot)] =                 \
           __builtin_amdgcn_s_memrealtime();                                                       \
   } while (0)
 #else

@@ -366,13 +366,19 @@ __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4
     const bool last = split_arrive_wave(bf.attn_cnt + item, (unsigned)S);
     PHASE_MARK(4);
     if (!last) return;
+    // the statistics and the first four payloads in one round trip
     float ms[8], ls[8];
+    f32x4 v0[4][PAY];
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) {
       const uint32_t off = min(s2, S - 1) * STRIDE + PAY * 1024;
       ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + r16 * 4, 0, 16));
       ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off + 64 + r16 * 4, 0, 16));
     }
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4)
+#pragma unroll
+      for (int u = 0; u < PAY; ++u) v0[u4][u] = ld_agent16(ws, min(u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
     float M = -INFINITY;
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
@@ -392,7 +398,8 @@ __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4
 #pragma unroll
       for (int u4 = 0; u4 < 4; ++u4)
 #pragma unroll
-        for (int u = 0; u < PAY; ++u) v[u4][u] = ld_agent16(ws, min(h2 + u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
+        for (int u = 0; u < PAY; ++u)
+          v[u4][u] = h2 == 0 ? v0[u4][u] : ld_agent16(ws, min(h2 + u4, S - 1) * STRIDE + (u * 64 + lane) * 16);
 #pragma unroll
       for (int u4 = 0; u4 < 4; ++u4)
 #pragma unroll
@@ -433,9 +440,12 @@ __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4
 // in the cache.  Splits are merged with log-sum-exp weights in split order by the last
 // wave to finish.
 template <class AT, int DH>
-__global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
+__global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
   typedef typename FragOf<AT>::type Frag;
+  constexpr int KH = 2;                               // waves per query tile (key halves of a group)
+  constexpr int NT = 64 * 4 * KH;                     // threads
   constexpr int NB = DH * sizeof(AT) <= 512 ? 4 : 2;  // 32-key blocks staged per group (LDS <= 160 KB)
+  constexpr int NBH = NB / KH;                        // blocks of a group per wave
   constexpr int NK = NB * 32;
   constexpr int ES = sizeof(AT);
   constexpr int KROW = DH + 16 / ES;                 // K row: DH + 16 B pad
@@ -443,13 +453,19 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   constexpr int KCPR = DH * ES / 16;                 // 16-byte chunks per K row
   constexpr int VCPR = NK * ES / 16;                 // 16-byte chunks per staged V^T row
   constexpr int KCH = NK * KCPR, VCH = DH * VCPR;    // chunks of one group
-  constexpr int CPT = (KCH + VCH) / 256;             // chunks per thread
-  static_assert((KCH + VCH) % 256 == 0, "group size");
-  __shared__ __attribute__((aligned(16))) AT ks[NK * KROW];
-  __shared__ __attribute__((aligned(16))) AT vs[DH * VROW];
+  constexpr int CPT = (KCH + VCH) / NT;              // chunks per thread
+  constexpr int KS_B = NK * KROW * ES, VS_B = DH * VROW * ES;
+  constexpr int CMB = DH / 4 + 2;                    // floats per lane handed from half 1 to half 0
+  constexpr int CMB_B = 4 * CMB * 64 * 4;
+  constexpr int LDS_B = KS_B + VS_B > CMB_B ? KS_B + VS_B : CMB_B;
+  static_assert((KCH + VCH) % NT == 0 && NB % KH == 0, "group size");
+  __shared__ __attribute__((aligned(16))) char lds_raw[LDS_B];
+  AT* ks = reinterpret_cast<AT*>(lds_raw);
+  AT* vs = reinterpret_cast<AT*>(lds_raw + KS_B);
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = w & 3, half = w >> 2;               // query tile slot, key half
   const int gq = d.Hq / d.Hkv;
   const int QT = (gq * d.H + 15) / 16, QG = (QT + 3) / 4;
   int idx = blockIdx.x;
@@ -459,7 +475,7 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
   idx /= QG;
   const int r = idx % d.Hkv;
   const int b = idx / d.Hkv;
-  const int qt = qg * 4 + w;
+  const int qt = qg * 4 + wq;
   const bool active = qt < QT;
   const int T = d.P + d.H;
   const int nblk = (T + 31) / 32;
@@ -498,7 +514,7 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
     u32x4 stage[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const char* src;
       if (c < KCH) {
         const int row = c / KCPR;                        // staged key row 0..NK-1
@@ -516,19 +532,22 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
     __syncthreads();                                     // previous group's LDS reads are done
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       AT* dst = c < KCH ? ks + (c / KCPR) * KROW + (c % KCPR) * (16 / ES)
                         : vs + ((c - KCH) / VCPR) * VROW + ((c - KCH) % VCPR) * (16 / ES);
       *reinterpret_cast<u32x4*>(dst) = stage[i];
     }
     __syncthreads();
     if (g0 == blk0) PHASE_MARK(1);
-    if (!active) continue;
-    // ---- scores of the group, masked past the split
-    float sv[NB][8];
+    // this wave's blocks of the group: [g0 + half*NBH, g0 + half*NBH + NBH) up to glast
+    const int jb = half * NBH;
+    if (!active || g0 + jb > glast) continue;
+    // ---- scores of the wave's blocks, masked past the split
+    float sv[NBH][8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int jh = 0; jh < NBH; ++jh) {
+      const int j = jb + jh;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       if (g0 + j <= glast) {
 #pragma unroll
@@ -540,9 +559,9 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
       const int kb = (g0 + j) * 32 + grp * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[j][i] = kb + i < kend ? s0[i] * sc : -INFINITY;
-        sv[j][4 + i] = kb + 16 + i < kend ? s1[i] * sc : -INFINITY;
-        mx = fmaxf(mx, fmaxf(sv[j][i], sv[j][4 + i]));
+        sv[jh][i] = kb + i < kend ? s0[i] * sc : -INFINITY;
+        sv[jh][4 + i] = kb + 16 + i < kend ? s1[i] * sc : -INFINITY;
+        mx = fmaxf(mx, fmaxf(sv[jh][i], sv[jh][4 + i]));
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -554,12 +573,13 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
 #pragma unroll
     for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int jh = 0; jh < NBH; ++jh) {
+      const int j = jb + jh;
       if (g0 + j > glast) break;
       Frag pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[j][e] - m_new);
+        const float p = exp2f(sv[jh][e] - m_new);
         l_part += p;
         pf[e] = to_elem<AT>(p);
       }
@@ -571,7 +591,32 @@ __global__ __launch_bounds__(256) void k_attn(Dims d, Bufs bf, int layer, int S,
     }
   }
   PHASE_MARK(2);
-  if (!active) return;
+  // ---- combine the two key halves of each query tile: half 1 hands (m, l, O) to half 0
+  // through LDS (the staging buffers are free once every wave is past its last group).
+  // Half 0 always holds the split's first key, so its running max is finite.
+  float* cmb = reinterpret_cast<float*>(lds_raw) + wq * CMB * 64;
+  __syncthreads();
+  if (half == 1 && active) {
+    cmb[lane] = m_run;
+    cmb[64 + lane] = l_part;
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cmb[(2 + 4 * t + i) * 64 + lane] = o[t][i];
+  }
+  __syncthreads();
+  if (half == 1 || !active) return;
+  {
+    const float m1 = cmb[lane], l1 = cmb[64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = exp2f(m_run - M), a1 = exp2f(m1 - M);
+    l_part = l_part * a0 + l1 * a1;
+    m_run = M;
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + cmb[(2 + 4 * t + i) * 64 + lane] * a1;
+  }
   attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head);
   PHASE_MARK(7);
 }
@@ -1085,7 +1130,7 @@ static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int l
     }
   }
   const int QG = (QT + 3) / 4;
-  dim3 grid(d.B * d.Hkv * QG * S), block(256);
+  dim3 grid(d.B * d.Hkv * QG * S), block(512);
   switch (d.dh) {
     case 32: hipLaunchKernelGGL((k_attn<AT, 32>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
     case 64: hipLaunchKernelGGL((k_attn<AT, 64>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
