@@ -1036,13 +1036,15 @@ size_t gemm_ws_floats(const Dims& d, const Plan& p) {
   return n;
 }
 
-// Splits across workgroups for a linear with K inputs and `tiles` 16-column tiles: a
-// power of two dividing the K/128 quads (int4 waves own whole quads), at most 32 k-blocks
-// per split (8 per wave), and enough workgroups to cover the 256 CUs when possible.
-static int pick_split(int K, int tiles) {
+// Splits across workgroups for a linear with K inputs: the fewest (a power of two dividing
+// the K/128 quads; int4 waves own whole quads) that keep a split at most 32 k-blocks (8 per
+// wave).  More splits would add workgroups, but each split costs a cross-workgroup hand-off
+// (agent-scope partials, arrival, reload by the last arrival), which on this chip takes
+// longer than streaming twice the weights per workgroup: QKV 7.8 -> 5.2 us at one split.
+static int pick_split(int K) {
   const int nq = K / 128;
   int S = 1;
-  while (S < 8 && nq % (2 * S) == 0 && (nq / S > 8 || tiles * S < 256)) S *= 2;
+  while (S < 8 && nq % (2 * S) == 0 && nq / S > 8) S *= 2;
   return S;
 }
 
@@ -1051,10 +1053,10 @@ static int attn_wide_tiles(int dh) { return dh <= 128 ? 16 : 8; }
 
 Plan make_plan(const Dims& d, WDtype wt) {
   Plan p;
-  p.s_qkv = pick_split(d.D, d.qkv / 16);
-  p.s_o = pick_split(d.Hq * d.dh, d.D / 16);
-  p.s_gu = pick_split(d.D, d.F / 16);
-  p.s_d = pick_split(d.F, d.D / 16);
+  p.s_qkv = pick_split(d.D);
+  p.s_o = pick_split(d.Hq * d.dh);
+  p.s_gu = pick_split(d.D);
+  p.s_d = pick_split(d.F);
   // Key splits only as far as needed to give the chip ~256 workgroups (a batch of many
   // samples needs none), at least four 32-key blocks per split, at most 8 splits (the
   // merge width).
