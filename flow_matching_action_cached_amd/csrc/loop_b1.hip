@@ -36,6 +36,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace phyai {
 
@@ -457,7 +458,9 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
   constexpr int KS_B = NK * KROW * ES, VS_B = DH * VROW * ES;
   constexpr int CMB = DH / 4 + 2;                    // floats per lane handed from half 1 to half 0
   constexpr int CMB_B = 4 * CMB * 64 * 4;
-  constexpr int LDS_B = KS_B + VS_B > CMB_B ? KS_B + VS_B : CMB_B;
+  constexpr int PAIR_B = 8 * (DH / 8 + 2) * 64 * 4;  // both halves hand over half their columns
+  constexpr int CMX_B = CMB_B > PAIR_B ? CMB_B : PAIR_B;
+  constexpr int LDS_B = KS_B + VS_B > CMX_B ? KS_B + VS_B : CMX_B;
   static_assert((KCH + VCH) % NT == 0 && NB % KH == 0, "group size");
   __shared__ __attribute__((aligned(16))) char lds_raw[LDS_B];
   AT* ks = reinterpret_cast<AT*>(lds_raw);
@@ -591,33 +594,165 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
     }
   }
   PHASE_MARK(2);
-  // ---- combine the two key halves of each query tile: half 1 hands (m, l, O) to half 0
-  // through LDS (the staging buffers are free once every wave is past its last group).
-  // Half 0 always holds the split's first key, so its running max is finite.
-  float* cmb = reinterpret_cast<float*>(lds_raw) + wq * CMB * 64;
-  __syncthreads();
-  if (half == 1 && active) {
-    cmb[lane] = m_run;
-    cmb[64 + lane] = l_part;
+  // ---- combine the two key halves of each query tile through LDS (the staging buffers
+  // are free once every wave is past its last group).  Half 0 always holds the split's
+  // first key, so its running max is finite.
+  constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;    // 16-byte partial slots per lane
+  constexpr int PAYH = PAY / 2;                        // slots finished by each half
+  constexpr bool PAIR = PAYH >= 1 && PAYH <= 4;        // both halves finish the tile
+  if constexpr (!PAIR) {
+    float* cmb = reinterpret_cast<float*>(lds_raw) + wq * CMB * 64;
+    __syncthreads();
+    if (half == 1 && active) {
+      cmb[lane] = m_run;
+      cmb[64 + lane] = l_part;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t)
+      for (int t = 0; t < DH / 16; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cmb[(2 + 4 * t + i) * 64 + lane] = o[t][i];
+        for (int i = 0; i < 4; ++i) cmb[(2 + 4 * t + i) * 64 + lane] = o[t][i];
+    }
+    __syncthreads();
+    if (half == 1 || !active) return;
+    {
+      const float m1 = cmb[lane], l1 = cmb[64 + lane];
+      const float M = fmaxf(m_run, m1);
+      const float a0 = exp2f(m_run - M), a1 = exp2f(m1 - M);
+      l_part = l_part * a0 + l1 * a1;
+      m_run = M;
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + cmb[(2 + 4 * t + i) * 64 + lane] * a1;
+    }
+    attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head);
+  } else {
+    // Both halves finish the tile, each its own half of the output columns (16-column
+    // tiles [half*T2, half*T2 + T2)): each hands the other (m, l) and the other's columns
+    // of its O^T, and both form the combination in the same order (half 0's part first).
+    // The half index is made a compile-time constant (H) so that the register arrays are
+    // indexed with constants (a run-time index would move them to scratch memory).
+    constexpr int T2 = DH / 32;
+    constexpr int CM2 = 4 * T2 + 2;                    // floats per lane handed over
+    __shared__ unsigned arrive_flag;
+    auto finish = [&](auto hc) {
+    constexpr int H = decltype(hc)::value;
+    float* mine = reinterpret_cast<float*>(lds_raw) + (wq * 2 + H) * CM2 * 64;
+    const float* other = reinterpret_cast<const float*>(lds_raw) + (wq * 2 + (H ^ 1)) * CM2 * 64;
+    __syncthreads();
+    if (active) {
+      mine[lane] = m_run;
+      mine[64 + lane] = l_part;
+#pragma unroll
+      for (int t2 = 0; t2 < T2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(2 + 4 * t2 + i) * 64 + lane] = o[(H ^ 1) * T2 + t2][i];
+    }
+    __syncthreads();
+    f32x4 oh[T2];                                      // this half's output tiles
+    if (active) {
+      const float mo = other[lane], lo = other[64 + lane];
+      const float m0 = H ? mo : m_run, m1 = H ? m_run : mo;
+      const float l0 = H ? lo : l_part, l1 = H ? l_part : lo;
+      const float M = fmaxf(m0, m1);
+      const float a0 = exp2f(m0 - M), a1 = exp2f(m1 - M);
+      l_part = l0 * a0 + l1 * a1;
+      m_run = M;
+#pragma unroll
+      for (int t2 = 0; t2 < T2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float own = o[H * T2 + t2][i], oth = other[(2 + 4 * t2 + i) * 64 + lane];
+          oh[t2][i] = H ? oth * a0 + own * a1 : own * a0 + oth * a1;
+        }
+    }
+    float l_row = l_part;
+    l_row += __shfl_xor(l_row, 16, 64);
+    l_row += __shfl_xor(l_row, 32, 64);
+    AT* op = static_cast<AT*>(bf.o);
+    auto write_out = [&](const f32x4 (&v)[T2], float inv) {
+#pragma unroll
+      for (int t2 = 0; t2 < T2; ++t2) {
+        AT* dst = op + sw_idx(m, head * DH + (H * T2 + t2) * 16 + grp * 4, qd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(v[t2][i] * inv);
+      }
+    };
+    if (S == 1) {
+      if (active && qvalid) write_out(oh, 1.0f / l_row);
+      return;
+    }
+    // Split partial (O / l in the activation type, 16-byte slots; (m, l) in fp32 by half
+    // 0), then one arrival per workgroup: the last workgroup of the query group merges
+    // its four tiles, each half its own slots, fetching every split's statistics and
+    // slots in one round trip.  Every split enters the merge through its stored value.
+    constexpr uint32_t STRIDE = PAY * 1024 + 128;       // bytes per split partial
+    const size_t item = (size_t)(b * d.Hkv + r) * QT + qt;
+    const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
+    if (active) {
+      const float inv_l = 1.0f / l_row;
+#pragma unroll
+      for (int uh = 0; uh < PAYH; ++uh) {
+        const int u = H * PAYH + uh;
+        f32x4 v;
+        if constexpr (ES == 2) {
+          const f32x4 a = oh[2 * uh] * inv_l, c = oh[2 * uh + 1] * inv_l;
+          const bf16x8 pk = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                             (bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+          v = __builtin_bit_cast(f32x4, pk);
+        } else {
+          v = oh[uh] * inv_l;
+        }
+        st_agent16(ws, s * STRIDE + (u * 64 + lane) * 16, v);
+      }
+      if (H == 0 && grp == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0,
+                                              16);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, l_row), ws,
+                                              s * STRIDE + PAY * 1024 + 64 + r16 * 4, 0, 16);
+      }
+    }
+    PHASE_MARK(3);
+    const bool last = split_arrive_wg(bf.attn_cnt + ((size_t)(b * d.Hkv + r) * QG + qg), (unsigned)S, &arrive_flag);
+    PHASE_MARK(4);
+    if (!last || !active) return;
+    float ms[8], ls[8];
+    f32x4 pv[8][PAYH];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const uint32_t base = min(s2, S - 1) * STRIDE;
+      ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, base + PAY * 1024 + r16 * 4, 0, 16));
+      ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, base + PAY * 1024 + 64 + r16 * 4, 0, 16));
+#pragma unroll
+      for (int uh = 0; uh < PAYH; ++uh) pv[s2][uh] = ld_agent16(ws, base + ((H * PAYH + uh) * 64 + lane) * 16);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if (s2 < S) M = fmaxf(M, ms[s2]);
+    float den = 0.f;
+    f32x4 acc[T2];
+#pragma unroll
+    for (int t2 = 0; t2 < T2; ++t2) acc[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+      den += wgt;
+#pragma unroll
+      for (int uh = 0; uh < PAYH; ++uh) {
+        if constexpr (ES == 2) {
+          const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2][uh]);
+          acc[2 * uh] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+          acc[2 * uh + 1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
+        } else {
+          acc[uh] += wgt * pv[s2][uh];
+        }
+      }
+    }
+    if (qvalid) write_out(acc, 1.0f / den);
+    };
+    if (half) finish(std::integral_constant<int, 1>{});
+    else finish(std::integral_constant<int, 0>{});
   }
-  __syncthreads();
-  if (half == 1 || !active) return;
-  {
-    const float m1 = cmb[lane], l1 = cmb[64 + lane];
-    const float M = fmaxf(m_run, m1);
-    const float a0 = exp2f(m_run - M), a1 = exp2f(m1 - M);
-    l_part = l_part * a0 + l1 * a1;
-    m_run = M;
-#pragma unroll
-    for (int t = 0; t < DH / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + cmb[(2 + 4 * t + i) * 64 + lane] * a1;
-  }
-  attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head);
   PHASE_MARK(7);
 }
 

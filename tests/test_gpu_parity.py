@@ -201,4 +201,9 @@ def test_int4_lossless_weights_match_bf16_path():
         inp[k] = q4.dequantize_stack(*q4.quantize_stack(inp[k])).astype(np.float32)
     got4 = _run(d4, inp)
     gotb = _run(db, inp)
-    assert rel_err(got4, gotb) <= 1e-3
+    # The two paths add their fp32 partial sums in different groupings (dequantised
+    # quads with a row-sum correction against plain bf16 products), and every GEMM input
+    # activation is rounded to bf16 (spacing 2^-8 = 3.9e-3 relative), so an input may land
+    # one bf16 step apart and the difference grows through the layers and steps (1.0e-3 to
+    # 1.4e-3 observed).  A mis-decoded nibble, scale or correction gives errors of order 1.
+    assert rel_err(got4, gotb) <= 5e-3
