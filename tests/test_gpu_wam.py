@@ -1,9 +1,10 @@
 """GPU parity of the joint video/action denoiser (guided branch pair) through the C ABI.
 
 Reduced shapes against the float64 oracle (bf16 weights and GEMM inputs, fp32
-accumulation: max error / max |ref| <= 2e-2); the full 28-layer, 4128-token shape through
-properties that hold at any size (equal branch conditions make the guidance scale
-irrelevant, bitwise; graph replay equals eager launches, bitwise; the state stays finite).
+accumulation: max error / max |ref| <= 2e-2), including the full width, heads, MLP and
+token count at one layer and one step; the full 28-layer, 8-step shape through properties
+that hold at any size (equal branch conditions make the guidance scale irrelevant,
+bitwise; graph replay equals eager launches, bitwise; the state stays finite).
 """
 import dataclasses
 
@@ -141,6 +142,27 @@ def test_joint_call_order_and_kind_errors():
     assert lib.phyai_wam_denoise(e_ctx._h, z.data_ptr(), a.data_ptr(), 1, z.data_ptr(), a.data_ptr()) == 2
     e_ctx.close()
     jd.close()
+
+
+@pytest.mark.slow
+def test_joint_full_width_one_layer_velocity_matches_oracle():
+    """Full width, heads, MLP and token count (2048, 16 x 128, 8192, 4096 + 32 tokens) at
+    reduced depth: one layer and one step, so the float64 oracle finishes in seconds.
+    The velocity v = (z_1 - z_0) / dt is compared (z_0 would otherwise dominate z_1)."""
+    d = dataclasses.replace(FULL, n_layers=1, n_steps=1)
+    inp = synth.make_wam_inputs(d, 5)
+    t = ex.schedule(d.n_steps)
+    dt = float(ex.step_sizes(t)[0])
+    jd = _make(d, _dev(inp), t)
+    zl, za = _run(jd, _dev(inp))
+    jd.close()
+    rl, ra = owam.denoise(inp, d, t)
+    z0 = np.concatenate([inp["z_lat"].ravel(), inp["z_act"].ravel()]).astype(np.float64)
+    got = (np.concatenate([zl.ravel(), za.ravel()]) - z0) / dt
+    ref = (np.concatenate([rl.ravel(), ra.ravel()]) - z0) / dt
+    err = rel_err(got, ref)
+    print(f"joint full width, 1 layer: velocity rel err {err:.3e}", flush=True)
+    assert err <= TOL
 
 
 @pytest.mark.slow
