@@ -471,9 +471,13 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
   const int wq = w & 3, half = w >> 2;               // query tile slot, key half
   const int gq = d.Hq / d.Hkv;
   const int QT = (gq * d.H + 15) / 16, QG = (QT + 3) / 4;
+  // Workgroups go to the 8 XCDs round robin: the split index is the workgroup index mod 8,
+  // so all query groups of one key split run on one XCD and share its L2 copy of the
+  // split's K/V (S <= 8; the slots s >= S of each row of 8 have no work).
   int idx = blockIdx.x;
-  const int s = idx % S;
-  idx /= S;
+  const int s = idx & 7;
+  if (s >= S) return;
+  idx >>= 3;
   const int qg = idx % QG;
   idx /= QG;
   const int r = idx % d.Hkv;
@@ -1267,7 +1271,7 @@ static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int l
     }
   }
   const int QG = (QT + 3) / 4;
-  dim3 grid(d.B * d.Hkv * QG * S), block(512);
+  dim3 grid(d.B * d.Hkv * QG * 8), block(512);  // 8 split slots per query group (S <= 8)
   switch (d.dh) {
     case 32: hipLaunchKernelGGL((k_attn<AT, 32>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
     case 64: hipLaunchKernelGGL((k_attn<AT, 64>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
