@@ -1208,10 +1208,18 @@ Plan make_plan(const Dims& d, WDtype wt) {
   // workgroups and at least one whole key group per split.
   p.attn_wide = wt != W_F32 && d.B * d.Hkv * QT >= 64;
   if (p.attn_wide) {
+    // One workgroup per CU at a time: pick the split count (<= 4, at least one key group
+    // per split) that minimises the rounds of 256 workgroups per unit of work, e.g. the
+    // joint denoiser's 544 query groups run in 9 rounds of quarter sweeps (2.25 full
+    // sweeps) instead of 3 rounds of full sweeps.
     const int tpw = attn_wide_tiles(d.dh), nbg = d.dh <= 64 ? 4 : 2;
     const int wbase = d.B * d.Hkv * ((QT + tpw - 1) / tpw);
-    S = std::max(1, (256 + wbase - 1) / wbase);
-    S = std::min(S, std::min(8, (nblk + nbg - 1) / nbg));
+    const int smax = std::min(4, (nblk + nbg - 1) / nbg);
+    S = 1;
+    for (int c = 2; c <= smax; ++c) {
+      const long rc = (long)((wbase * c + 255) / 256) * S, rs = (long)((wbase * S + 255) / 256) * c;
+      if (rc < rs) S = c;  // rounds(c)/c < rounds(S)/S
+    }
   }
   int bps = (nblk + S - 1) / S;
   p.attn_bps = bps;
