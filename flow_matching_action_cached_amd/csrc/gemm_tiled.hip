@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
 // (two workgroups fit a CU), and the tile shape follows the output size:
 //   gate/up (2F columns)        256 x 256, each wave 64 x 64
 //   QKV, O and down when there are >= 512 tiles of 128 x 128: 128 x 128, waves 32 x 32
+//   (O / down: four stages of 32 k-columns, 5 % faster than two of 64 on these shapes)
 //   otherwise (few output tiles) QKV: 64 x 128 with 8 waves and three stages; O / down:
 //   64 x 128 with 16 waves and 128-wide stages
 template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
@@ -233,7 +234,7 @@ hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, 
       return launch_cfg<2, 2, 2, 4, 3, 2, EPI_QKV>(d, b, g, n_cols, st);
     case EPI_RESID: {
       const int tiles128 = (d.M + 127) / 128 * (n_cols / 128);
-      if (tiles128 >= 512) return launch_cfg<2, 2, 4, 4, 2, 2, EPI_RESID>(d, b, g, n_cols, st);
+      if (tiles128 >= 512) return launch_cfg<2, 2, 4, 4, 4, 1, EPI_RESID>(d, b, g, n_cols, st);
       return launch_cfg<1, 2, 4, 4, 3, 4, EPI_RESID>(d, b, g, n_cols, st);
     }
     case EPI_GEGLU:
