@@ -862,10 +862,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
     for (int t = 0; t < DH / 16; ++t) o[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  PHASE_MARK(0);
   u32x4 stage[CPT];
   load_group(blk0, stage);
   store_group(stage, 0);
   __syncthreads();
+  PHASE_MARK(1);
   int buf = 0;
   for (int g0 = blk0; g0 < blk1; g0 += NB) {
     const int glast = min(blk1, g0 + NB) - 1;
@@ -884,15 +886,29 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
 #pragma unroll
       for (int p = 0; p < QPW; ++p) s0[p] = s1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (g0 + j <= glast) {
+        // all K fragments of the block in flight before the first product, and the dh sum
+        // as two interleaved chains per key half (even / odd 32-wide dh slices)
+        Frag kf[DH / 32][2];
 #pragma unroll
         for (int jj = 0; jj < DH / 32; ++jj) {
-          const Frag k0 = load_frag(kb_ + (j * 32 + r16) * KROW + 32 * jj + grp * 8);
-          const Frag k1 = load_frag(kb_ + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8);
+          kf[jj][0] = load_frag(kb_ + (j * 32 + r16) * KROW + 32 * jj + grp * 8);
+          kf[jj][1] = load_frag(kb_ + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int p = 0; p < QPW; ++p) {
-            s0[p] = mma(k0, qf[p][jj], s0[p]);
-            s1[p] = mma(k1, qf[p][jj], s1[p]);
+        for (int p = 0; p < QPW; ++p) {
+          f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < DH / 32; jj += 2) {
+            s0[p] = mma(kf[jj][0], qf[p][jj], s0[p]);
+            s1[p] = mma(kf[jj][1], qf[p][jj], s1[p]);
+            if (jj + 1 < DH / 32) {
+              e0 = mma(kf[jj + 1][0], qf[p][jj + 1], e0);
+              e1 = mma(kf[jj + 1][1], qf[p][jj + 1], e1);
+            }
           }
+          s0[p] += e0;
+          s1[p] += e1;
         }
       }
       const int kb = (g0 + j) * 32 + grp * 4;
@@ -929,18 +945,28 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
           l_part[p] += pv;
           pf[p][e] = to_elem<AT>(pv);
         }
+      // V fragments in batches of up to 8 (registers), each batch in flight before its products
+      constexpr int VB = DH / 16 < 8 ? DH / 16 : 8;
 #pragma unroll
-      for (int t = 0; t < DH / 16; ++t) {
-        const AT* vp = vb_ + (t * 16 + r16) * VROW + j * 32 + grp * 4;
-        const Frag vf = load_frag_split4(vp, vp + 16);
+      for (int t0 = 0; t0 < DH / 16; t0 += VB) {
+        Frag vf[VB];
 #pragma unroll
-        for (int p = 0; p < QPW; ++p) o[p][t] = mma(vf, pf[p], o[p][t]);
+        for (int t = 0; t < VB; ++t) {
+          const AT* vp = vb_ + ((t0 + t) * 16 + r16) * VROW + j * 32 + grp * 4;
+          vf[t] = load_frag_split4(vp, vp + 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < VB; ++t)
+#pragma unroll
+          for (int p = 0; p < QPW; ++p) o[p][t0 + t] = mma(vf[t], pf[p], o[p][t0 + t]);
       }
     }
     if (has_next) store_group(stage, buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
+  PHASE_MARK(2);
 #pragma unroll
   for (int p = 0; p < QPW; ++p)
     if (active[p])
