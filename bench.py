@@ -154,11 +154,15 @@ def cpu_baseline(d, inputs):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    ox.denoise(inputs, d, t=schedule(d.n_steps))
-    sec = time.perf_counter() - t0
+    ts = []
+    for _ in range(4):  # one warm-up, three timed
+        t0 = time.perf_counter()
+        ox.denoise(inputs, d, t=schedule(d.n_steps))
+        ts.append(time.perf_counter() - t0)
+    sec = statistics.median(ts[1:])
     return {"value": round(sec * 1000.0, 1), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
-            "sample": "1 chunk (10 Euler steps) of the pi0.5-shaped workload at batch 1, float64 NumPy"}
+            "sample": "1 chunk (10 Euler steps) of the pi0.5-shaped workload at batch 1, float64 NumPy; "
+                      "median of 3 timed runs after 1 warm-up"}
 
 
 def main():
