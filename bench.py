@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "ms per action chunk (10 Euler steps) at batch 1; chunks/sec at batch 32"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
+# loop kernels and their ids for phyai_enqueue_kernel_repeat; "attn_merge" combines the
+# key splits of the few-row attention (its own launch), and has no algorithmic bytes of its own
+KERNEL_IDS = {"qkv": 0, "attention": 1, "attn_merge": 7, "o_proj": 2, "gate_up": 3, "down": 4, "out_euler": 5}
 KERNELS = ["qkv", "attention", "o_proj", "gate_up", "down", "out_euler"]
 
 
@@ -115,10 +118,11 @@ def time_chunks(ex, noise, out, steps, warmup, torch):
     return a.elapsed_time(b) / steps
 
 
-def kernel_times(ex, reps, torch):
+def kernel_times(ex, reps, torch, names=KERNELS):
     """Mean duration of each loop kernel, one graph replay of `reps` launches each."""
     res = {}
-    for which, name in enumerate(KERNELS):
+    for name in names:
+        which = KERNEL_IDS[name]
         ex.enqueue_kernel_repeat(which, 0, reps)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -236,16 +240,7 @@ def main():
     p99 = lat[min(len(lat) - 1, int(round(0.99 * (len(lat) - 1))))]
 
     # isolated kernel durations: one graph replay of back-to-back launches each
-    per_launch_us = {}
-    for which, name in enumerate(KERNELS):
-        ex.enqueue_kernel_repeat(which, 0, args.kernel_reps)   # capture + warm
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        ex.enqueue_kernel_repeat(which, 0, args.kernel_reps)
-        b.record()
-        torch.cuda.synchronize()
-        per_launch_us[name] = a.elapsed_time(b) * 1000.0 / args.kernel_reps
+    per_launch_us = kernel_times(ex, args.kernel_reps, torch, KERNELS + ["attn_merge"])
     launches = {"qkv": d.n_layers, "attention": d.n_layers, "o_proj": d.n_layers, "gate_up": d.n_layers,
                 "down": d.n_layers, "out_euler": 1}
     share = {k: per_launch_us[k] * launches[k] for k in KERNELS}

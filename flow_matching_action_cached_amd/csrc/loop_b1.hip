@@ -5,7 +5,8 @@
 //   k_gemm<QKV>    adaptive-RMSNorm folded in, fused Q|K|V projection, chunk K/V
 //                  written straight into the cache rows after the prefix;
 //   k_attn         split-key flash decode over [cached prefix ; chunk] keys,
-//                  online softmax, deterministic log-sum-exp merge;
+//                  online softmax, one partial per split;
+//   k_attn_merge   log-sum-exp merge of the splits in split order;
 //   k_gemm<RESID>  output projection + residual;
 //   k_gemm<GEGLU>  adaptive-RMSNorm folded in, gate/up projection, gelu(g)*u;
 //   k_gemm<RESID>  down projection + residual;
@@ -322,14 +323,16 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
 
 // ------------------------------------------------------------------ attention
 // End of one query tile's attention (one wave): with S > 1 key splits, publish this split's
-// partial, and the last split to arrive merges all S partials in split order with
-// log-sum-exp weights; then the normalised output goes to o (swizzled [Mpad][Hq*dh], the A
-// operand of the output projection).  o holds O^T of the tile (lane: column r16, rows
+// partial; then either k_attn_merge combines the splits in a later launch (ext_merge), or
+// the last split to arrive merges all S partials in split order with log-sum-exp weights.
+// The normalised output goes to o (swizzled [Mpad][Hq*dh], the A operand of the output
+// projection).  o holds O^T of the tile (lane: column r16, rows
 // 4 grp + i of 16-column tile t), m_run / l_part the running max (log2 units) and this
 // lane's part of the row sums.  item indexes the tile's split workspace and counter.
 template <class AT, int DH>
 __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4 (&o)[DH / 16], float m_run,
-                                            float l_part, int S, int s, size_t item, bool qvalid, int m, int head) {
+                                            float l_part, int S, int s, size_t item, bool qvalid, int m, int head,
+                                            bool ext_merge) {
   constexpr int ES = sizeof(AT);
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   const int qd = d.Hq * DH;
@@ -364,6 +367,7 @@ __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4
                                             0, 16);
     }
     PHASE_MARK(3);
+    if (ext_merge) return;                           // k_attn_merge combines the splits
     const bool last = split_arrive_wave(bf.attn_cnt + item, (unsigned)S);
     PHASE_MARK(4);
     if (!last) return;
@@ -432,20 +436,21 @@ __device__ __forceinline__ void attn_finish(const Dims& d, const Bufs& bf, f32x4
 // Split-key flash decode.  The query rows of one KV head r are the g*H pairs
 // (query head r*g + j, chunk token t), row j*H + t, in 16-row tiles; the keys are
 // the P cached prefix rows followed by the H chunk rows (no mask among them).
-// A workgroup owns (sample, KV head, 4 query tiles, key split).  Its 256 threads stage
-// the split's keys -- up to NB blocks of 32 at once -- as K and V^T tiles in LDS with one
-// burst of loads, and each wave runs one query tile over them: S^T = K q^T on MFMA, a
-// direct softmax over the staged keys (online rescaling only between groups of NB
-// blocks), then O^T += V^T P^T on MFMA.  The probabilities come out of the first product
-// already laid out as the second product's B operand, which is why V is kept transposed
-// in the cache.  Splits are merged with log-sum-exp weights in split order by the last
-// wave to finish.
-template <class AT, int DH>
-__global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
+// A workgroup owns (sample, KV head, 4 query tiles, key split).  Its threads stage the
+// split's keys -- up to NB blocks of 32 at once -- as K and V^T tiles in LDS with one
+// burst of loads; for each query tile one wave (NB = 1) or two waves, one per half of the
+// staged blocks, run S^T = K q^T on MFMA, a direct softmax over the staged keys (online
+// rescaling only between groups of NB blocks), then O^T += V^T P^T on MFMA, and the two
+// halves combine through LDS.  The probabilities come out of the first product already
+// laid out as the second product's B operand, which is why V is kept transposed in the
+// cache.  Each split leaves a partial (O / l, m, l) for k_attn_merge.
+template <class AT, int DH, int NB>
+__global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, int layer, int S, int bps) {
   typedef typename FragOf<AT>::type Frag;
-  constexpr int KH = 2;                               // waves per query tile (key halves of a group)
+  constexpr int KH = NB >= 2 ? 2 : 1;                 // waves per query tile (key halves of a group)
   constexpr int NT = 64 * 4 * KH;                     // threads
-  constexpr int NB = DH * sizeof(AT) <= 512 ? 4 : 2;  // 32-key blocks staged per group (LDS <= 160 KB)
+  static_assert(NB == 1 || NB == 2 || (NB == 4 && DH * sizeof(AT) <= 512),
+                "32-key blocks staged per group (LDS <= 160 KB)");
   constexpr int NBH = NB / KH;                        // blocks of a group per wave
   constexpr int NK = NB * 32;
   constexpr int ES = sizeof(AT);
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
   constexpr int CMB = DH / 4 + 2;                    // floats per lane handed from half 1 to half 0
   constexpr int CMB_B = 4 * CMB * 64 * 4;
   constexpr int PAIR_B = 8 * (DH / 8 + 2) * 64 * 4;  // both halves hand over half their columns
-  constexpr int CMX_B = CMB_B > PAIR_B ? CMB_B : PAIR_B;
+  constexpr int CMX_B = KH == 1 ? 0 : CMB_B > PAIR_B ? CMB_B : PAIR_B;
   constexpr int LDS_B = KS_B + VS_B > CMX_B ? KS_B + VS_B : CMX_B;
   static_assert((KCH + VCH) % NT == 0 && NB % KH == 0, "group size");
   __shared__ __attribute__((aligned(16))) char lds_raw[LDS_B];
@@ -471,13 +476,14 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
   const int wq = w & 3, half = w >> 2;               // query tile slot, key half
   const int gq = d.Hq / d.Hkv;
   const int QT = (gq * d.H + 15) / 16, QG = (QT + 3) / 4;
-  // Workgroups go to the 8 XCDs round robin: the split index is the workgroup index mod 8,
-  // so all query groups of one key split run on one XCD and share its L2 copy of the
-  // split's K/V (S <= 8; the slots s >= S of each row of 8 have no work).
+  // Workgroups go to the 8 XCDs round robin: the split index is the workgroup index mod 8
+  // (or mod 16 / 32 for more splits), so all query groups of one key split run on one XCD
+  // and share its L2 copy of the split's K/V (S <= 32; slots s >= S have no work).
   int idx = blockIdx.x;
-  const int s = idx & 7;
+  const int sl = S > 16 ? 5 : S > 8 ? 4 : 3;
+  const int s = idx & ((1 << sl) - 1);
   if (s >= S) return;
-  idx >>= 3;
+  idx >>= sl;
   const int qg = idx % QG;
   idx /= QG;
   const int r = idx % d.Hkv;
@@ -604,7 +610,10 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
   constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;    // 16-byte partial slots per lane
   constexpr int PAYH = PAY / 2;                        // slots finished by each half
   constexpr bool PAIR = PAYH >= 1 && PAYH <= 4;        // both halves finish the tile
-  if constexpr (!PAIR) {
+  if constexpr (KH == 1) {                             // one wave per tile: nothing to combine
+    if (!active) return;
+    attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head, true);
+  } else if constexpr (!PAIR) {
     float* cmb = reinterpret_cast<float*>(lds_raw) + wq * CMB * 64;
     __syncthreads();
     if (half == 1 && active) {
@@ -628,7 +637,7 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * a0 + cmb[(2 + 4 * t + i) * 64 + lane] * a1;
     }
-    attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head);
+    attn_finish<AT, DH>(d, bf, o, m_run, l_part, S, s, ((size_t)(b * d.Hkv + r) * QT + qt), qvalid, m, head, true);
   } else {
     // Both halves finish the tile, each its own half of the output columns (16-column
     // tiles [half*T2, half*T2 + T2)): each hands the other (m, l) and the other's columns
@@ -637,7 +646,6 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
     // indexed with constants (a run-time index would move them to scratch memory).
     constexpr int T2 = DH / 32;
     constexpr int CM2 = 4 * T2 + 2;                    // floats per lane handed over
-    __shared__ unsigned arrive_flag;
     auto finish = [&](auto hc) {
     constexpr int H = decltype(hc)::value;
     float* mine = reinterpret_cast<float*>(lds_raw) + (wq * 2 + H) * CM2 * 64;
@@ -685,10 +693,8 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
       if (active && qvalid) write_out(oh, 1.0f / l_row);
       return;
     }
-    // Split partial (O / l in the activation type, 16-byte slots; (m, l) in fp32 by half
-    // 0), then one arrival per workgroup: the last workgroup of the query group merges
-    // its four tiles, each half its own slots, fetching every split's statistics and
-    // slots in one round trip.  Every split enters the merge through its stored value.
+    // Split partial (O / l in the activation type, 16-byte slots, each half its own; (m, l)
+    // in fp32 by half 0); k_attn_merge combines the splits in the next launch.
     constexpr uint32_t STRIDE = PAY * 1024 + 128;       // bytes per split partial
     const size_t item = (size_t)(b * d.Hkv + r) * QT + qt;
     const __amdgpu_buffer_rsrc_t ws = agent_rsrc(bf.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
@@ -706,58 +712,81 @@ __global__ __launch_bounds__(512) void k_attn(Dims d, Bufs bf, int layer, int S,
         } else {
           v = oh[uh] * inv_l;
         }
-        st_agent16(ws, s * STRIDE + (u * 64 + lane) * 16, v);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws, s * STRIDE + (u * 64 + lane) * 16, 0, 0);
       }
       if (H == 0 && grp == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0,
-                                              16);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, m_run), ws, s * STRIDE + PAY * 1024 + r16 * 4, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, l_row), ws,
-                                              s * STRIDE + PAY * 1024 + 64 + r16 * 4, 0, 16);
+                                              s * STRIDE + PAY * 1024 + 64 + r16 * 4, 0, 0);
       }
     }
     PHASE_MARK(3);
-    const bool last = split_arrive_wg(bf.attn_cnt + ((size_t)(b * d.Hkv + r) * QG + qg), (unsigned)S, &arrive_flag);
-    PHASE_MARK(4);
-    if (!last || !active) return;
-    float ms[8], ls[8];
-    f32x4 pv[8][PAYH];
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const uint32_t base = min(s2, S - 1) * STRIDE;
-      ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, base + PAY * 1024 + r16 * 4, 0, 16));
-      ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, base + PAY * 1024 + 64 + r16 * 4, 0, 16));
-#pragma unroll
-      for (int uh = 0; uh < PAYH; ++uh) pv[s2][uh] = ld_agent16(ws, base + ((H * PAYH + uh) * 64 + lane) * 16);
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
-      if (s2 < S) M = fmaxf(M, ms[s2]);
-    float den = 0.f;
-    f32x4 acc[T2];
-#pragma unroll
-    for (int t2 = 0; t2 < T2; ++t2) acc[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
-      den += wgt;
-#pragma unroll
-      for (int uh = 0; uh < PAYH; ++uh) {
-        if constexpr (ES == 2) {
-          const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2][uh]);
-          acc[2 * uh] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
-          acc[2 * uh + 1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
-        } else {
-          acc[uh] += wgt * pv[s2][uh];
-        }
-      }
-    }
-    if (qvalid) write_out(acc, 1.0f / den);
     };
     if (half) finish(std::integral_constant<int, 1>{});
     else finish(std::integral_constant<int, 0>{});
   }
   PHASE_MARK(7);
+}
+
+// Merge of the key splits of the few-row attention, one launch after it: a one-wave
+// workgroup per (query tile, 16-byte slot); each lane reads its slot and its row's (m, l)
+// from every split,
+// weights split s by 2^(m_s - M) l_s (M the largest m_s) and writes the normalised output
+// columns of the slot to o.  Slot u of a lane holds output columns 32u + 4 grp + i and
+// 32u + 16 + 4 grp + i (bf16 partials) or 16u + 4 grp + i (fp32), row r16 of the tile.
+template <class AT, int DH, int SM>
+__global__ __launch_bounds__(64) void k_attn_merge(Dims d, Bufs bf, int S) {
+  constexpr int ES = sizeof(AT);
+  constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;
+  constexpr uint32_t STRIDE = PAY * 1024 + 128;
+  const int gq = d.Hq / d.Hkv, QT = (gq * d.H + 15) / 16;
+  const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4;
+  const int u = blockIdx.x % PAY, item = blockIdx.x / PAY;  // one wave per (query tile, slot)
+  if (item >= d.B * d.Hkv * QT) return;
+  const int qt = item % QT, r = (item / QT) % d.Hkv, b = item / QT / d.Hkv;
+  const int qrow = qt * 16 + r16;
+  if (qrow >= gq * d.H) return;
+  const int head = r * gq + qrow / d.H, m = b * d.H + qrow % d.H;
+  const char* ws = reinterpret_cast<const char*>(bf.attn_ws) + (size_t)item * S * STRIDE;
+  float ms[SM], ls[SM];
+  u32x4 pv[SM];
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2) {
+    const char* sp = ws + (size_t)min(s2, S - 1) * STRIDE;
+    ms[s2] = *reinterpret_cast<const float*>(sp + PAY * 1024 + r16 * 4);
+    ls[s2] = *reinterpret_cast<const float*>(sp + PAY * 1024 + 64 + r16 * 4);
+    pv[s2] = *reinterpret_cast<const u32x4*>(sp + (u * 64 + lane) * 16);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2)
+    if (s2 < S) M = fmaxf(M, ms[s2]);
+  float den = 0.f;
+  f32x4 acc[ES == 2 ? 2 : 1];
+#pragma unroll
+  for (int t = 0; t < (ES == 2 ? 2 : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2) {
+    const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+    den += wgt;
+    if constexpr (ES == 2) {
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2]);
+      acc[0] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+      acc[1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
+    } else {
+      acc[0] += wgt * __builtin_bit_cast(f32x4, pv[s2]);
+    }
+  }
+  const float inv = 1.0f / den;
+  const int qd = d.Hq * DH;
+  AT* op = static_cast<AT*>(bf.o);
+#pragma unroll
+  for (int t = 0; t < (ES == 2 ? 2 : 1); ++t) {
+    const int col = (ES == 2 ? 32 * u + 16 * t : 16 * u) + grp * 4;
+    AT* dst = op + sw_idx(m, head * DH + col, qd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = to_elem<AT>(acc[t][i] * inv);
+  }
 }
 
 // ------------------------------------------------------------------ attention, many query rows
@@ -971,7 +1000,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
   for (int p = 0; p < QPW; ++p)
     if (active[p])
       attn_finish<AT, DH>(d, bf, o[p], m_run[p], l_part[p], S, s, (size_t)(b * d.Hkv + r) * QT + qt[p], qvalid[p],
-                          mrow[p], head[p]);
+                          mrow[p], head[p], false);
 }
 
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
@@ -1223,13 +1252,16 @@ Plan make_plan(const Dims& d, WDtype wt) {
   p.s_gu = pick_split(d.D);
   p.s_d = pick_split(d.F);
   // Key splits only as far as needed to give the chip ~256 workgroups (a batch of many
-  // samples needs none), at least four 32-key blocks per split, at most 8 splits (the
-  // merge width).
+  // samples needs none), at most 32 (the merge width of k_attn_merge).  The splits are
+  // merged by a launch of their own over many workgroups, so that a split can be as
+  // short as one 32-key block: at batch 1 the time of a split is its load of K/V into one
+  // CU, and 28 one-block splits beat 7 four-block splits merged in-kernel (8.54 -> 8.05
+  // ms per chunk).
   const int T = d.P + d.H, nblk = (T + 31) / 32;
   const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16, QG = (QT + 3) / 4;
   const int base = d.B * d.Hkv * QG;
   int S = std::max(1, 256 / base);
-  S = std::min(S, std::min(8, (nblk + 3) / 4));
+  S = std::min(S, std::min(32, nblk));
   // Many query tiles (bf16): the shared-staging kernel, with key splits only up to ~256
   // workgroups and at least one whole key group per split.
   p.attn_wide = wt != W_F32 && d.B * d.Hkv * QT >= 64;
@@ -1286,12 +1318,35 @@ static hipError_t launch_gemm(const Dims& d, const Bufs& b, const GemmLaunch& g,
 }
 
 template <class AT>
-static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int layer, hipStream_t st) {
+static hipError_t launch_attn_merge(const Dims& d, const Bufs& b, int S, hipStream_t st) {
+  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
+  const int pay = sizeof(AT) == 2 ? d.dh / 32 : d.dh / 16;
+  dim3 mgrid(d.B * d.Hkv * QT * pay), mblock(64);
+#define PHYAI_MERGE(DH)                                                                          \
+  if (S > 16) hipLaunchKernelGGL((k_attn_merge<AT, DH, 32>), mgrid, mblock, 0, st, d, b, S);      \
+  else hipLaunchKernelGGL((k_attn_merge<AT, DH, 16>), mgrid, mblock, 0, st, d, b, S);
+  switch (d.dh) {
+    case 32: PHYAI_MERGE(32) break;
+    case 64: PHYAI_MERGE(64) break;
+    case 128: PHYAI_MERGE(128) break;
+    case 256: PHYAI_MERGE(256) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef PHYAI_MERGE
+  return hipGetLastError();
+}
+
+// part 0: the attention kernel; part 1: the merge of its key splits (a launch only for the
+// few-row kernel with more than one split).
+template <class AT>
+static hipError_t launch_attn_part(const Dims& d, const Bufs& b, const Plan& p, int layer, int part,
+                                   hipStream_t st) {
   const int T = d.P + d.H, nblk = (T + 31) / 32;
   const int S = (nblk + p.attn_bps - 1) / p.attn_bps;
   const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
   if constexpr (sizeof(AT) == 2) {
     if (p.attn_wide) {
+      if (part) return hipSuccess;                    // merged in-kernel
       const int tpw = attn_wide_tiles(d.dh);
       dim3 grid(d.B * d.Hkv * ((QT + tpw - 1) / tpw) * S), block(512);
       switch (d.dh) {
@@ -1304,15 +1359,26 @@ static hipError_t launch_attn(const Dims& d, const Bufs& b, const Plan& p, int l
       return hipGetLastError();
     }
   }
+  if (S > 32) return hipErrorInvalidValue;
+  if (part) return S > 1 ? launch_attn_merge<AT>(d, b, S, st) : hipSuccess;
   const int QG = (QT + 3) / 4;
-  dim3 grid(d.B * d.Hkv * QG * 8), block(512);  // 8 split slots per query group (S <= 8)
+  dim3 grid(d.B * d.Hkv * QG * (S > 16 ? 32 : S > 8 ? 16 : 8));  // 8, 16 or 32 split slots per query group
+  // blocks staged per group: one or two when a split has that many (four would not always
+  // fit LDS); a single block is run by one wave per query tile
+  const int nb = p.attn_bps == 1 ? 1 : (p.attn_bps <= 2 || d.dh * (int)sizeof(AT) > 512) ? 2 : 4;
+#define PHYAI_ATTN(DH)                                                                                        \
+  if (nb == 1) hipLaunchKernelGGL((k_attn<AT, DH, 1>), grid, dim3(256), 0, st, d, b, layer, S, p.attn_bps);    \
+  else if (nb == 2) hipLaunchKernelGGL((k_attn<AT, DH, 2>), grid, dim3(512), 0, st, d, b, layer, S, p.attn_bps); \
+  else hipLaunchKernelGGL((k_attn<AT, DH, (DH * sizeof(AT) <= 512 ? 4 : 2)>), grid, dim3(512), 0, st, d, b, layer, \
+                          S, p.attn_bps);
   switch (d.dh) {
-    case 32: hipLaunchKernelGGL((k_attn<AT, 32>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
-    case 64: hipLaunchKernelGGL((k_attn<AT, 64>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
-    case 128: hipLaunchKernelGGL((k_attn<AT, 128>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
-    case 256: hipLaunchKernelGGL((k_attn<AT, 256>), grid, block, 0, st, d, b, layer, S, p.attn_bps); break;
+    case 32: PHYAI_ATTN(32) break;
+    case 64: PHYAI_ATTN(64) break;
+    case 128: PHYAI_ATTN(128) break;
+    case 256: PHYAI_ATTN(256) break;
     default: return hipErrorInvalidValue;
   }
+#undef PHYAI_ATTN
   return hipGetLastError();
 }
 
@@ -1322,8 +1388,10 @@ template <> size_t wbytes_row<bf16>(int K) { return (size_t)K * 2; }
 template <> size_t wbytes_row<i4>(int K) { return (size_t)K / 2; }
 
 // One launch of kernel `which` for (step k, layer l).  Kinds: 0 QKV, 1 attention,
-// 2 O + residual, 3 gate/up GeGLU, 4 down + residual, 5 out-projection/Euler/in-projection
-// (layer ignored), 6 in-projection of step 0 (layer ignored).
+// 7 merge of the attention's key splits (no launch when there is none), 2 O + residual,
+// 3 gate/up GeGLU, 4 down + residual, 5 out-projection/Euler/in-projection (layer
+// ignored), 6 in-projection of step 0 (layer ignored).  A layer runs kLayerOrder.
+static constexpr int kLayerOrder[6] = {0, 1, 7, 2, 3, 4};
 template <class AT, class WT, class IOT>
 static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
                              hipStream_t st) {
@@ -1340,7 +1408,9 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_QKV, d.qkv, st);
       return launch_gemm<AT, WT, EPI_QKV, 1>(d, b, g, d.qkv / 16, st);
     case 1:
-      return launch_attn<AT>(d, b, p, l, st);
+      return launch_attn_part<AT>(d, b, p, l, 0, st);
+    case 7:
+      return launch_attn_part<AT>(d, b, p, l, 1, st);
     case 2:  // consumer of h is the MLP norm 2l+1
       g.A = b.o; g.lda = qd; g.K = qd;
       g.W = static_cast<const char*>(b.w_o) + wbytes_row<WT>(qd) * d.D * l;
@@ -1380,7 +1450,7 @@ static hipError_t denoise_impl(const Dims& d, const Bufs& b, const Plan& p, hipS
   hipError_t e = launch_one<AT, WT, IOT>(d, b, p, 6, 0, 0, st);
   for (int k = 0; k < d.N && e == hipSuccess; ++k) {
     for (int l = 0; l < d.L && e == hipSuccess; ++l)
-      for (int which = 0; which < 5 && e == hipSuccess; ++which) e = launch_one<AT, WT, IOT>(d, b, p, which, k, l, st);
+      for (int i = 0; i < 6 && e == hipSuccess; ++i) e = launch_one<AT, WT, IOT>(d, b, p, kLayerOrder[i], k, l, st);
     if (e == hipSuccess) e = launch_one<AT, WT, IOT>(d, b, p, 5, k, 0, st);
   }
   return e;
@@ -1414,7 +1484,9 @@ static hipError_t launch_one_wam(const Dims& d, const Bufs& b, const Plan& p, in
       g.cvec = cv + (size_t)l * d.qkv;
       return launch_gemm_tiled(d, b, g, EPI_QKV, d.qkv, st);
     case 1:
-      return launch_attn<bf16>(d, b, p, 0, st);
+      return launch_attn_part<bf16>(d, b, p, 0, 0, st);
+    case 7:
+      return launch_attn_part<bf16>(d, b, p, 0, 1, st);
     case 2:
       g.A = b.o; g.K = qd; g.W = static_cast<const bf16*>(b.w_o) + (size_t)l * d.D * qd;
       g.scale_next = md + (size_t)(2 * l + 1) * 2 * d.D;
@@ -1447,7 +1519,7 @@ hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipS
   hipError_t e = launch_one_wam(d, b, p, 6, 0, 0, st);
   for (int k = 0; k < d.N && e == hipSuccess; ++k) {
     for (int l = 0; l < d.L && e == hipSuccess; ++l)
-      for (int which = 0; which < 5 && e == hipSuccess; ++which) e = launch_one_wam(d, b, p, which, k, l, st);
+      for (int i = 0; i < 6 && e == hipSuccess; ++i) e = launch_one_wam(d, b, p, kLayerOrder[i], k, l, st);
     if (e == hipSuccess) e = launch_one_wam(d, b, p, 5, k, 0, st);
   }
   return e;

@@ -431,7 +431,7 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
 phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int reps) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();
-  if (which < 0 || which > 6 || reps < 1 || reps > 100000 || layer < 0 || layer >= c->base.L)
+  if (which < 0 || which > 7 || reps < 1 || reps > 100000 || layer < 0 || layer >= c->base.L)
     return fail(c, PHYAI_ERR_INVALID_ARG, "enqueue_kernel_repeat: bad kernel id, layer or reps");
   if (!c->have_weights || !(c->have_prefix || c->joint) || !c->have_tables)
     return fail(c, PHYAI_ERR_BAD_STATE, "enqueue_kernel_repeat: weights, prefix and tables must be set");

@@ -160,9 +160,10 @@ phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
 
 /* Measurement aid: enqueue on the context stream one graph replay of `reps` back-to-back
  * launches of a single kernel of the loop, with the arguments it has at step 0 and layer
- * `layer`.  which: 0 norm-folded QKV (+ chunk K/V into the cache), 1 attention, 2 O-projection
- * + residual, 3 gate/up + GeGLU, 4 down-projection + residual, 5 out-projection + Euler +
- * in-projection, 6 first in-projection.  Requires weights, prefix and tables.  The caller
+ * `layer`.  which: 0 norm-folded QKV (+ chunk K/V into the cache), 1 attention, 7 merge of
+ * the attention's key splits (an empty replay where attention merges in-kernel or runs
+ * unsplit), 2 O-projection + residual, 3 gate/up + GeGLU, 4 down-projection + residual,
+ * 5 out-projection + Euler + in-projection, 6 first in-projection.  Requires weights, prefix and tables.  The caller
  * brackets the call with events on the same stream to time one kernel in isolation.  It
  * overwrites the context's activations, state and chunk K/V rows (re-run phyai_denoise after). */
 phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, int reps);
@@ -179,7 +180,7 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, i
  *   v  = v_u + gamma (v_c - v_u),   z += dt_k v
  * The same context calls apply: phyai_set_timestep_tables, phyai_set_graph_mode, phyai_sync,
  * phyai_last_error, phyai_get_modulation ([n_steps][2][2L+1][2][D], branch-major: cond then
- * uncond), phyai_enqueue_kernel_repeat (which 0..4 as for the expert, 5 out-projections +
+ * uncond), phyai_enqueue_kernel_repeat (which 0..4 and 7 as for the expert, 5 out-projections +
  * guidance + Euler + in-projections, 6 first in-projections) and phyai_destroy.
  * phyai_set_prefix_kv and phyai_denoise refuse a joint context (PHYAI_ERR_BAD_STATE), and the
  * phyai_wam_* calls refuse an action-expert context. */

@@ -138,10 +138,11 @@ def test_pi05_graph_replay_bitwise():
     assert all(torch.equal(eager, o) for o in outs)
 
 
-def test_tiny_long_prefix_uses_bounded_splits():
-    """A prefix long enough that four-block splits would exceed the merge width
-    (prefix 1200 -> 38 key blocks)."""
-    d = dataclasses.replace(TINY, prefix_len=1200)
+@pytest.mark.parametrize("prefix_len", [1200, 2100])
+def test_tiny_long_prefix_uses_bounded_splits(prefix_len):
+    """Prefixes with more key blocks than the merge width (32 splits): 1200 -> 38 blocks
+    in 19 splits of two, 2100 -> 67 blocks in 23 splits of three (four staged blocks)."""
+    d = dataclasses.replace(TINY, prefix_len=prefix_len)
     inp = synth.make_expert_inputs(d, 0)
     got = _run(d, inp)
     assert rel_err(got, ex.denoise(inp, d)) <= 1e-4
