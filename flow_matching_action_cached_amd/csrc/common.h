@@ -176,6 +176,10 @@ __device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t by
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 16);
 }
 
+// 2^x on the hardware exponential (v_exp_f32) without the range scaling of exp2f for
+// results below 2^-126: softmax weights that small count as zero.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -574,22 +574,32 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
           s1 = mma(load_frag(ks + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8), qf[jj], s1);
         }
       }
+      // raw scores (the scale is applied inside the exponential), masked past the split
+      // only in a block that straddles its end
       const int kb = (g0 + j) * 32 + grp * 4;
+      const bool full = (g0 + j) * 32 + 32 <= kend;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[jh][i] = kb + i < kend ? s0[i] * sc : -INFINITY;
-        sv[jh][4 + i] = kb + 16 + i < kend ? s1[i] * sc : -INFINITY;
+        sv[jh][i] = full || kb + i < kend ? s0[i] : -INFINITY;
+        sv[jh][4 + i] = full || kb + 16 + i < kend ? s1[i] : -INFINITY;
         mx = fmaxf(mx, fmaxf(sv[jh][i], sv[jh][4 + i]));
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    l_part *= alpha;
-    m_run = m_new;
+    // Reference max in scaled (log2) units.  It is raised (and O, l rescaled) only when a
+    // row's max exceeds it by more than 8: until then the weights stay below 2^8.
+    const float m_cand = fmaxf(m_run, mx * sc);
+    if (g0 == blk0) {
+      m_run = m_cand;
+    } else if (__any(m_cand > m_run + 8.f)) {
+      const float alpha = fast_exp2(m_run - m_cand);
+      l_part *= alpha;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
+      for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
+      m_run = m_cand;
+    }
+    const float m_new = m_run;
 #pragma unroll
     for (int jh = 0; jh < NBH; ++jh) {
       const int j = jb + jh;
@@ -597,7 +607,7 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
       Frag pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[jh][e] - m_new);
+        const float p = fast_exp2(fmaf(sv[jh][e], sc, -m_new));
         l_part += p;
         pf[e] = to_elem<AT>(p);
       }
@@ -953,13 +963,16 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
           s1[p] += e1;
         }
       }
+      // raw scores (scaled inside the exponential), masked only in a block that straddles
+      // the end of the split
       const int kb = (g0 + j) * 32 + grp * 4;
+      const bool full = (g0 + j) * 32 + 32 <= kend;
 #pragma unroll
       for (int p = 0; p < QPW; ++p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sv[p][j][i] = kb + i < kend ? s0[p][i] * sc : -INFINITY;
-          sv[p][j][4 + i] = kb + 16 + i < kend ? s1[p][i] * sc : -INFINITY;
+          sv[p][j][i] = full || kb + i < kend ? s0[p][i] : -INFINITY;
+          sv[p][j][4 + i] = full || kb + 16 + i < kend ? s1[p][i] : -INFINITY;
           mx[p] = fmaxf(mx[p], fmaxf(sv[p][j][i], sv[p][j][4 + i]));
         }
     }
@@ -967,12 +980,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
     for (int p = 0; p < QPW; ++p) {
       mx[p] = fmaxf(mx[p], __shfl_xor(mx[p], 16, 64));
       mx[p] = fmaxf(mx[p], __shfl_xor(mx[p], 32, 64));
-      const float m_new = fmaxf(m_run[p], mx[p]);
-      const float alpha = exp2f(m_run[p] - m_new);
-      l_part[p] *= alpha;
-      m_run[p] = m_new;
+      // reference max in log2 units, raised (with a rescale) only when exceeded by more than 8
+      const float m_cand = fmaxf(m_run[p], mx[p] * sc);
+      if (g0 == blk0) {
+        m_run[p] = m_cand;
+      } else if (__any(m_cand > m_run[p] + 8.f)) {
+        const float alpha = fast_exp2(m_run[p] - m_cand);
+        l_part[p] *= alpha;
 #pragma unroll
-      for (int t = 0; t < DH / 16; ++t) o[p][t] *= alpha;
+        for (int t = 0; t < DH / 16; ++t) o[p][t] *= alpha;
+        m_run[p] = m_cand;
+      }
     }
     // ---- per key block: probabilities, then O^T += V^T P^T (V fragments shared)
 #pragma unroll
@@ -983,7 +1001,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
       for (int p = 0; p < QPW; ++p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = exp2f(sv[p][j][e] - m_run[p]);
+          const float pv = fast_exp2(fmaf(sv[p][j][e], sc, -m_run[p]));
           l_part[p] += pv;
           pf[p][e] = to_elem<AT>(pv);
         }
