@@ -49,7 +49,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
   static_assert(NSTG >= 2 && NSTG <= 4, "pipeline depth");
   static_assert(EPI != EPI_GEGLU || WNT % 2 == 0, "gate/up tiles come in pairs");
   static_assert(BM <= 64 * NW, "one thread per tile row for the row statistics");
-  __shared__ __attribute__((aligned(16))) u32x4 lds[NSTG][LA + LB][64];
+  // One LDS object per stage: with distinct objects the compiler can tell that the reads of
+  // stage ks do not alias the direct-to-LDS copies into the other stages, and does not wait
+  // for those copies before the reads (with one array it waits for every copy in flight).
+  __shared__ __attribute__((aligned(16))) u32x4 lds0[LA + LB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 lds1[LA + LB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 lds2[NSTG >= 3 ? LA + LB : 1][64];
+  __shared__ __attribute__((aligned(16))) u32x4 lds3[NSTG >= 4 ? LA + LB : 1][64];
+  auto stage = [&](int b) -> u32x4 (*)[64] { return b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3; };
   __shared__ float rinv_s[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
         const int b2 = blk - LA;
         src = W + sw_frag(wtile(tn * BNT + b2 / BKB), ks * BKB + b2 % BKB, g.K, lane);
       }
-      __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&lds[buf][blk][0], 16,
+      __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&stage(buf)[blk][0], 16,
                                        0, 0);
     }
   };
@@ -135,10 +142,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
         for (int kb = 0; kb < BKB; ++kb) {
           bf16x8 af[WMT], bw[WNT];
 #pragma unroll
-          for (int i = 0; i < WMT; ++i) af[i] = __builtin_bit_cast(bf16x8, lds[j][(wm * WMT + i) * BKB + kb][lane]);
+          for (int i = 0; i < WMT; ++i) af[i] = __builtin_bit_cast(bf16x8, stage(j)[(wm * WMT + i) * BKB + kb][lane]);
 #pragma unroll
           for (int t = 0; t < WNT; ++t)
-            bw[t] = __builtin_bit_cast(bf16x8, lds[j][LA + (wn * WNT + t) * BKB + kb][lane]);
+            bw[t] = __builtin_bit_cast(bf16x8, stage(j)[LA + (wn * WNT + t) * BKB + kb][lane]);
 #pragma unroll
           for (int i = 0; i < WMT; ++i)
 #pragma unroll
