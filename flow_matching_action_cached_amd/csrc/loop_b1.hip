@@ -966,15 +966,27 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
       // raw scores (scaled inside the exponential), masked only in a block that straddles
       // the end of the split
       const int kb = (g0 + j) * 32 + grp * 4;
-      const bool full = (g0 + j) * 32 + 32 <= kend;
+      if ((g0 + j) * 32 + 32 <= kend) {                // uniform: every key of the block valid
+#pragma unroll
+        for (int p = 0; p < QPW; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[p][j][i] = s0[p][i];
+            sv[p][j][4 + i] = s1[p][i];
+          }
+      } else {
+#pragma unroll
+        for (int p = 0; p < QPW; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[p][j][i] = kb + i < kend ? s0[p][i] : -INFINITY;
+            sv[p][j][4 + i] = kb + 16 + i < kend ? s1[p][i] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int p = 0; p < QPW; ++p)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[p][j][i] = full || kb + i < kend ? s0[p][i] : -INFINITY;
-          sv[p][j][4 + i] = full || kb + 16 + i < kend ? s1[p][i] : -INFINITY;
-          mx[p] = fmaxf(mx[p], fmaxf(sv[p][j][i], sv[p][j][4 + i]));
-        }
+        for (int i = 0; i < 4; ++i) mx[p] = fmaxf(mx[p], fmaxf(sv[p][j][i], sv[p][j][4 + i]));
     }
 #pragma unroll
     for (int p = 0; p < QPW; ++p) {

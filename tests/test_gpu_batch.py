@@ -55,6 +55,19 @@ def test_tiny_bf16_many_rows(batch):
         assert rel_err(got[b], ref[b]) <= 2e-2
 
 
+@pytest.mark.parametrize("prefix_len", [100, 1200, 2100])
+def test_tiny_bf16_few_rows_key_splits(prefix_len):
+    """Batch 1 (16 rows, the few-row kernels) in bf16 with prefixes that give one-, two-
+    and three-block key splits (4, 19 and 23 splits; one, two and four staged blocks),
+    each merged by the split-merge launch."""
+    d = dataclasses.replace(TINY_BF16, prefix_len=prefix_len)
+    inp = synth.make_expert_inputs(d, 1)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"tiny bf16 batch 1 prefix {prefix_len} rel err {err:.3e}")
+    assert err <= 2e-2
+
+
 def test_tiny_bf16_batch_below_capacity_and_graph_equals_eager():
     """A context sized for 16 samples running 9 of them (a smaller bucket), graph and
     eager giving identical bits."""
