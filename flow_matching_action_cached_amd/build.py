@@ -21,7 +21,9 @@ HEADERS = [os.path.join(CSRC, n) for n in ("common.h", "kernels.h", "epilogue.h"
 # Packed-fp32 VALU forms are kept out of every code object (they are not needed here and
 # the build stays on plain fp32 instructions).
 GPU_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # leading scalar kernel arguments are preloaded into SGPRs at wave launch
+             "-mllvm", "-amdgpu-kernarg-preload-count=8"]
 
 
 def hipcc() -> str:

@@ -60,8 +60,12 @@ __device__ __forceinline__ bf16x8 int4_frag_biased(uint32_t w) {
 }
 
 // ------------------------------------------------------------------ weight-streaming GEMM
+// The operands that the weight and activation loads need (W, A, K, splits, second row
+// block) lead the argument list as scalars: they are preloaded into SGPRs at wave launch,
+// so the loads do not wait for the kernel-argument fetch.
 template <class AT, class WT, int MT, int NT, int KBW, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
+__global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, int Kp, int Sp, int nsec, Dims d,
+                                              Bufs bf, GemmLaunch g) {
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_GEGLU);
   constexpr bool INT4 = __is_same(WT, i4);
   __shared__ f32x4 red[4][NT][MT][64];
@@ -69,19 +73,55 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
   __shared__ unsigned flag;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int s = blockIdx.x % g.S, tile = blockIdx.x / g.S;
+  const int s = blockIdx.x % Sp, tile = blockIdx.x / Sp;
   int nrow[NT];
   nrow[0] = tile * 16;
-  if (NT == 2) nrow[NT - 1] = g.n_second + tile * 16;
+  if (NT == 2) nrow[NT - 1] = nsec + tile * 16;
 
   PHASE_MARK(0);
   // this wave's k-blocks: [kbeg, min(kbeg + KBW, kend)), contiguous
-  const int KB = g.K / 32, kbs = KB / g.S;
+  const int KB = Kp / 32, kbs = KB / Sp;
   const int kbeg = s * kbs + w * KBW, kend = s * kbs + kbs;
 
-  // ---- 1. loads, in the order their results are needed (vmcnt retires in order):
-  // epilogue operands and norm statistics (L2) first, then per quad the weights (HBM)
-  // and activations (L2).  Addresses are clamped to valid rows/quads instead of
+  // ---- 1. loads: first the weights (HBM) and activations (L2), whose addresses come from
+  // the preloaded arguments alone.
+  // A wave owns exactly KBW k-blocks (the host sizes splits so that every wave is full),
+  // except int4 splits of fewer than four quads, whose surplus waves are idle: the
+  // branch below is uniform and no per-block exit exists that the compiler could sink
+  // the loads behind.
+  const bool wave_active = kbeg < kend;
+  const AT* A = static_cast<const AT*>(Ap);
+  typedef typename FragOf<AT>::type AFrag;
+  AFrag af[KBW][MT];
+  typename FragOf<AT>::type wf[INT4 ? 1 : KBW][INT4 ? 1 : NT];   // fp32 / bf16 weight fragments
+  constexpr int NQW = (INT4 && KBW >= 4) ? KBW / 4 : 1;          // int4 quads per wave (KBW >= 4)
+  u32x4 wq[NQW][NT];                                               // int4: one 16-byte slot per quad
+  float wsc[NQW][NT];
+  if (wave_active) {
+#pragma unroll
+    for (int i = 0; i < KBW; ++i) {
+      const int kb = kbeg + i;
+      if constexpr (!INT4) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          wf[i][nt] = load_frag(static_cast<const WT*>(Wp) + sw_frag(nrow[nt] >> 4, kb, Kp, lane));
+      } else {
+        if ((i & 3) == 0) {
+          const int q = kb >> 2;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            wq[i >> 2][nt] =
+                reinterpret_cast<const u32x4*>(Wp)[((size_t)(nrow[nt] >> 4) * (Kp >> 7) + q) * 64 + lane];
+            wsc[i >> 2][nt] = bf16_bits_to_f32(g.Ws[(size_t)(nrow[nt] + r16) * (g.K >> 7) + q]);
+          }
+        }
+      }
+#pragma unroll
+      for (int mtl = 0; mtl < MT; ++mtl) af[i][mtl] = load_frag(A + sw_frag(mtl, kb, Kp, lane));
+    }
+  }
+  // ---- 1b. then the epilogue operands and norm statistics (L2), which wait for the
+  // kernel-argument fetch.  Addresses are clamped to valid rows/quads instead of
   // predicating the loads; rows/quads past the end are masked out afterwards.
   const int mt = w;                            // M-tile this wave finishes in the epilogue
   float epi_h[4] = {0.f, 0.f, 0.f, 0.f};       // residual rows (RESID)
@@ -109,65 +149,8 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) ssv[j] = p[min(j, n4 - 1)];
   }
-  // A wave owns exactly KBW k-blocks (the host sizes splits so that every wave is full),
-  // except int4 splits of fewer than four quads, whose surplus waves are idle: the
-  // branch below is uniform and no per-block exit exists that the compiler could sink
-  // the loads behind.
-  const bool wave_active = kbeg < kend;
-  const AT* A = static_cast<const AT*>(g.A);
-  typedef typename FragOf<AT>::type AFrag;
-  AFrag af[KBW][MT];
-  typename FragOf<AT>::type wf[INT4 ? 1 : KBW][INT4 ? 1 : NT];   // fp32 / bf16 weight fragments
-  constexpr int NQW = (INT4 && KBW >= 4) ? KBW / 4 : 1;          // int4 quads per wave (KBW >= 4)
-  u32x4 wq[NQW][NT];                                               // int4: one 16-byte slot per quad
-  float wsc[NQW][NT];
-  if (wave_active) {
-#pragma unroll
-    for (int i = 0; i < KBW; ++i) {
-      const int kb = kbeg + i;
-      if constexpr (!INT4) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          wf[i][nt] = load_frag(static_cast<const WT*>(g.W) + sw_frag(nrow[nt] >> 4, kb, g.K, lane));
-      } else {
-        if ((i & 3) == 0) {
-          const int q = kb >> 2;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            wq[i >> 2][nt] =
-                reinterpret_cast<const u32x4*>(g.W)[((size_t)(nrow[nt] >> 4) * (g.K >> 7) + q) * 64 + lane];
-            wsc[i >> 2][nt] = bf16_bits_to_f32(g.Ws[(size_t)(nrow[nt] + r16) * (g.K >> 7) + q]);
-          }
-        }
-      }
-#pragma unroll
-      for (int mtl = 0; mtl < MT; ++mtl) af[i][mtl] = load_frag(A + sw_frag(mtl, kb, g.K, lane));
-    }
-  }
   // keep every load above in flight together: nothing below may be scheduled before them
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NORM) {
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < n4) {
-        ss += ssv[j][0];
-        ss += ssv[j][1];
-        ss += ssv[j][2];
-        ss += ssv[j][3];
-      }
-    // fixed-order combination of the four quarters of a row
-    const float s1 = __shfl_xor(ss, 1, 64);
-    const float s2 = __shfl_xor(ss, 2, 64);
-    const float s3 = __shfl_xor(ss, 3, 64);
-    float q0, q1, q2, q3;  // quarter 0..3 of this row
-    q0 = squart == 0 ? ss : squart == 1 ? s1 : squart == 2 ? s2 : s3;
-    q1 = squart == 1 ? ss : squart == 0 ? s1 : squart == 3 ? s2 : s3;
-    q2 = squart == 2 ? ss : squart == 3 ? s1 : squart == 0 ? s2 : s3;
-    q3 = squart == 3 ? ss : squart == 2 ? s1 : squart == 1 ? s2 : s3;
-    if (squart == 0 && (tid >> 2) < d.M) rinv_s[tid >> 2] = 1.0f / sqrtf((((q0 + q1) + q2) + q3) / (float)d.D + d.eps);
-  }
-
   PHASE_MARK(1);
   // ---- 2. MFMA
   f32x4 acc[NT][MT];
@@ -213,6 +196,30 @@ __global__ __launch_bounds__(256) void k_gemm(Dims d, Bufs bf, GemmLaunch g) {
             for (int e = 0; e < 4; ++e) acc[nt][mtl][e] += wsc[qi][nt] * (part[nt][mtl][e] - 136.0f * rs[mtl][e]);
       }
     }
+  }
+
+  // row norms (needed by the epilogue only): after the products, so that the MFMAs start
+  // as soon as the weights and activations have landed
+  if constexpr (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < n4) {
+        ss += ssv[j][0];
+        ss += ssv[j][1];
+        ss += ssv[j][2];
+        ss += ssv[j][3];
+      }
+    // fixed-order combination of the four quarters of a row
+    const float s1 = __shfl_xor(ss, 1, 64);
+    const float s2 = __shfl_xor(ss, 2, 64);
+    const float s3 = __shfl_xor(ss, 3, 64);
+    float q0, q1, q2, q3;  // quarter 0..3 of this row
+    q0 = squart == 0 ? ss : squart == 1 ? s1 : squart == 2 ? s2 : s3;
+    q1 = squart == 1 ? ss : squart == 0 ? s1 : squart == 3 ? s2 : s3;
+    q2 = squart == 2 ? ss : squart == 3 ? s1 : squart == 0 ? s2 : s3;
+    q3 = squart == 3 ? ss : squart == 2 ? s1 : squart == 1 ? s2 : s3;
+    if (squart == 0 && (tid >> 2) < d.M) rinv_s[tid >> 2] = 1.0f / sqrtf((((q0 + q1) + q2) + q3) / (float)d.D + d.eps);
   }
 
   PHASE_MARK(2);
@@ -1337,10 +1344,10 @@ static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& 
   if (__is_same(WT, i4) && qps > 4 && qps % 4) return hipErrorInvalidValue;
   dim3 grid(tiles * g.S), block(256);
   switch (kbw) {
-    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, d, b, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, d, b, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, d, b, g); break;
-    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, d, b, g); break;
+    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
+    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
