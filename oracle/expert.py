@@ -27,7 +27,10 @@ design notes with its reason):
 * adaptive RMSNorm  h / sqrt(mean(h^2) + eps) * (1 + scale) + shift, no gain;
 * pre-norm layer: attention block then GeGLU MLP block, both residual;
 * chunk tokens attend to every prefix key and every chunk key (no mask among
-  them, no positional encoding, softmax scale 1/sqrt(head_dim));
+  them, softmax scale 1/sqrt(head_dim)); by default no positional encoding is
+  applied to the chunk (the prefix K/V is given already encoded); with a
+  rotary base theta > 0 the chunk's queries and keys are rotated at positions
+  P + t (rope below);
 * grouped-query heads: query head i reads KV head floor(i / (Hq/Hkv));
 * GELU in its tanh form; no biases in the expert linears.
 """
@@ -118,6 +121,26 @@ def attention(q, k, v):
     return out
 
 
+def rope(x, positions, theta):
+    """Rotary position embedding on interleaved pairs: for each head row at position
+    p, the pair (x_{2i}, x_{2i+1}) is turned by the angle p * theta^(-2i/dh).
+
+    x: [n_heads][T][dh]; positions: [T].  A fidelity variant of the expert (the
+    pages stress positional precision, PhyAI reading Sec. 2); the pages print no
+    convention, so interleaved pairs and base theta are a reading.
+    """
+    x = np.asarray(x, F64)
+    dh = x.shape[-1]
+    freq = F64(theta) ** (-2.0 * np.arange(dh // 2, dtype=F64) / dh)
+    ang = np.asarray(positions, F64)[:, None] * freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
 def _heads(x, n_heads, head_dim):
     """[T][n_heads*head_dim] -> [n_heads][T][head_dim]."""
     return x.reshape(x.shape[0], n_heads, head_dim).transpose(1, 0, 2)
@@ -136,6 +159,11 @@ def expert_layer(h, l, mods, p, k_pre_l, v_pre_l, dims):
     q = _heads(qkv[:, : hq * dh], hq, dh)
     kc = _heads(qkv[:, hq * dh:(hq + hkv) * dh], hkv, dh)
     vc = _heads(qkv[:, (hq + hkv) * dh:], hkv, dh)
+    theta = getattr(dims, "rope_theta", 0.0)
+    if theta > 0:  # chunk token t sits at position P + t, after the prefix
+        pos = np.asarray(k_pre_l).shape[0] + np.arange(h.shape[0])
+        q = rope(q, pos, theta)
+        kc = rope(kc, pos, theta)
     kk = np.concatenate([np.asarray(k_pre_l, F64).transpose(1, 0, 2), kc], axis=1)
     vv = np.concatenate([np.asarray(v_pre_l, F64).transpose(1, 0, 2), vc], axis=1)
     o = attention(q, kk, vv)                                   # [Hq][H][dh]

@@ -65,6 +65,7 @@ class ExpertDims:
     weight_dtype: str          # "f32" | "bf16" | "int4"
     rms_eps: float = 1e-6
     weight_std: float = 0.02
+    rope_theta: float = 0.0    # > 0: rotary embedding of the chunk's Q/K at positions P + t
 
     @property
     def n_mod(self) -> int:    # one (scale, shift) pair per norm: 2 per layer + final

@@ -371,3 +371,53 @@ def test_batch_independence():
     one = _inputs(d, batch=1, samples=[2])
     assert np.array_equal(ex.denoise(one, d)[0], xb[2])
     assert np.array_equal(one["noise"][0], inp["noise"][2])
+
+
+# ---------------------------------------------------------------- rotary position embedding
+# Fidelity variant of the expert: the chunk's queries and keys rotated at positions P + t
+# (interleaved pairs, base theta; a reading, the pages print no convention).
+
+def test_rope_hand_worked_example():
+    """dh = 4, theta = 16: pair 0 turns by p rad, pair 1 by p * 16^(-1/2) = p / 4 rad.
+    x = [1, 0, 1, 0] at p = 4 -> [cos 4, sin 4, cos 1, sin 1]; x = [0, 1, 0, 1] at p = 4
+    -> [-sin 4, cos 4, -sin 1, cos 1] (counter-clockwise turn of (x_2i, x_2i+1))."""
+    x = np.array([[[1.0, 0.0, 1.0, 0.0], [0.0, 1.0, 0.0, 1.0]]])
+    got = ex.rope(x, np.array([4.0, 4.0]), 16.0)
+    want = np.array([[[math.cos(4), math.sin(4), math.cos(1), math.sin(1)],
+                      [-math.sin(4), math.cos(4), -math.sin(1), math.cos(1)]]])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_identity_norms_composition_and_relative_positions():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((2, 6, 16))
+    k = rng.standard_normal((2, 6, 16))
+    pos = np.array([0.0, 1.0, 5.0, 33.0, 816.0, 865.0])
+    # position 0 is the identity; every pair keeps its length
+    np.testing.assert_array_equal(ex.rope(q[:, :1], np.array([0.0]), 1e4), q[:, :1])
+    rq = ex.rope(q, pos, 1e4)
+    np.testing.assert_allclose(np.hypot(rq[..., 0::2], rq[..., 1::2]), np.hypot(q[..., 0::2], q[..., 1::2]),
+                               rtol=1e-13)
+    # angles are linear in the position: R(a) R(b) = R(a + b)
+    a, b = np.array([3.0] * 6), pos
+    np.testing.assert_allclose(ex.rope(ex.rope(q, a, 1e4), b, 1e4), ex.rope(q, a + b, 1e4), atol=1e-12)
+    # scores depend only on the position difference: <R(m) q, R(n) k> = <R(m+s) q, R(n+s) k>
+    m, n, s = pos, pos[::-1].copy(), 97.0
+    d0 = np.sum(ex.rope(q, m, 1e4) * ex.rope(k, n, 1e4), axis=-1)
+    d1 = np.sum(ex.rope(q, m + s, 1e4) * ex.rope(k, n + s, 1e4), axis=-1)
+    np.testing.assert_allclose(d0, d1, atol=1e-11)
+
+
+def test_rope_variant_is_wired_into_the_loop():
+    """theta = 0 is the plain expert and theta > 0 changes the result; with no prefix a
+    one-token chunk sits at position 0, where the rotation is the identity, so it equals
+    the plain expert."""
+    d = synth.CONFIGS["tiny"]
+    inp = synth.make_expert_inputs(d, 0)
+    plain = ex.denoise(inp, d)
+    rot = ex.denoise(inp, dataclasses.replace(d, rope_theta=1e4))
+    assert ex.rel_err(rot, plain) > 1e-3
+    d1 = dataclasses.replace(d, prefix_len=0, chunk_len=1)
+    inp1 = synth.make_expert_inputs(d1, 0)
+    np.testing.assert_allclose(ex.denoise(inp1, dataclasses.replace(d1, rope_theta=1e4)), ex.denoise(inp1, d1),
+                               rtol=0, atol=1e-14)
