@@ -18,6 +18,7 @@ dominant kernel, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -177,8 +178,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,b32,wam",
-                    help="comma-separated variants to measure after the batch-1 line: int4, b32, wam")
+    ap.add_argument("--variants", default="int4,rope,b32,wam",
+                    help="comma-separated variants to measure after the batch-1 line: int4, rope, b32, wam")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -287,6 +288,29 @@ def main():
                                         "algorithmic_bytes": b4,
                                         "hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] int4 variant: {ms4:.4f} ms/chunk", file=sys.stderr, flush=True)
+
+    if "rope" in todo:
+        # the same batch-1 workload with the chunk's queries and keys rotated (base 1e4)
+        dr = dataclasses.replace(d, rope_theta=1e4)
+        er = fm.ActionExpert.from_dims(dr)
+        er.set_weights(w)
+        er.set_prefix_kv(kp, vp)
+        er.set_timestep_tables(schedule(d.n_steps))
+        for _ in range(args.warmup):
+            er.denoise(noise, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            er.denoise(noise, out)
+        b.record()
+        torch.cuda.synchronize()
+        msr = a.elapsed_time(b) / args.steps
+        er.close()
+        variants["rope_batch1"] = {"ms_per_chunk": round(msr, 4), "chunks_per_s": round(1000.0 / msr, 2),
+                                   "rope_theta": 1e4,
+                                   "hbm_frac": round(chunk_bytes(d) / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] rope variant: {msr:.4f} ms/chunk", file=sys.stderr, flush=True)
 
     if "b32" in todo:
         # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs

@@ -26,6 +26,22 @@ struct GemmLaunch {
   const float* scale_next;   // raw scale of the norm that consumes h (RESID)
 };
 
+// Rotary position embedding of the QKV output y at token row m, column col (PhyAI reading
+// Sec. 2 stresses positional precision; the pages print no convention): the query and key
+// columns of every head form interleaved pairs (2i, 2i+1), turned by the angle
+// p * theta^(-2i/dh) at the chunk token's position p = P + (m mod H).  yp is the pair
+// partner's value (the neighbouring lane holds column col ^ 1 of the same row); value
+// columns are returned unchanged.  Angle in fp32: the position is exact, the frequency is
+// rounded once.
+__device__ __forceinline__ float rope_rotate(const Dims& d, int m, int col, float y, float yp) {
+  if (col >= (d.Hq + d.Hkv) * d.dh) return y;
+  const int pair = (col % d.dh) >> 1;
+  const float freq = exp2f(-(float)(2 * pair) / (float)d.dh * log2f(d.rope_theta));
+  float sn, cs;
+  sincosf((float)(d.P + m % d.H) * freq, &sn, &cs);
+  return (col & 1) ? fmaf(yp, sn, y * cs) : fmaf(y, cs, -yp * sn);
+}
+
 // QKV output y of token row m, column col: q rows go to q [M][Hq*dh]; the chunk's own
 // K and V go straight into the cache after the prefix rows (V transposed).
 template <class AT>

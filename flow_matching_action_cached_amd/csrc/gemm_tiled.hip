@@ -171,10 +171,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
         const int col = (vt0 + j) * 16 + r16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = m0 + e;
+          const int m = m0 + e, mc = min(m, d.M - 1);  // rows past the end: any valid row's tables
+          const float c = g.cvec[(size_t)(mc / d.rows_per_tab) * bf.cv_stride + col];
+          float y = rinv_s[m - tm * BM] * acc[i][j][e] + c;
+          if (d.rope_theta > 0.f) y = rope_rotate(d, m, col, y, __shfl_xor(y, 1, 64));  // all lanes shuffle
           if (m >= d.M) continue;
-          const float c = g.cvec[(size_t)(m / d.rows_per_tab) * bf.cv_stride + col];
-          qkv_store<AT>(d, bf, g.layer, m, col, rinv_s[m - tm * BM] * acc[i][j][e] + c);
+          qkv_store<AT>(d, bf, g.layer, m, col, y);
         }
       }
     } else if constexpr (EPI == EPI_RESID) {

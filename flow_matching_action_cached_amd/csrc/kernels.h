@@ -23,6 +23,7 @@ struct Dims {
   int joint;                       // 1: joint video/action denoiser (no prefix, guided branch pair)
   int Tl, Cl;                      // joint denoiser: latent tokens and their channels (0 otherwise)
   float gamma;                     // joint denoiser: guidance scale
+  float rope_theta;                // > 0: rotary embedding of the chunk's Q/K at positions P + t
 };
 
 // Device pointers of one context.  Element types depend on the weight dtype:

@@ -282,9 +282,10 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
     AT* vt = static_cast<AT*>(bf.vt);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + grp * 4 + i;
+      const int m = mt * 16 + grp * 4 + i;       // < 64: rinv_s holds every row slot
+      float y = rinv_s[m] * tot[0][i] + c;
+      if (d.rope_theta > 0.f) y = rope_rotate(d, m, col, y, __shfl_xor(y, 1, 64));  // all lanes shuffle
       if (m >= d.M) continue;
-      const float y = rinv_s[m] * tot[0][i] + c;
       const int b = m / d.H, t = m % d.H;
       if (col < qd) {
         q[(size_t)m * qd + col] = to_elem<AT>(y);

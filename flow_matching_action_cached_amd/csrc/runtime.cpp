@@ -154,7 +154,8 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   if (!cfg) return PHYAI_ERR_INVALID_ARG;
   const phyai_config& g = *cfg;
   if (g.n_layers < 1 || g.width < 1 || g.n_q_heads < 1 || g.n_kv_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 ||
-      g.action_dim < 1 || g.chunk_len < 1 || g.max_prefix_len < 1 || g.max_batch < 1 || !(g.rms_eps > 0.f))
+      g.action_dim < 1 || g.chunk_len < 1 || g.max_prefix_len < 1 || g.max_batch < 1 || !(g.rms_eps > 0.f) ||
+      !(g.rope_theta == 0.f || (g.rope_theta > 1.f && g.rope_theta < 1e30f)))
     return PHYAI_ERR_INVALID_ARG;
   if (g.weight_dtype != PHYAI_F32 && g.weight_dtype != PHYAI_BF16 && g.weight_dtype != PHYAI_INT4_G128)
     return PHYAI_ERR_INVALID_ARG;
@@ -196,6 +197,7 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   d.Tl = 0;
   d.Cl = 0;
   d.gamma = 0.f;
+  d.rope_theta = g.rope_theta;
 
   const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
   Layout lay;
@@ -534,6 +536,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   d.Tl = g.latent_tokens;
   d.Cl = g.latent_dim;
   d.gamma = 0.f;
+  d.rope_theta = 0.f;
   // mirror into cfg the fields the shared calls read
   c->cfg.n_layers = g.n_layers; c->cfg.width = g.width; c->cfg.n_q_heads = g.n_heads; c->cfg.n_kv_heads = g.n_heads;
   c->cfg.head_dim = g.head_dim; c->cfg.mlp_dim = g.mlp_dim; c->cfg.action_dim = g.action_dim;

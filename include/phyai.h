@@ -78,6 +78,12 @@ typedef struct {
   phyai_dtype weight_dtype;
   float rms_eps;              /* > 0, e.g. 1e-6 */
   size_t max_arena_bytes;     /* 0 = no limit; else creation fails with OOM above it */
+  float rope_theta;           /* 0: no positional encoding of the chunk (the prefix K/V comes
+                                 encoded); > 1: rotary embedding of the chunk's queries and keys
+                                 at positions P + t (chunk token t after a P-token prefix):
+                                 interleaved pairs (2i, 2i+1) of every head turned by
+                                 (P + t) * rope_theta^(-2i/head_dim) (the pages stress positional
+                                 precision, PhyAI reading Sec. 2; the convention is a reading) */
 } phyai_config;
 
 /* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,

@@ -69,6 +69,9 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(head_dim=48))[0] == 5
     assert _create(lib, _cfg(n_q_heads=3, n_kv_heads=2))[0] == 5
     assert _create(lib, _cfg(chunk_len=50, max_batch=2))[0] == 5   # many rows need bf16 weights
+    assert _create(lib, _cfg(rope_theta=0.5))[0] == 1               # rotary base must be 0 or > 1
+    assert _create(lib, _cfg(rope_theta=-1e4))[0] == 1
+    assert _create(lib, _cfg(rope_theta=float("nan")))[0] == 1
     st, h = _create(lib, _cfg(n_layers=0))
     assert h.value is None
 

@@ -138,6 +138,21 @@ def test_pi05_graph_replay_bitwise():
     assert all(torch.equal(eager, o) for o in outs)
 
 
+@pytest.mark.parametrize("cfg,tol", [("tiny", 1e-4), ("pi05", 2e-2)])
+def test_rope_variant_matches_oracle(cfg, tol):
+    """Rotary embedding of the chunk's queries and keys (positions P + t, base 1e4) in the
+    QKV epilogue of the weight-streaming GEMM, against the oracle's rotation."""
+    d = dataclasses.replace({"tiny": TINY, "pi05": PI05}[cfg], rope_theta=1e4)
+    _say(f"case: rope {cfg}")
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    ref = ex.denoise(inp, d)
+    err = rel_err(got, ref)
+    _say(f"rope {cfg} rel err {err:.3e}")
+    assert err <= tol
+    assert rel_err(ref, ex.denoise(inp, dataclasses.replace(d, rope_theta=0.0))) > 2 * tol  # the rotation matters
+
+
 @pytest.mark.parametrize("prefix_len", [1200, 2100])
 def test_tiny_long_prefix_uses_bounded_splits(prefix_len):
     """Prefixes with more key blocks than the merge width (32 splits): 1200 -> 38 blocks
