@@ -25,7 +25,9 @@ design notes with its reason):
   [sin | cos] halves;
 * one linear map per norm turns the embedding into (scale, shift);
 * adaptive RMSNorm  h / sqrt(mean(h^2) + eps) * (1 + scale) + shift, no gain;
-* pre-norm layer: attention block then GeGLU MLP block, both residual;
+* pre-norm layer: attention block then GeGLU MLP block, both residual; with a
+  gated residual (fidelity variant) each norm's map also yields a gate and the
+  block's output enters the residual as gate * output;
 * chunk tokens attend to every prefix key and every chunk key (no mask among
   them, softmax scale 1/sqrt(head_dim)); by default no positional encoding is
   applied to the chunk (the prefix K/V is given already encoded); with a
@@ -72,20 +74,21 @@ def timestep_embedding(t: float, width: int) -> np.ndarray:
 
 
 def modulation_tables(t, w_mod, b_mod) -> np.ndarray:
-    """Per-step (scale, shift) of every adaptive norm: m = W_m[j] e(t_k) + b_m[j].
+    """Per-step (scale, shift[, gate]) of every adaptive norm: m = W_m[j] e(t_k) + b_m[j].
 
-    Returns [N][n_mod][2][D] float64; index j = 2l (attention norm of layer l),
-    2l+1 (MLP norm of layer l), 2L (final norm).  These are the precomputed
-    timestep/modulation tables of PhyAI reading Sec. 5.1 / 5.5.
+    Returns [N][n_mod][R][D] float64 with R = W_m rows / D (2: scale, shift; 3 with the
+    residual gate); index j = 2l (attention norm of layer l), 2l+1 (MLP norm of layer
+    l), 2L (final norm).  These are the precomputed timestep/modulation tables of
+    PhyAI reading Sec. 5.1 / 5.5.
     """
     w_mod = np.asarray(w_mod, dtype=F64)
     b_mod = np.asarray(b_mod, dtype=F64)
-    n_mod, two_d, d = w_mod.shape
-    out = np.empty((len(t), n_mod, 2, d), dtype=F64)
+    n_mod, rows, d = w_mod.shape
+    out = np.empty((len(t), n_mod, rows // d, d), dtype=F64)
     for k, tk in enumerate(np.asarray(t, dtype=F64)):
         e = timestep_embedding(tk, d)
         m = np.einsum("jod,d->jo", w_mod, e) + b_mod
-        out[k] = m.reshape(n_mod, 2, d)
+        out[k] = m.reshape(n_mod, rows // d, d)
     return out
 
 
@@ -153,7 +156,8 @@ def expert_layer(h, l, mods, p, k_pre_l, v_pre_l, dims):
     (PhyAI reading Sec. 5.1: the prefix KV is computed once and reused).
     """
     hq, hkv, dh, f = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.mlp_dim
-    sc, sh = mods[2 * l]
+    gated = mods.shape[1] == 3  # residual gates: the third row of each norm's map
+    sc, sh = mods[2 * l][0], mods[2 * l][1]
     u = ada_rms(h, sc, sh, dims.rms_eps)
     qkv = u @ p["w_qkv"][l].T
     q = _heads(qkv[:, : hq * dh], hq, dh)
@@ -168,12 +172,14 @@ def expert_layer(h, l, mods, p, k_pre_l, v_pre_l, dims):
     vv = np.concatenate([np.asarray(v_pre_l, F64).transpose(1, 0, 2), vc], axis=1)
     o = attention(q, kk, vv)                                   # [Hq][H][dh]
     o = o.transpose(1, 0, 2).reshape(h.shape[0], hq * dh)
-    h = h + o @ p["w_o"][l].T
-    sc, sh = mods[2 * l + 1]
+    blk = o @ p["w_o"][l].T
+    h = h + (mods[2 * l][2] * blk if gated else blk)
+    sc, sh = mods[2 * l + 1][0], mods[2 * l + 1][1]
     u = ada_rms(h, sc, sh, dims.rms_eps)
     gu = u @ p["w_gu"][l].T
     a = gelu_tanh(gu[:, :f]) * gu[:, f:]
-    return h + a @ p["w_d"][l].T
+    blk = a @ p["w_d"][l].T
+    return h + (mods[2 * l + 1][2] * blk if gated else blk)
 
 
 def velocity(x, mods, p, k_pre, v_pre, dims):
@@ -185,7 +191,7 @@ def velocity(x, mods, p, k_pre, v_pre, dims):
     h = x @ p["w_in"].T + p["b_in"]
     for l in range(dims.n_layers):
         h = expert_layer(h, l, mods, p, k_pre[l], v_pre[l], dims)
-    sc, sh = mods[2 * dims.n_layers]
+    sc, sh = mods[2 * dims.n_layers][0], mods[2 * dims.n_layers][1]
     u = ada_rms(h, sc, sh, dims.rms_eps)
     return u @ p["w_out"].T + p["b_out"]
 

@@ -66,6 +66,7 @@ class ExpertDims:
     rms_eps: float = 1e-6
     weight_std: float = 0.02
     rope_theta: float = 0.0    # > 0: rotary embedding of the chunk's Q/K at positions P + t
+    gated_residual: bool = False  # each norm's map also yields a residual gate (3 D rows)
 
     @property
     def n_mod(self) -> int:    # one (scale, shift) pair per norm: 2 per layer + final
@@ -111,7 +112,8 @@ def expert_param_shapes(d: ExpertDims) -> dict:
     L, D, A, F = d.n_layers, d.width, d.action_dim, d.mlp_dim
     return {
         "w_in": (D, A), "b_in": (D,), "w_out": (A, D), "b_out": (A,),
-        "w_mod": (d.n_mod, 2 * D, D), "b_mod": (d.n_mod, 2 * D),
+        "w_mod": (d.n_mod, (3 if getattr(d, "gated_residual", False) else 2) * D, D),
+        "b_mod": (d.n_mod, (3 if getattr(d, "gated_residual", False) else 2) * D),
         "w_qkv": (L, d.qkv_dim, D), "w_o": (L, D, d.n_q_heads * d.head_dim),
         "w_gu": (L, 2 * F, D), "w_d": (L, D, F),
     }
@@ -197,7 +199,8 @@ def wam_param_shapes(d: WamDims) -> dict:
         "w_in_lat": (D, d.latent_dim), "b_in_lat": (D,), "w_in_act": (D, d.action_dim), "b_in_act": (D,),
         "w_out_lat": (d.latent_dim, D), "b_out_lat": (d.latent_dim,),
         "w_out_act": (d.action_dim, D), "b_out_act": (d.action_dim,),
-        "w_mod": (d.n_mod, 2 * D, D), "b_mod": (d.n_mod, 2 * D),
+        "w_mod": (d.n_mod, (3 if getattr(d, "gated_residual", False) else 2) * D, D),
+        "b_mod": (d.n_mod, (3 if getattr(d, "gated_residual", False) else 2) * D),
         "w_qkv": (L, 3 * hd, D), "w_o": (L, D, hd), "w_gu": (L, 2 * F, D), "w_d": (L, D, F),
     }
 

@@ -421,3 +421,47 @@ def test_rope_variant_is_wired_into_the_loop():
     inp1 = synth.make_expert_inputs(d1, 0)
     np.testing.assert_allclose(ex.denoise(inp1, dataclasses.replace(d1, rope_theta=1e4)), ex.denoise(inp1, d1),
                                rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- gated residual
+# Fidelity variant: each norm's modulation map yields (scale, shift, gate) and a block's
+# output enters the residual as gate * output (a reading; the pages print no equation).
+
+def _gated(d):
+    dg = dataclasses.replace(d, gated_residual=True)
+    return dg, synth.make_expert_inputs(dg, 0)
+
+
+def test_gated_residual_with_unit_gates_is_the_plain_expert():
+    """Gate rows of W_mod zero and their bias one: gate = 1 exactly, so the result equals the
+    plain expert fed the same scale and shift rows, bit for bit."""
+    d = synth.CONFIGS["tiny"]
+    dg, inp = _gated(d)
+    D = d.width
+    inp["w_mod"][:, 2 * D:, :] = 0.0
+    inp["b_mod"][:, 2 * D:] = 1.0
+    plain = dict(inp, w_mod=inp["w_mod"][:, : 2 * D, :].copy(), b_mod=inp["b_mod"][:, : 2 * D].copy())
+    np.testing.assert_array_equal(ex.denoise(inp, dg), ex.denoise(plain, d))
+    # any other gate changes the result
+    inp["b_mod"][:, 2 * D:] = 0.5
+    assert ex.rel_err(ex.denoise(inp, dg), ex.denoise(plain, d)) > 1e-3
+
+
+def test_gated_residual_with_zero_gates_drops_every_block():
+    """Gate = 0: every attention and MLP block vanishes from the residual stream, so the
+    velocity is the final norm and out-projection of the in-projection alone -- a model
+    with no layers and the same final-norm rows."""
+    d = synth.CONFIGS["tiny"]
+    dg, inp = _gated(d)
+    D, L = d.width, d.n_layers
+    inp["w_mod"][:, 2 * D:, :] = 0.0
+    inp["b_mod"][:, 2 * D:] = 0.0
+    d0 = dataclasses.replace(d, n_layers=0)
+    none = dict(inp)
+    none["w_mod"] = inp["w_mod"][2 * L:, : 2 * D, :].copy()
+    none["b_mod"] = inp["b_mod"][2 * L:, : 2 * D].copy()
+    for k in ("w_qkv", "w_o", "w_gu", "w_d"):
+        none[k] = inp[k][:0]
+    none["k_pre"] = inp["k_pre"][:, :0]
+    none["v_pre"] = inp["v_pre"][:, :0]
+    np.testing.assert_allclose(ex.denoise(inp, dg), ex.denoise(none, d0), rtol=0, atol=1e-13)
