@@ -178,8 +178,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,b32,wam",
-                    help="comma-separated variants to measure after the batch-1 line: int4, rope, b32, wam")
+    ap.add_argument("--variants", default="int4,rope,gated,b32,wam",
+                    help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, b32, wam")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -311,6 +311,33 @@ def main():
                                    "rope_theta": 1e4,
                                    "hbm_frac": round(chunk_bytes(d) / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] rope variant: {msr:.4f} ms/chunk", file=sys.stderr, flush=True)
+
+    if "gated" in todo:
+        # the same batch-1 workload with residual gates (a third row block of W_mod, seeded)
+        dg = dataclasses.replace(d, gated_residual=True)
+        inpg = synth.make_expert_inputs(dg, 0)
+        wg = dict(w)
+        for k in ("w_mod", "b_mod"):
+            wg[k] = torch.from_numpy(inpg[k]).cuda().to(torch.bfloat16).contiguous()
+        del inpg
+        eg = fm.ActionExpert.from_dims(dg)
+        eg.set_weights(wg)
+        eg.set_prefix_kv(kp, vp)
+        eg.set_timestep_tables(schedule(d.n_steps))
+        for _ in range(args.warmup):
+            eg.denoise(noise, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            eg.denoise(noise, out)
+        b.record()
+        torch.cuda.synchronize()
+        msg = a.elapsed_time(b) / args.steps
+        eg.close()
+        variants["gated_residual_batch1"] = {"ms_per_chunk": round(msg, 4), "chunks_per_s": round(1000.0 / msg, 2),
+                                             "hbm_frac": round(chunk_bytes(d) / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] gated-residual variant: {msg:.4f} ms/chunk", file=sys.stderr, flush=True)
 
     if "b32" in todo:
         # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs

@@ -183,13 +183,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const int col = (vt0 + j) * 16 + r16;
+        const float gt = g.gate ? g.gate[col] : 1.f;  // residual gate (1: plain residual, exact)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + e;
           float hn = 0.f;
           if (m < d.M) {
             const float sc1 = 1.0f + g.scale_next[(size_t)(m / d.rows_per_tab) * scale_tab + col];
-            hn = resid_store<AT>(d, bf, m, col, bf.h[(size_t)m * d.D + col], acc[i][j][e], sc1);
+            hn = resid_store<AT>(d, bf, m, col, bf.h[(size_t)m * d.D + col], gt * acc[i][j][e], sc1);
           }
           const float sq = sum16(hn * hn);
           if (r16 == 0 && m < d.M) bf.ssq[(size_t)m * (d.D / 16) + vt0 + j] = sq;

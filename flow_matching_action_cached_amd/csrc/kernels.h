@@ -24,6 +24,7 @@ struct Dims {
   int Tl, Cl;                      // joint denoiser: latent tokens and their channels (0 otherwise)
   float gamma;                     // joint denoiser: guidance scale
   float rope_theta;                // > 0: rotary embedding of the chunk's Q/K at positions P + t
+  int gated;                       // 1: each norm's map also yields a residual gate (3 D rows per norm)
 };
 
 // Device pointers of one context.  Element types depend on the weight dtype:
@@ -37,6 +38,7 @@ struct Bufs {
   const uint16_t *s_qkv, *s_o, *s_gu, *s_d;                 // int4 scales (bf16 bits)
   void *kc, *vt;          // K cache [Bmax][L][Hkv][KS][dh], V^T cache [Bmax][L][Hkv][dh][KS] (act)
   const float* mod;       // [N][ntab][nmod][2][D] (scale, shift)
+  const float* gate;      // [N][ntab][nmod][D] residual gates (gated variant; null otherwise)
   const float* cvec;      // [N][ntab][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
   const float* dt;        // [N]
   int cv_stride, cv_gu_off, cv_out_off;
@@ -76,7 +78,7 @@ hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int whic
 
 // One-off kernels.
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,
-                          float* mod_out, float* cvec_out, hipStream_t stream);
+                          float* mod_out, float* cvec_out, float* gate_out, hipStream_t stream);
 hipError_t enqueue_install_prefix(const Dims& d, const void* k, const void* v, int batch, int prefix_len,
                                   void* kc, void* vt, size_t elem_bytes, hipStream_t stream);
 hipError_t enqueue_quantize_int4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
   if constexpr (EPI == EPI_RESID) {
     const int col = nrow[0] + r16;
     epi_c0 = g.scale_next[col];
+    epi_c1 = g.gate ? g.gate[col] : 1.f;   // residual gate (1: plain residual, exact)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(mt * 16 + grp * 4 + i, d.M - 1);
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
       const int m = mt * 16 + grp * 4 + i;
       float hn = 0.f;
       if (m < d.M) {
-        hn = epi_h[i] + tot[0][i];
+        hn = epi_h[i] + epi_c1 * tot[0][i];
         bf.h[(size_t)m * d.D + col] = hn;
         hs[sw_idx(m, col, d.D)] = to_elem<AT>(hn * sc1);
       }
@@ -1467,6 +1468,7 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       g.W = static_cast<const char*>(b.w_o) + wbytes_row<WT>(qd) * d.D * l;
       g.Ws = b.s_o ? b.s_o + (size_t)l * d.D * (qd / 128) : nullptr;
       g.S = p.s_o; g.scale_next = b.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D;
+      g.gate = b.gate ? b.gate + ((size_t)k * d.nmod + 2 * l) * d.D : nullptr;  // attention block of layer l
       if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
       return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
     case 3:
@@ -1483,6 +1485,7 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       g.S = p.s_d;
       const int jn = (l + 1 < d.L) ? 2 * (l + 1) : 2 * d.L;
       g.scale_next = b.mod + (((size_t)k * d.nmod + jn) * 2) * d.D;
+      g.gate = b.gate ? b.gate + ((size_t)k * d.nmod + 2 * l + 1) * d.D : nullptr;  // MLP block of layer l
       if (d.M > 64) return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
       return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
     }

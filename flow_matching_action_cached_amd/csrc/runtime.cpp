@@ -155,7 +155,8 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   const phyai_config& g = *cfg;
   if (g.n_layers < 1 || g.width < 1 || g.n_q_heads < 1 || g.n_kv_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 ||
       g.action_dim < 1 || g.chunk_len < 1 || g.max_prefix_len < 1 || g.max_batch < 1 || !(g.rms_eps > 0.f) ||
-      !(g.rope_theta == 0.f || (g.rope_theta > 1.f && g.rope_theta < 1e30f)))
+      !(g.rope_theta == 0.f || (g.rope_theta > 1.f && g.rope_theta < 1e30f)) ||
+      (g.gated_residual != 0 && g.gated_residual != 1))
     return PHYAI_ERR_INVALID_ARG;
   if (g.weight_dtype != PHYAI_F32 && g.weight_dtype != PHYAI_BF16 && g.weight_dtype != PHYAI_INT4_G128)
     return PHYAI_ERR_INVALID_ARG;
@@ -198,13 +199,15 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   d.Cl = 0;
   d.gamma = 0.f;
   d.rope_theta = g.rope_theta;
+  d.gated = g.gated_residual;
 
   const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
   Layout lay;
   const size_t o_w_in = lay.take((size_t)D * A * c->es_io), o_b_in = lay.take((size_t)D * c->es_io);
   const size_t o_w_out = lay.take((size_t)A * D * c->es_io), o_b_out = lay.take((size_t)A * c->es_io);
-  const size_t o_w_mod = lay.take((size_t)d.nmod * 2 * D * D * c->es_io);
-  const size_t o_b_mod = lay.take((size_t)d.nmod * 2 * D * c->es_io);
+  const int R = d.gated ? 3 : 2;  // modulation rows per norm: scale, shift (, residual gate)
+  const size_t o_w_mod = lay.take((size_t)d.nmod * R * D * D * c->es_io);
+  const size_t o_b_mod = lay.take((size_t)d.nmod * R * D * c->es_io);
   const size_t o_w_qkv = lay.take(wrow_bytes(c->wt, D) * d.qkv * L);
   const size_t o_w_o = lay.take(wrow_bytes(c->wt, qd) * D * L);
   const size_t o_w_gu = lay.take(wrow_bytes(c->wt, D) * 2 * F * L);
@@ -297,8 +300,9 @@ phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
   HIPCHK(c, cp(c->b.b_in, w->b_in, (size_t)D * e));
   HIPCHK(c, cp(c->b.w_out, w->w_out, (size_t)A * D * e));
   HIPCHK(c, cp(c->b.b_out, w->b_out, (size_t)A * e));
-  HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * 2 * D * D * e));
-  HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * 2 * D * e));
+  const int R = d.gated ? 3 : 2;
+  HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * R * D * D * e));
+  HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * R * D * e));
   // expert linears: re-laid out into the fragment-native (swizzled) layout the kernels stream
   if (c->wt != W_INT4) {
     auto sw = [&](const void* dst, const void* src, int64_t rows, int cols) {
@@ -365,8 +369,9 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
     if (c->tab) hipFree(c->tab);
     c->tab = nullptr;
     c->tab_cap = 0;
+    const size_t gate_f = d.gated ? (size_t)n_steps * d.ntab * d.nmod * d.D : 0;
     const size_t bytes = align256(mod_f * 4) + align256(cv_f * 4) + align256((size_t)n_steps * 4) * 2 +
-                         align256((size_t)n_steps * d.D * 8);
+                         align256((size_t)n_steps * d.D * 8) + align256(gate_f * 4);
     if (hipMalloc(&c->tab, bytes) != hipSuccess) return fail(c, PHYAI_ERR_OOM, "set_timestep_tables: hipMalloc");
     c->tab_cap = n_steps;
   }
@@ -382,6 +387,8 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   c->t_dev = reinterpret_cast<float*>(p);
   p += align256((size_t)cap * 4);
   c->e_dev = reinterpret_cast<double*>(p);
+  p += align256((size_t)cap * d.D * 8);
+  float* gate = d.gated ? reinterpret_cast<float*>(p) : nullptr;  // [cap][ntab][nmod][D]
   // step sizes dt_k = t_{k+1} - t_k with t_N = 0
   std::vector<float> dth(n_steps);
   for (int i = 0; i < n_steps; ++i) {
@@ -391,12 +398,13 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   HIPCHK(c, hipMemcpyAsync(c->t_dev, t_host, (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
   HIPCHK(c, hipMemcpyAsync(dt, dth.data(), (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
   c->b.mod = mod;
+  c->b.gate = gate;
   c->b.cvec = cvec;
   c->b.dt = dt;
   c->b.cv_stride = cv_stride;
   c->b.cv_gu_off = d.L * d.qkv;
   c->b.cv_out_off = d.L * d.qkv + d.L * 2 * d.F;
-  HIPCHK(c, enqueue_tables(d, c->b, c->wt, c->t_dev, c->e_dev, mod, cvec, c->stream));
+  HIPCHK(c, enqueue_tables(d, c->b, c->wt, c->t_dev, c->e_dev, mod, cvec, gate, c->stream));
   // host buffers above must outlive the async copies
   HIPCHK(c, hipStreamSynchronize(c->stream));
   c->n_steps = n_steps;
@@ -537,6 +545,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   d.Cl = g.latent_dim;
   d.gamma = 0.f;
   d.rope_theta = 0.f;
+  d.gated = 0;
   // mirror into cfg the fields the shared calls read
   c->cfg.n_layers = g.n_layers; c->cfg.width = g.width; c->cfg.n_q_heads = g.n_heads; c->cfg.n_kv_heads = g.n_heads;
   c->cfg.head_dim = g.head_dim; c->cfg.mlp_dim = g.mlp_dim; c->cfg.action_dim = g.action_dim;

@@ -48,17 +48,19 @@ __global__ void k_embed(const float* t, int N, int D, double* e) {
   e[idx] = c < half ? sin(ang) : cos(ang);
 }
 
-// One wave per (table tb, row o of W_mod[j]) (j = norm, o in [0, 2D)):
+// One wave per (table tb, row o of W_mod[j]) (j = norm, o in [0, R D): scale, shift and,
+// with R = 3, the residual gate):
 // m_k = W_mod[j][o] . (e(t_k) + cond_tb) + b_mod[j][o] for every step k, accumulated in fp64.
 // cond (io [ntab][D]) may be null (no condition: a single table).
 template <class IOT>
 __global__ __launch_bounds__(256) void k_modulation(const IOT* w_mod, const IOT* b_mod, const IOT* cond,
-                                                    const double* e, int N, int nmod, int D, int ntab, float* mod) {
+                                                    const double* e, int N, int nmod, int D, int ntab, int R,
+                                                    float* mod, float* gate) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= ntab * nmod * 2 * D) return;
-  const int tb = row / (nmod * 2 * D), wrow = row % (nmod * 2 * D);
-  const int j = wrow / (2 * D), o = wrow % (2 * D);
+  if (row >= ntab * nmod * R * D) return;
+  const int tb = row / (nmod * R * D), wrow = row % (nmod * R * D);
+  const int j = wrow / (R * D), o = wrow % (R * D);
   const IOT* wr = w_mod + (size_t)wrow * D;
   const double bias = (double)to_f32(b_mod[wrow]);
   for (int k0 = 0; k0 < N; k0 += 8) {
@@ -73,8 +75,12 @@ __global__ __launch_bounds__(256) void k_modulation(const IOT* w_mod, const IOT*
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const double v = wave_sum(acc[kk]);
-      if (lane == 0 && k0 + kk < N)
-        mod[((((size_t)(k0 + kk) * ntab + tb) * nmod + j) * 2 + (o >= D ? 1 : 0)) * D + (o % D)] = (float)(v + bias);
+      if (lane == 0 && k0 + kk < N) {
+        if (o < 2 * D)
+          mod[((((size_t)(k0 + kk) * ntab + tb) * nmod + j) * 2 + (o >= D ? 1 : 0)) * D + (o % D)] = (float)(v + bias);
+        else
+          gate[(((size_t)(k0 + kk) * ntab + tb) * nmod + j) * D + (o - 2 * D)] = (float)(v + bias);
+      }
     }
   }
 }
@@ -220,15 +226,17 @@ __global__ void k_swizzle_int4(const uint8_t* src, uint32_t* dst, int64_t rows, 
 // ================================================================== host side
 template <class WT, class IOT>
 static hipError_t tables_impl(const Dims& d, const Bufs& b, const float* t_dev, double* e, float* mod,
-                              float* cvec, hipStream_t st) {
+                              float* cvec, float* gate, hipStream_t st) {
   const int ne = d.N * d.D;
   hipLaunchKernelGGL(k_embed, dim3((ne + 255) / 256), dim3(256), 0, st, t_dev, d.N, d.D, e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int rows = d.ntab * d.nmod * 2 * d.D;
+  const int R = d.gated ? 3 : 2;
+  if (d.gated && !gate) return hipErrorInvalidValue;
+  const int rows = d.ntab * d.nmod * R * d.D;
   hipLaunchKernelGGL((k_modulation<IOT>), dim3((rows + 3) / 4), dim3(256), 0, st, static_cast<const IOT*>(b.w_mod),
                      static_cast<const IOT*>(b.b_mod), static_cast<const IOT*>(b.cond), e, d.N, d.nmod, d.D, d.ntab,
-                     mod);
+                     R, mod, gate);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   // out-projection rows: the expert has A; the joint denoiser has Cl latent + A action rows
@@ -240,11 +248,11 @@ static hipError_t tables_impl(const Dims& d, const Bufs& b, const float* t_dev, 
 }
 
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e,
-                          float* mod, float* cvec, hipStream_t st) {
+                          float* mod, float* cvec, float* gate, hipStream_t st) {
   switch (wt) {
-    case W_F32: return tables_impl<float, float>(d, b, t_dev, e, mod, cvec, st);
-    case W_BF16: return tables_impl<bf16, bf16>(d, b, t_dev, e, mod, cvec, st);
-    case W_INT4: return tables_impl<i4, bf16>(d, b, t_dev, e, mod, cvec, st);
+    case W_F32: return tables_impl<float, float>(d, b, t_dev, e, mod, cvec, gate, st);
+    case W_BF16: return tables_impl<bf16, bf16>(d, b, t_dev, e, mod, cvec, gate, st);
+    case W_INT4: return tables_impl<i4, bf16>(d, b, t_dev, e, mod, cvec, gate, st);
   }
   return hipErrorInvalidValue;
 }

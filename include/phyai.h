@@ -84,6 +84,10 @@ typedef struct {
                                  interleaved pairs (2i, 2i+1) of every head turned by
                                  (P + t) * rope_theta^(-2i/head_dim) (the pages stress positional
                                  precision, PhyAI reading Sec. 2; the convention is a reading) */
+  int gated_residual;         /* 0: plain residual blocks; 1: each norm's modulation map also
+                                 yields a gate g (w_mod [2L+1][3D][D], b_mod [2L+1][3D]: rows
+                                 0..D-1 scale, D..2D-1 shift, 2D..3D-1 gate) and a block's
+                                 output enters the residual as g * output (a reading) */
 } phyai_config;
 
 /* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,
@@ -93,7 +97,9 @@ typedef struct {
  * (w = code * scale), as written by phyai_quantize_int4_g128.
  *   w_in [D][A], b_in [D], w_out [A][D], b_out [A]
  *   w_mod [2L+1][2D][D], b_mod [2L+1][2D]   (rows 0..D-1 scale, D..2D-1 shift; norm j:
- *                                           2l attention norm, 2l+1 MLP norm, 2L final)
+ *                                           2l attention norm, 2l+1 MLP norm, 2L final;
+ *                                           gated_residual: [2L+1][3D][D] and [2L+1][3D],
+ *                                           rows 2D..3D-1 the residual gate)
  *   w_qkv [L][(Hq+2Hkv)*dh][D]  (rows: q heads, then k heads, then v heads)
  *   w_o [L][D][Hq*dh], w_gu [L][2F][D] (rows 0..F-1 gate, F..2F-1 up), w_d [L][D][F] */
 typedef struct {

@@ -65,6 +65,16 @@ def test_tiny_bf16_many_rows_rope():
     assert err <= 2e-2
 
 
+def test_tiny_bf16_many_rows_gated_residual():
+    """Residual gates through the tiled residual epilogue (272 rows, ragged last tile)."""
+    d = dataclasses.replace(TINY_BF16, batch=17, gated_residual=True)
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"tiny bf16 batch 17 gated rel err {err:.3e}")
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("prefix_len", [100, 1200, 2100])
 def test_tiny_bf16_few_rows_key_splits(prefix_len):
     """Batch 1 (16 rows, the few-row kernels) in bf16 with prefixes that give one-, two-

@@ -153,6 +153,19 @@ def test_rope_variant_matches_oracle(cfg, tol):
     assert rel_err(ref, ex.denoise(inp, dataclasses.replace(d, rope_theta=0.0))) > 2 * tol  # the rotation matters
 
 
+@pytest.mark.parametrize("cfg,tol", [("tiny", 1e-4), ("pi05", 2e-2)])
+def test_gated_residual_variant_matches_oracle(cfg, tol):
+    """Residual gates from a third row block of each norm's modulation map, applied in the
+    residual epilogues of the weight-streaming GEMMs, against the oracle."""
+    d = dataclasses.replace({"tiny": TINY, "pi05": PI05}[cfg], gated_residual=True)
+    _say(f"case: gated residual {cfg}")
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"gated {cfg} rel err {err:.3e}")
+    assert err <= tol
+
+
 @pytest.mark.parametrize("prefix_len", [1200, 2100])
 def test_tiny_long_prefix_uses_bounded_splits(prefix_len):
     """Prefixes with more key blocks than the merge width (32 splits): 1200 -> 38 blocks
