@@ -23,7 +23,8 @@ design notes with its reason):
   advances by dt_k = t_{k+1} - t_k with t_N = 0 (uniform schedule: dt = -1/N);
 * sinusoidal embedding with periods log-spaced between 4e-3 and 4.0,
   [sin | cos] halves;
-* one linear map per norm turns the embedding into (scale, shift);
+* one linear map per norm turns the embedding into (scale, shift); optionally
+  (fidelity variant) the embedding first passes a time MLP W2 swish(W1 e + b1) + b2;
 * adaptive RMSNorm  h / sqrt(mean(h^2) + eps) * (1 + scale) + shift, no gain;
 * pre-norm layer: attention block then GeGLU MLP block, both residual; with a
   gated residual (fidelity variant) each norm's map also yields a gate and the
@@ -73,13 +74,25 @@ def timestep_embedding(t: float, width: int) -> np.ndarray:
     return np.concatenate([np.sin(ang), np.cos(ang)])
 
 
-def modulation_tables(t, w_mod, b_mod) -> np.ndarray:
+def swish(z):
+    """swish(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def time_mlp(e, w1, b1, w2, b2):
+    """Time MLP of the fidelity variant: W2 swish(W1 e + b1) + b2 (float64)."""
+    u = swish(np.asarray(w1, F64) @ e + np.asarray(b1, F64))
+    return np.asarray(w2, F64) @ u + np.asarray(b2, F64)
+
+
+def modulation_tables(t, w_mod, b_mod, tmlp=None) -> np.ndarray:
     """Per-step (scale, shift[, gate]) of every adaptive norm: m = W_m[j] e(t_k) + b_m[j].
 
     Returns [N][n_mod][R][D] float64 with R = W_m rows / D (2: scale, shift; 3 with the
     residual gate); index j = 2l (attention norm of layer l), 2l+1 (MLP norm of layer
     l), 2L (final norm).  These are the precomputed timestep/modulation tables of
-    PhyAI reading Sec. 5.1 / 5.5.
+    PhyAI reading Sec. 5.1 / 5.5.  ``tmlp`` = (W1, b1, W2, b2) runs the embedding through
+    the time MLP first.
     """
     w_mod = np.asarray(w_mod, dtype=F64)
     b_mod = np.asarray(b_mod, dtype=F64)
@@ -87,6 +100,8 @@ def modulation_tables(t, w_mod, b_mod) -> np.ndarray:
     out = np.empty((len(t), n_mod, rows // d, d), dtype=F64)
     for k, tk in enumerate(np.asarray(t, dtype=F64)):
         e = timestep_embedding(tk, d)
+        if tmlp is not None:
+            e = time_mlp(e, *tmlp)
         m = np.einsum("jod,d->jo", w_mod, e) + b_mod
         out[k] = m.reshape(n_mod, rows // d, d)
     return out
@@ -224,7 +239,8 @@ def denoise(inputs: dict, dims, t=None, linears: dict | None = None, samples=Non
     if t is None:
         t = schedule(dims.n_steps)
     p = as_f64_params(inputs, linears)
-    tables = modulation_tables(t, inputs["w_mod"], inputs["b_mod"])
+    tmlp = tuple(inputs[k] for k in ("w_tm1", "b_tm1", "w_tm2", "b_tm2")) if getattr(dims, "time_mlp", False) else None
+    tables = modulation_tables(t, inputs["w_mod"], inputs["b_mod"], tmlp)
     noise = np.asarray(inputs["noise"], dtype=F64)
     if samples is None:
         samples = range(noise.shape[0])

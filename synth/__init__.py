@@ -39,6 +39,7 @@ TENSOR_IDS = {
     "w_in": 1, "b_in": 2, "w_out": 3, "b_out": 4, "w_mod": 5, "b_mod": 6,
     "w_qkv": 7, "w_o": 8, "w_gu": 9, "w_d": 10,
     "k_pre": 11, "v_pre": 12, "noise": 13,
+    "w_tm1": 14, "b_tm1": 15, "w_tm2": 16, "b_tm2": 17,
     # prefix network used by the cached-vs-recomputed check
     "p_tokens": 20, "p_w_qkv": 21, "p_w_o": 22, "p_w_gu": 23, "p_w_d": 24,
     # joint video/action (WAM) variant
@@ -67,6 +68,7 @@ class ExpertDims:
     weight_std: float = 0.02
     rope_theta: float = 0.0    # > 0: rotary embedding of the chunk's Q/K at positions P + t
     gated_residual: bool = False  # each norm's map also yields a residual gate (3 D rows)
+    time_mlp: bool = False     # the timestep embedding passes W2 swish(W1 e + b1) + b2 first
 
     @property
     def n_mod(self) -> int:    # one (scale, shift) pair per norm: 2 per layer + final
@@ -116,6 +118,7 @@ def expert_param_shapes(d: ExpertDims) -> dict:
         "b_mod": (d.n_mod, (3 if getattr(d, "gated_residual", False) else 2) * D),
         "w_qkv": (L, d.qkv_dim, D), "w_o": (L, D, d.n_q_heads * d.head_dim),
         "w_gu": (L, 2 * F, D), "w_d": (L, D, F),
+        **({"w_tm1": (D, D), "b_tm1": (D,), "w_tm2": (D, D), "b_tm2": (D,)} if getattr(d, "time_mlp", False) else {}),
     }
 
 

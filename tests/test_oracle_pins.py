@@ -465,3 +465,34 @@ def test_gated_residual_with_zero_gates_drops_every_block():
     none["k_pre"] = inp["k_pre"][:, :0]
     none["v_pre"] = inp["v_pre"][:, :0]
     np.testing.assert_allclose(ex.denoise(inp, dg), ex.denoise(none, d0), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- time MLP
+# Fidelity variant: the timestep embedding passes W2 swish(W1 e + b1) + b2 before the
+# modulation maps (a reading; the pages only name the timestep/modulation tables).
+
+def test_time_mlp_identity_weights_give_swish_of_the_embedding():
+    """W1 = W2 = I, zero biases: e' = swish(e) = e * expit(e) (scipy's logistic function)."""
+    from scipy.special import expit
+    D = 16
+    e = ex.timestep_embedding(0.37, D)
+    got = ex.time_mlp(e, np.eye(D), np.zeros(D), np.eye(D), np.zeros(D))
+    np.testing.assert_allclose(got, e * expit(e), rtol=1e-15, atol=0)
+    assert ex.swish(np.array([0.0]))[0] == 0.0
+
+
+def test_time_mlp_wiring():
+    """W2 = 0: e' = b2 for every t, so all steps share one table; b2 = 0 as well leaves only
+    b_mod.  With drawn weights the tables differ from the plain map."""
+    d = dataclasses.replace(synth.CONFIGS["tiny"], time_mlp=True)
+    inp = synth.make_expert_inputs(d, 0)
+    t = ex.schedule(d.n_steps)
+    tm = (inp["w_tm1"], inp["b_tm1"], np.zeros_like(inp["w_tm2"]), inp["b_tm2"])
+    tab = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"], tm)
+    for k in range(1, d.n_steps):
+        np.testing.assert_array_equal(tab[k], tab[0])
+    want = np.einsum("jod,d->jo", np.asarray(inp["w_mod"], np.float64), np.asarray(inp["b_tm2"], np.float64))
+    np.testing.assert_allclose(tab[0].reshape(want.shape), want + inp["b_mod"], rtol=1e-12, atol=1e-14)
+    full = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"], tuple(inp[k] for k in ("w_tm1", "b_tm1", "w_tm2", "b_tm2")))
+    plain = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"])
+    assert np.max(np.abs(full - plain)) > 1e-3
