@@ -45,11 +45,11 @@ class Config(ctypes.Structure):
                 ("action_dim", ctypes.c_int), ("chunk_len", ctypes.c_int), ("max_prefix_len", ctypes.c_int),
                 ("max_batch", ctypes.c_int), ("weight_dtype", ctypes.c_int), ("rms_eps", ctypes.c_float),
                 ("max_arena_bytes", ctypes.c_size_t), ("rope_theta", ctypes.c_float),
-                ("gated_residual", ctypes.c_int)]
+                ("gated_residual", ctypes.c_int), ("time_mlp", ctypes.c_int)]
 
 
 _WFIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d",
-            "s_qkv", "s_o", "s_gu", "s_d")
+            "s_qkv", "s_o", "s_gu", "s_d", "w_tm1", "b_tm1", "w_tm2", "b_tm2")
 
 
 class Weights(ctypes.Structure):
@@ -170,12 +170,12 @@ class ActionExpert(_Context):
 
     def __init__(self, *, n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim,
                  chunk_len, max_prefix_len, max_batch=1, weight_dtype="bf16", rms_eps=1e-6,
-                 max_arena_bytes=0, stream=None, rope_theta=0.0, gated_residual=False):
+                 max_arena_bytes=0, stream=None, rope_theta=0.0, gated_residual=False, time_mlp=False):
         self._lib = load_library()
         self.weight_dtype = weight_dtype
         cfg = Config(n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim, chunk_len,
                      max_prefix_len, max_batch, _DTYPES[weight_dtype], rms_eps, max_arena_bytes, rope_theta,
-                     int(bool(gated_residual)))
+                     int(bool(gated_residual)), int(bool(time_mlp)))
         self.cfg = cfg
         self._stream = stream
         h = ctypes.c_void_p()
@@ -192,7 +192,8 @@ class ActionExpert(_Context):
                    head_dim=d.head_dim, mlp_dim=d.mlp_dim, action_dim=d.action_dim, chunk_len=d.chunk_len,
                    max_prefix_len=kw.pop("max_prefix_len", d.prefix_len), max_batch=kw.pop("max_batch", d.batch),
                    weight_dtype=d.weight_dtype, rms_eps=d.rms_eps, rope_theta=getattr(d, "rope_theta", 0.0),
-                   gated_residual=getattr(d, "gated_residual", False), **kw)
+                   gated_residual=getattr(d, "gated_residual", False), time_mlp=getattr(d, "time_mlp", False),
+                   **kw)
 
     def set_weights(self, w: dict):
         """w: dict of contiguous cuda tensors named as in phyai_weights."""

@@ -25,6 +25,7 @@ struct Dims {
   float gamma;                     // joint denoiser: guidance scale
   float rope_theta;                // > 0: rotary embedding of the chunk's Q/K at positions P + t
   int gated;                       // 1: each norm's map also yields a residual gate (3 D rows per norm)
+  int tmlp;                        // 1: the timestep embedding passes the time MLP first
 };
 
 // Device pointers of one context.  Element types depend on the weight dtype:
@@ -34,6 +35,7 @@ struct Bufs {
   const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;  // io (joint denoiser: latent projections)
   const void *w_in2, *b_in2, *w_out2, *b_out2;              // joint denoiser: action projections
   const void* cond;                                         // [ntab][D] io: added to the embedding
+  const void *w_tm1, *b_tm1, *w_tm2, *b_tm2;                // time MLP (io [D][D], [D]; tmlp only)
   const void *w_qkv, *w_o, *w_gu, *w_d;                     // expert linears
   const uint16_t *s_qkv, *s_o, *s_gu, *s_d;                 // int4 scales (bf16 bits)
   void *kc, *vt;          // K cache [Bmax][L][Hkv][KS][dh], V^T cache [Bmax][L][Hkv][dh][KS] (act)
@@ -76,7 +78,7 @@ hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipS
 hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
                            hipStream_t stream);
 
-// One-off kernels.
+// One-off kernels.  With Dims::tmlp, e_scratch holds 3 N D doubles (embedding, hidden, MLP output).
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,
                           float* mod_out, float* cvec_out, float* gate_out, hipStream_t stream);
 hipError_t enqueue_install_prefix(const Dims& d, const void* k, const void* v, int batch, int prefix_len,

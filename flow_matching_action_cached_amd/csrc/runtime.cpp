@@ -156,7 +156,7 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   if (g.n_layers < 1 || g.width < 1 || g.n_q_heads < 1 || g.n_kv_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 ||
       g.action_dim < 1 || g.chunk_len < 1 || g.max_prefix_len < 1 || g.max_batch < 1 || !(g.rms_eps > 0.f) ||
       !(g.rope_theta == 0.f || (g.rope_theta > 1.f && g.rope_theta < 1e30f)) ||
-      (g.gated_residual != 0 && g.gated_residual != 1))
+      (g.gated_residual != 0 && g.gated_residual != 1) || (g.time_mlp != 0 && g.time_mlp != 1))
     return PHYAI_ERR_INVALID_ARG;
   if (g.weight_dtype != PHYAI_F32 && g.weight_dtype != PHYAI_BF16 && g.weight_dtype != PHYAI_INT4_G128)
     return PHYAI_ERR_INVALID_ARG;
@@ -200,6 +200,7 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   d.gamma = 0.f;
   d.rope_theta = g.rope_theta;
   d.gated = g.gated_residual;
+  d.tmlp = g.time_mlp;
 
   const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
   Layout lay;
@@ -212,6 +213,8 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   const size_t o_w_o = lay.take(wrow_bytes(c->wt, qd) * D * L);
   const size_t o_w_gu = lay.take(wrow_bytes(c->wt, D) * 2 * F * L);
   const size_t o_w_d = lay.take(wrow_bytes(c->wt, F) * D * L);
+  const size_t tm_w = d.tmlp ? (size_t)D * D * c->es_io : 0, tm_b = d.tmlp ? (size_t)D * c->es_io : 0;
+  const size_t o_w_tm1 = lay.take(tm_w), o_b_tm1 = lay.take(tm_b), o_w_tm2 = lay.take(tm_w), o_b_tm2 = lay.take(tm_b);
   size_t o_s_qkv = 0, o_s_o = 0, o_s_gu = 0, o_s_d = 0;
   if (c->wt == W_INT4) {
     o_s_qkv = lay.take((size_t)d.qkv * (D / 128) * 2 * L);
@@ -254,6 +257,9 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   b.w_in = base + o_w_in; b.b_in = base + o_b_in; b.w_out = base + o_w_out; b.b_out = base + o_b_out;
   b.w_mod = base + o_w_mod; b.b_mod = base + o_b_mod;
   b.w_qkv = base + o_w_qkv; b.w_o = base + o_w_o; b.w_gu = base + o_w_gu; b.w_d = base + o_w_d;
+  if (d.tmlp) {
+    b.w_tm1 = base + o_w_tm1; b.b_tm1 = base + o_b_tm1; b.w_tm2 = base + o_w_tm2; b.b_tm2 = base + o_b_tm2;
+  }
   if (c->wt == W_INT4) {
     b.s_qkv = reinterpret_cast<uint16_t*>(base + o_s_qkv);
     b.s_o = reinterpret_cast<uint16_t*>(base + o_s_o);
@@ -290,6 +296,8 @@ phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
     return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: null weight pointer");
   if (c->wt == W_INT4 && (!w->s_qkv || !w->s_o || !w->s_gu || !w->s_d))
     return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: int4 weights need the four scale arrays");
+  if (c->base.tmlp && (!w->w_tm1 || !w->b_tm1 || !w->w_tm2 || !w->b_tm2))
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_weights: the time MLP needs w_tm1, b_tm1, w_tm2 and b_tm2");
   const Dims& d = c->base;
   const int L = d.L, D = d.D, F = d.F, A = d.A, qd = d.Hq * d.dh;
   const size_t e = c->es_io;
@@ -303,6 +311,12 @@ phyai_status phyai_set_weights(phyai_ctx* c, const phyai_weights* w) {
   const int R = d.gated ? 3 : 2;
   HIPCHK(c, cp(c->b.w_mod, w->w_mod, (size_t)d.nmod * R * D * D * e));
   HIPCHK(c, cp(c->b.b_mod, w->b_mod, (size_t)d.nmod * R * D * e));
+  if (d.tmlp) {
+    HIPCHK(c, cp(c->b.w_tm1, w->w_tm1, (size_t)D * D * e));
+    HIPCHK(c, cp(c->b.b_tm1, w->b_tm1, (size_t)D * e));
+    HIPCHK(c, cp(c->b.w_tm2, w->w_tm2, (size_t)D * D * e));
+    HIPCHK(c, cp(c->b.b_tm2, w->b_tm2, (size_t)D * e));
+  }
   // expert linears: re-laid out into the fragment-native (swizzled) layout the kernels stream
   if (c->wt != W_INT4) {
     auto sw = [&](const void* dst, const void* src, int64_t rows, int cols) {
@@ -370,8 +384,9 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
     c->tab = nullptr;
     c->tab_cap = 0;
     const size_t gate_f = d.gated ? (size_t)n_steps * d.ntab * d.nmod * d.D : 0;
+    const size_t e_f = (size_t)n_steps * d.D * (d.tmlp ? 3 : 1);  // embedding (+ time-MLP hidden, output)
     const size_t bytes = align256(mod_f * 4) + align256(cv_f * 4) + align256((size_t)n_steps * 4) * 2 +
-                         align256((size_t)n_steps * d.D * 8) + align256(gate_f * 4);
+                         align256(e_f * 8) + align256(gate_f * 4);
     if (hipMalloc(&c->tab, bytes) != hipSuccess) return fail(c, PHYAI_ERR_OOM, "set_timestep_tables: hipMalloc");
     c->tab_cap = n_steps;
   }
@@ -387,7 +402,7 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   c->t_dev = reinterpret_cast<float*>(p);
   p += align256((size_t)cap * 4);
   c->e_dev = reinterpret_cast<double*>(p);
-  p += align256((size_t)cap * d.D * 8);
+  p += align256((size_t)cap * d.D * (d.tmlp ? 3 : 1) * 8);
   float* gate = d.gated ? reinterpret_cast<float*>(p) : nullptr;  // [cap][ntab][nmod][D]
   // step sizes dt_k = t_{k+1} - t_k with t_N = 0
   std::vector<float> dth(n_steps);
@@ -546,6 +561,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   d.gamma = 0.f;
   d.rope_theta = 0.f;
   d.gated = 0;
+  d.tmlp = 0;
   // mirror into cfg the fields the shared calls read
   c->cfg.n_layers = g.n_layers; c->cfg.width = g.width; c->cfg.n_q_heads = g.n_heads; c->cfg.n_kv_heads = g.n_heads;
   c->cfg.head_dim = g.head_dim; c->cfg.mlp_dim = g.mlp_dim; c->cfg.action_dim = g.action_dim;

@@ -48,6 +48,33 @@ __global__ void k_embed(const float* t, int N, int D, double* e) {
   e[idx] = c < half ? sin(ang) : cos(ang);
 }
 
+// Time MLP layer (fidelity variant): out[k][o] = act(W[o] . in[k] + b[o]) for every step k,
+// accumulated in fp64; act = swish (z / (1 + exp(-z))) for the first layer, identity for the
+// second.  One wave per output row o.
+template <class IOT>
+__global__ __launch_bounds__(256) void k_time_mlp(const IOT* w, const IOT* bias, const double* in, int N, int D,
+                                                  int swish, double* out) {
+  const int lane = threadIdx.x & 63;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (o >= D) return;
+  const IOT* wr = w + (size_t)o * D;
+  const double b = (double)to_f32(bias[o]);
+  for (int k0 = 0; k0 < N; k0 += 8) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = lane; c < D; c += 64) {
+      const double wv = (double)to_f32(wr[c]);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        if (k0 + kk < N) acc[kk] += wv * in[(size_t)(k0 + kk) * D + c];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const double v = wave_sum(acc[kk]) + b;
+      if (lane == 0 && k0 + kk < N) out[(size_t)(k0 + kk) * D + o] = swish ? v / (1.0 + exp(-v)) : v;
+    }
+  }
+}
+
 // One wave per (table tb, row o of W_mod[j]) (j = norm, o in [0, R D): scale, shift and,
 // with R = 3, the residual gate):
 // m_k = W_mod[j][o] . (e(t_k) + cond_tb) + b_mod[j][o] for every step k, accumulated in fp64.
@@ -231,6 +258,18 @@ static hipError_t tables_impl(const Dims& d, const Bufs& b, const float* t_dev, 
   hipLaunchKernelGGL(k_embed, dim3((ne + 255) / 256), dim3(256), 0, st, t_dev, d.N, d.D, e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (d.tmlp) {  // e -> swish(W1 e + b1) -> W2 (.) + b2, in the scratch after e
+    const double* e0 = e;
+    double* e1 = e + (size_t)d.N * d.D;
+    double* e2 = e1 + (size_t)d.N * d.D;
+    hipLaunchKernelGGL((k_time_mlp<IOT>), dim3((d.D + 3) / 4), dim3(256), 0, st, static_cast<const IOT*>(b.w_tm1),
+                       static_cast<const IOT*>(b.b_tm1), e0, d.N, d.D, 1, e1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_time_mlp<IOT>), dim3((d.D + 3) / 4), dim3(256), 0, st, static_cast<const IOT*>(b.w_tm2),
+                       static_cast<const IOT*>(b.b_tm2), e1, d.N, d.D, 0, e2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    e = e2;
+  }
   const int R = d.gated ? 3 : 2;
   if (d.gated && !gate) return hipErrorInvalidValue;
   const int rows = d.ntab * d.nmod * R * d.D;

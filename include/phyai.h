@@ -88,6 +88,9 @@ typedef struct {
                                  yields a gate g (w_mod [2L+1][3D][D], b_mod [2L+1][3D]: rows
                                  0..D-1 scale, D..2D-1 shift, 2D..3D-1 gate) and a block's
                                  output enters the residual as g * output (a reading) */
+  int time_mlp;               /* 0: the modulation maps read the timestep embedding e(t); 1: they
+                                 read W_tm2 swish(W_tm1 e + b_tm1) + b_tm2 (phyai_weights w_tm*,
+                                 swish(z) = z / (1 + exp(-z)); a reading) */
 } phyai_config;
 
 /* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,
@@ -106,6 +109,7 @@ typedef struct {
   const void *w_in, *b_in, *w_out, *b_out, *w_mod, *b_mod;
   const void *w_qkv, *w_o, *w_gu, *w_d;
   const void *s_qkv, *s_o, *s_gu, *s_d;
+  const void *w_tm1, *b_tm1, *w_tm2, *b_tm2;   /* time_mlp only: [D][D], [D], [D][D], [D] (io type) */
 } phyai_weights;
 
 /* Create a context on the current HIP device.  hip_stream: the hipStream_t every

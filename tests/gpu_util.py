@@ -22,7 +22,7 @@ def device_inputs(d, inputs):
     import flow_matching_action_cached_amd as fm
     el = torch_dtype(d)
     out = {}
-    for k in WEIGHT_KEYS:
+    for k in WEIGHT_KEYS + tuple(k for k in ("w_tm1", "b_tm1", "w_tm2", "b_tm2") if k in inputs):
         a = torch.from_numpy(np.ascontiguousarray(inputs[k])).cuda()
         if d.weight_dtype == "int4" and k in LINEARS:
             packed, scales = fm.quantize_int4_g128(a)
@@ -40,7 +40,7 @@ def make_expert(d, dev, t, graph=True, **kw):
     import flow_matching_action_cached_amd as fm
     ex = fm.ActionExpert.from_dims(d, **kw)
     w = {k: dev[k] for k in WEIGHT_KEYS}
-    for k in ("s_qkv", "s_o", "s_gu", "s_d"):
+    for k in ("s_qkv", "s_o", "s_gu", "s_d", "w_tm1", "b_tm1", "w_tm2", "b_tm2"):
         if k in dev:
             w[k] = dev[k]
     ex.set_weights(w)

@@ -73,6 +73,7 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(rope_theta=-1e4))[0] == 1
     assert _create(lib, _cfg(rope_theta=float("nan")))[0] == 1
     assert _create(lib, _cfg(gated_residual=2))[0] == 1
+    assert _create(lib, _cfg(time_mlp=-1))[0] == 1
     st, h = _create(lib, _cfg(n_layers=0))
     assert h.value is None
 

@@ -166,6 +166,37 @@ def test_gated_residual_variant_matches_oracle(cfg, tol):
     assert err <= tol
 
 
+def test_time_mlp_tables_and_loop_match_oracle():
+    """Time MLP before the modulation maps (tables built on the GPU in fp64): the tables and
+    the whole tiny fp32 loop against the oracle."""
+    d = dataclasses.replace(TINY, time_mlp=True)
+    inp = synth.make_expert_inputs(d, 0)
+    t = ex.schedule(d.n_steps)
+    dev = device_inputs(d, inp)
+    e = make_expert(d, dev, t)
+    got_tab = e.get_modulation().cpu().numpy()
+    got = e.denoise(dev["noise"]).cpu().numpy()
+    e.sync()
+    e.close()
+    tm = tuple(inp[k] for k in ("w_tm1", "b_tm1", "w_tm2", "b_tm2"))
+    ref_tab = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"], tm)
+    np.testing.assert_allclose(got_tab, ref_tab, rtol=0, atol=1e-6 * np.abs(ref_tab).max())
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"time-mlp tiny rel err {err:.3e}")
+    assert err <= 1e-4
+
+
+def test_pi05_fidelity_variants_combined_match_oracle():
+    """RoPE, residual gates and the time MLP together on the pi0.5-shaped bf16 expert."""
+    d = dataclasses.replace(PI05, rope_theta=1e4, gated_residual=True, time_mlp=True)
+    _say("case: pi05 rope + gated + time MLP")
+    inp = synth.make_expert_inputs(d, 0)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"pi05 fidelity variants rel err {err:.3e}")
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("prefix_len", [1200, 2100])
 def test_tiny_long_prefix_uses_bounded_splits(prefix_len):
     """Prefixes with more key blocks than the merge width (32 splits): 1200 -> 38 blocks
