@@ -178,8 +178,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,gated,b32,wam",
-                    help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, b32, wam")
+    ap.add_argument("--variants", default="int4,rope,gated,prefill,b32,wam",
+                    help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, "
+                         "prefill, b32, wam")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -338,6 +339,35 @@ def main():
         variants["gated_residual_batch1"] = {"ms_per_chunk": round(msg, 4), "chunks_per_s": round(1000.0 / msg, 2),
                                              "hbm_frac": round(chunk_bytes(d) / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] gated-residual variant: {msg:.4f} ms/chunk", file=sys.stderr, flush=True)
+
+    if "prefill" in todo:
+        # prefix prefill: the prefix network (the expert's layer with a plain RMSNorm) over the
+        # 816 prefix tokens, writing every layer's K/V into the cache; eager launches
+        pre = synth.make_prefix_inputs(d, 1)
+        ep = fm.ActionExpert.from_dims(d, prefill=True)
+        ep.set_weights(w)
+        ep.set_prefill_weights({k: torch.from_numpy(pre[k]).cuda().to(torch.bfloat16).contiguous()
+                                for k in ("w_qkv", "w_o", "w_gu", "w_d")})
+        tok = torch.from_numpy(pre["tokens"]).cuda().to(torch.bfloat16).contiguous()
+        del pre
+        for _ in range(args.warmup):
+            ep.prefill(tok)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            ep.prefill(tok)
+        b.record()
+        torch.cuda.synchronize()
+        msp = a.elapsed_time(b) / args.steps
+        ep.sync()
+        ep.close()
+        # 2 x rows x params of the four linears, plus QK^T and PV over the prefix keys, per layer
+        rows, per_layer = d.prefix_len, d.qkv_dim * d.width + d.width * d.n_q_heads * d.head_dim + 3 * d.mlp_dim * d.width
+        pf = d.n_layers * (2 * rows * per_layer + 4 * d.n_q_heads * rows * rows * d.head_dim)
+        variants["prefill_816_batch1"] = {"ms_per_prefix": round(msp, 4), "algorithmic_tflop": round(pf / 1e12, 4),
+                                          "mfma_frac": round(pf / (msp * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        print(f"[bench] prefill variant: {msp:.4f} ms per prefix", file=sys.stderr, flush=True)
 
     if "b32" in todo:
         # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs

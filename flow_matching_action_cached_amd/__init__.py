@@ -25,7 +25,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "bad state", 3: "out of memory", 4:
           5: "unsupported"}
 
 EXPORTED = (
-    "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_timestep_tables",
+    "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_prefill_weights", "phyai_prefill",
+    "phyai_set_timestep_tables",
     "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
     "phyai_enqueue_kernel_repeat", "phyai_wam_create", "phyai_wam_set_weights", "phyai_wam_set_conditions",
@@ -45,7 +46,7 @@ class Config(ctypes.Structure):
                 ("action_dim", ctypes.c_int), ("chunk_len", ctypes.c_int), ("max_prefix_len", ctypes.c_int),
                 ("max_batch", ctypes.c_int), ("weight_dtype", ctypes.c_int), ("rms_eps", ctypes.c_float),
                 ("max_arena_bytes", ctypes.c_size_t), ("rope_theta", ctypes.c_float),
-                ("gated_residual", ctypes.c_int), ("time_mlp", ctypes.c_int)]
+                ("gated_residual", ctypes.c_int), ("time_mlp", ctypes.c_int), ("prefill", ctypes.c_int)]
 
 
 _WFIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", "w_gu", "w_d",
@@ -54,6 +55,10 @@ _WFIELDS = ("w_in", "b_in", "w_out", "b_out", "w_mod", "b_mod", "w_qkv", "w_o", 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WFIELDS]
+
+
+class PrefillWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_qkv", "w_o", "w_gu", "w_d")]
 
 
 class WamConfig(ctypes.Structure):
@@ -86,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_create.argtypes = [ctypes.POINTER(Config), vp, ctypes.POINTER(vp)]
     lib.phyai_set_weights.argtypes = [vp, ctypes.POINTER(Weights)]
     lib.phyai_set_prefix_kv.argtypes = [vp, vp, vp, ci, ci]
+    lib.phyai_set_prefill_weights.argtypes = [vp, ctypes.POINTER(PrefillWeights)]
+    lib.phyai_prefill.argtypes = [vp, vp, ci, ci]
     lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
     lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
     lib.phyai_set_graph_mode.argtypes = [vp, ci]
@@ -170,12 +177,13 @@ class ActionExpert(_Context):
 
     def __init__(self, *, n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim,
                  chunk_len, max_prefix_len, max_batch=1, weight_dtype="bf16", rms_eps=1e-6,
-                 max_arena_bytes=0, stream=None, rope_theta=0.0, gated_residual=False, time_mlp=False):
+                 max_arena_bytes=0, stream=None, rope_theta=0.0, gated_residual=False, time_mlp=False,
+                 prefill=False):
         self._lib = load_library()
         self.weight_dtype = weight_dtype
         cfg = Config(n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim, action_dim, chunk_len,
                      max_prefix_len, max_batch, _DTYPES[weight_dtype], rms_eps, max_arena_bytes, rope_theta,
-                     int(bool(gated_residual)), int(bool(time_mlp)))
+                     int(bool(gated_residual)), int(bool(time_mlp)), int(bool(prefill)))
         self.cfg = cfg
         self._stream = stream
         h = ctypes.c_void_p()
@@ -203,6 +211,18 @@ class ActionExpert(_Context):
         ws = Weights(*[_ptr(w.get(n)) for n in _WFIELDS])
         self._check(self._lib.phyai_set_weights(self._h, ctypes.byref(ws)))
         self.sync()
+
+    def set_prefill_weights(self, w: dict):
+        """w: dict of contiguous cuda tensors w_qkv, w_o, w_gu, w_d of the prefix network."""
+        ws = PrefillWeights(*[_ptr(w.get(n)) for n in ("w_qkv", "w_o", "w_gu", "w_d")])
+        self._check(self._lib.phyai_set_prefill_weights(self._h, ctypes.byref(ws)))
+
+    def prefill(self, tokens):
+        """tokens: cuda [B][P][width] in the weight element type; computes and installs the
+        prefix K/V (asynchronous on the stream)."""
+        assert tokens.is_contiguous() and tokens.dim() == 3
+        self._check(self._lib.phyai_prefill(self._h, _ptr(tokens), int(tokens.shape[0]), int(tokens.shape[1])))
+        self._batch = int(tokens.shape[0])
 
     def set_prefix_kv(self, k, v):
         """k, v: cuda [B][L][P][Hkv][dh] in the weight element type."""

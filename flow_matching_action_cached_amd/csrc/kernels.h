@@ -73,6 +73,14 @@ hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype w
 hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, int which, int k, int l,
                        hipStream_t stream);
 
+// Prefix prefill: the dims of running the layer stack over batch x prefix_len prefix rows with
+// no cached keys (their K/V land in cache rows [0, prefix_len) of every layer), and the
+// enqueue of the whole prefill on `stream`: input kernel, then the layers' launches.  b holds
+// the prefix network's linears and zero modulation tables (plain RMSNorm).
+Dims prefill_dims(const Dims& base, int batch, int prefix_len);
+hipError_t enqueue_prefill(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, const void* tokens,
+                           hipStream_t stream);
+
 // Joint video/action denoiser (bf16): whole guided loop, and one launch of a loop kernel.
 hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipStream_t stream);
 hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,

@@ -1510,6 +1510,57 @@ static hipError_t denoise_impl(const Dims& d, const Bufs& b, const Plan& p, hipS
   return e;
 }
 
+// ------------------------------------------------------------------ prefix prefill
+// The prefix rows enter the layer stack as given (no in-projection): h = tokens, hs = h (the
+// prefix network's norm is a plain RMSNorm: zero scale and shift) and the row statistics.
+// One workgroup per token row.
+template <class AT, class IOT>
+__global__ __launch_bounds__(256) void k_prefill_in(Dims d, Bufs bf, const IOT* tokens) {
+  const int m = blockIdx.x, tid = threadIdx.x;
+  AT* hs = static_cast<AT*>(bf.hs);
+  for (int n0 = 0; n0 < d.D; n0 += 256) {
+    const int n = n0 + tid;  // D % 256 == 0: every thread has a column
+    const float v = to_f32(tokens[(size_t)m * d.D + n]);
+    bf.h[(size_t)m * d.D + n] = v;
+    hs[sw_idx(m, n, d.D)] = to_elem<AT>(v);
+    const float sq = sum16(v * v);
+    if ((tid & 15) == 0) bf.ssq[(size_t)m * (d.D / 16) + n / 16] = sq;
+  }
+}
+
+Dims prefill_dims(const Dims& base, int batch, int prefix_len) {
+  Dims d = base;
+  d.B = batch;
+  d.H = prefix_len;           // the prefix rows take the place of the chunk ...
+  d.P = 0;                    // ... with no cached keys before them
+  d.M = batch * prefix_len;
+  d.Mst = d.M;
+  d.N = 1;
+  d.rope_theta = 0.f;         // the prefix network: plain layers (its K/V are stored as computed)
+  d.gated = 0;
+  d.tmlp = 0;
+  return d;
+}
+
+template <class AT>
+static hipError_t prefill_impl(const Dims& d, const Bufs& b, const Plan& p, const void* tokens, hipStream_t st) {
+  hipLaunchKernelGGL((k_prefill_in<AT, AT>), dim3(d.M), dim3(256), 0, st, d, b, static_cast<const AT*>(tokens));
+  hipError_t e = hipGetLastError();
+  // every layer's QKV epilogue writes the prefix rows' K/V into cache rows [0, prefix_len)
+  for (int l = 0; l < d.L && e == hipSuccess; ++l)
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = launch_one<AT, AT, AT>(d, b, p, kLayerOrder[i], 0, l, st);
+  return e;
+}
+
+hipError_t enqueue_prefill(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, const void* tokens,
+                           hipStream_t st) {
+  switch (wt) {
+    case W_F32: return prefill_impl<float>(d, b, p, tokens, st);
+    case W_BF16: return prefill_impl<bf16>(d, b, p, tokens, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t enqueue_one(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, int which, int k, int l,
                        hipStream_t st) {
   switch (wt) {

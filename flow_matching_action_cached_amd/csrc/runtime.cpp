@@ -27,6 +27,9 @@ struct phyai_ctx {
   std::string err;
   WDtype wt = W_F32;
   size_t es_io = 4, es_act = 4;      // element bytes of io weights / GEMM activations
+  // prefix prefill (config prefill): the prefix network's linears and zero modulation tables
+  bool prefill = false, have_prefill_weights = false;
+  Bufs bp{};                          // c->b with the prefix network's linears and zero tables
 
   void* arena = nullptr;
   size_t arena_bytes = 0;
@@ -169,8 +172,16 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
       (g.weight_dtype != PHYAI_BF16 || ((g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim) % 128))
     return PHYAI_ERR_UNSUPPORTED;
   if (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) return PHYAI_ERR_UNSUPPORTED;
+  if (g.prefill != 0 && g.prefill != 1) return PHYAI_ERR_INVALID_ARG;
+  // the prefill runs the loop's kernels over batch x prefix rows: no int4 prefix network, and
+  // more than 64 rows need the bf16 tiled GEMMs
+  if (g.prefill && (g.weight_dtype == PHYAI_INT4_G128 ||
+                    (g.max_prefix_len * g.max_batch > 64 &&
+                     (g.weight_dtype != PHYAI_BF16 || ((g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim) % 128))))
+    return PHYAI_ERR_UNSUPPORTED;
 
   phyai_ctx* c = new phyai_ctx();
+  c->prefill = g.prefill != 0;
   c->cfg = g;
   c->stream = static_cast<hipStream_t>(hip_stream);
   c->wt = g.weight_dtype == PHYAI_F32 ? W_F32 : g.weight_dtype == PHYAI_BF16 ? W_BF16 : W_INT4;
@@ -225,19 +236,38 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   const size_t kv_elems = (size_t)d.B * L * d.Hkv * d.KS * d.dh;
   const size_t o_kc = lay.take(kv_elems * c->es_act), o_vt = lay.take(kv_elems * c->es_act);
   const size_t zero_begin = o_kc;
-  const size_t o_x = lay.take((size_t)d.M * A * 4), o_h = lay.take((size_t)d.M * D * 4);
-  const size_t o_ssq = lay.take((size_t)(D / 16) * d.Mst * 4);
-  const size_t mpad = (size_t)(d.M + 15) / 16 * 16;  // swizzled activations hold whole 16-row tiles
-  const size_t o_hs = lay.take(mpad * D * c->es_act), o_q = lay.take((size_t)d.M * qd * c->es_act);
+  // the prefill runs the same kernels over batch x prefix rows (no cached keys): its dims
+  Dims dp = prefill_dims(d, g.max_batch, g.max_prefix_len);
+  const size_t rows = c->prefill ? std::max<size_t>(d.M, dp.M) : (size_t)d.M;  // activation rows
+  const size_t o_x = lay.take((size_t)d.M * A * 4), o_h = lay.take(rows * D * 4);
+  const size_t o_ssq = lay.take((size_t)(D / 16) * rows * 4);
+  const size_t mpad = (rows + 15) / 16 * 16;  // swizzled activations hold whole 16-row tiles
+  const size_t o_hs = lay.take(mpad * D * c->es_act), o_q = lay.take(rows * qd * c->es_act);
   const size_t o_o = lay.take(mpad * qd * c->es_act), o_act = lay.take(mpad * F * c->es_act);
   // scratch for split reductions: upper bounds over every batch / prefix length
   const int nblk_max = (d.P + d.H + 31) / 32;
-  const size_t attn_ws = attn_counters(d) * nblk_max * ((size_t)(d.dh / 16) * 256 + 32);
+  size_t attn_ws = attn_counters(d) * nblk_max * ((size_t)(d.dh / 16) * 256 + 32);
+  size_t attn_cnt_n = attn_counters(d);
   Plan pmax = make_plan(d, c->wt);
+  size_t gemm_ws_n = std::max<size_t>(gemm_ws_floats(d, pmax), 1);
+  if (c->prefill) {
+    const int nblk_p = (dp.H + 31) / 32;
+    attn_ws = std::max(attn_ws, attn_counters(dp) * nblk_p * ((size_t)(d.dh / 16) * 256 + 32));
+    attn_cnt_n = std::max(attn_cnt_n, attn_counters(dp));
+    gemm_ws_n = std::max(gemm_ws_n, gemm_ws_floats(dp, make_plan(dp, c->wt)));
+  }
   const size_t o_attn_ws = lay.take(attn_ws * 4);
-  const size_t o_attn_cnt = lay.take(attn_counters(d) * 4);
-  const size_t o_gemm_ws = lay.take(std::max<size_t>(gemm_ws_floats(d, pmax), 1) * 4);
+  const size_t o_attn_cnt = lay.take(attn_cnt_n * 4);
+  const size_t o_gemm_ws = lay.take(gemm_ws_n * 4);
   const size_t o_gemm_cnt = lay.take(gemm_counters(d) * 4);
+  // prefill: the prefix network's four linears (same shapes as the expert's) and zero tables
+  const size_t pw = c->prefill ? 1 : 0;
+  const size_t o_pw_qkv = lay.take(pw * wrow_bytes(c->wt, D) * d.qkv * L);
+  const size_t o_pw_o = lay.take(pw * wrow_bytes(c->wt, qd) * D * L);
+  const size_t o_pw_gu = lay.take(pw * wrow_bytes(c->wt, D) * 2 * F * L);
+  const size_t o_pw_d = lay.take(pw * wrow_bytes(c->wt, F) * D * L);
+  const size_t zcv = (size_t)d.L * d.qkv + (size_t)d.L * 2 * d.F + d.A;
+  const size_t o_zmod = lay.take(pw * (size_t)d.nmod * 2 * D * 4), o_zcv = lay.take(pw * zcv * 4);
   c->arena_bytes = lay.off;
   if (g.max_arena_bytes && c->arena_bytes > g.max_arena_bytes) {
     delete c;
@@ -275,6 +305,17 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   b.attn_cnt = reinterpret_cast<unsigned*>(base + o_attn_cnt);
   b.gemm_ws = reinterpret_cast<float*>(base + o_gemm_ws);
   b.gemm_cnt = reinterpret_cast<unsigned*>(base + o_gemm_cnt);
+  if (c->prefill) {  // prefix network: its own linears, plain RMSNorm (zero scale and shift)
+    c->bp = b;
+    c->bp.w_qkv = base + o_pw_qkv; c->bp.w_o = base + o_pw_o; c->bp.w_gu = base + o_pw_gu;
+    c->bp.w_d = base + o_pw_d;
+    c->bp.mod = reinterpret_cast<const float*>(base + o_zmod);
+    c->bp.cvec = reinterpret_cast<const float*>(base + o_zcv);
+    c->bp.cv_stride = (int)zcv;
+    c->bp.cv_gu_off = d.L * d.qkv;
+    c->bp.cv_out_off = d.L * d.qkv + d.L * 2 * d.F;
+    c->bp.gate = nullptr;
+  }
   // cache (keys past the live rows must read as finite), activations and counters start at 0
   if (hipMemsetAsync(base + zero_begin, 0, c->arena_bytes - zero_begin, c->stream) != hipSuccess ||
       hipStreamSynchronize(c->stream) != hipSuccess) {
@@ -484,6 +525,44 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
     it = c->kgraphs.emplace(key, exec).first;
   }
   HIPCHK(c, hipGraphLaunch(it->second, c->stream));
+  return PHYAI_OK;
+}
+
+phyai_status phyai_set_prefill_weights(phyai_ctx* c, const phyai_prefill_weights* w) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!c->prefill) return fail(c, PHYAI_ERR_BAD_STATE, "set_prefill_weights: context created without prefill");
+  if (!w || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_d)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "set_prefill_weights: null weight pointer");
+  const Dims& d = c->base;
+  const int L = d.L, D = d.D, F = d.F, qd = d.Hq * d.dh;
+  auto sw = [&](const void* dst, const void* src, int64_t rows, int cols) {
+    return enqueue_swizzle(src, const_cast<void*>(dst), rows, cols, c->es_io, c->stream);
+  };
+  HIPCHK(c, sw(c->bp.w_qkv, w->w_qkv, (int64_t)L * d.qkv, D));
+  HIPCHK(c, sw(c->bp.w_o, w->w_o, (int64_t)L * D, qd));
+  HIPCHK(c, sw(c->bp.w_gu, w->w_gu, (int64_t)L * 2 * F, D));
+  HIPCHK(c, sw(c->bp.w_d, w->w_d, (int64_t)L * D, F));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->have_prefill_weights = true;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_prefill(phyai_ctx* c, const void* tokens, int batch, int prefix_len) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (!c->prefill) return fail(c, PHYAI_ERR_BAD_STATE, "prefill: context created without prefill");
+  if (!tokens) return fail(c, PHYAI_ERR_INVALID_ARG, "prefill: null tokens");
+  if (!c->have_prefill_weights) return fail(c, PHYAI_ERR_BAD_STATE, "prefill: prefix network weights not set");
+  if (batch < 1 || batch > c->base.B || prefix_len < 1 || prefix_len > c->cfg.max_prefix_len)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "prefill: batch or prefix length outside the context's capacity");
+  const Dims d = prefill_dims(c->base, batch, prefix_len);
+  const Plan plan = make_plan(d, c->wt);
+  HIPCHK(c, enqueue_prefill(d, c->bp, plan, c->wt, tokens, c->stream));
+  // the new prefix replaces the old one (the invalidation point); graphs read the cache in place
+  c->have_prefix = true;
+  c->batch = batch;
+  c->prefix_len = prefix_len;
   return PHYAI_OK;
 }
 

@@ -91,6 +91,9 @@ typedef struct {
   int time_mlp;               /* 0: the modulation maps read the timestep embedding e(t); 1: they
                                  read W_tm2 swish(W_tm1 e + b_tm1) + b_tm2 (phyai_weights w_tm*,
                                  swish(z) = z / (1 + exp(-z)); a reading) */
+  int prefill;                /* 1: the context also holds a prefix network and can compute the
+                                 prefix K/V itself (phyai_prefill); fp32 or bf16 weights, bf16 when
+                                 max_batch * max_prefix_len > 64 */
 } phyai_config;
 
 /* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,
@@ -129,6 +132,26 @@ phyai_status phyai_set_weights(phyai_ctx* ctx, const phyai_weights* w);
  * 1 <= prefix_len <= max_prefix_len. */
 phyai_status phyai_set_prefix_kv(phyai_ctx* ctx, const void* k, const void* v,
                                  int batch, int prefix_len);
+
+/* Prefix network of a context created with prefill = 1: the four linears of its L layers
+ * (dev pointers, fp32 or bf16 as the expert's; shapes and row order as the expert's w_qkv,
+ * w_o, w_gu, w_d).  The layer is the expert's with a plain RMSNorm in place of the
+ * adaptive one, no positional encoding, and bidirectional attention among the prefix
+ * tokens only.  Copied (re-laid out) into the arena. */
+typedef struct {
+  const void *w_qkv, *w_o, *w_gu, *w_d;
+} phyai_prefill_weights;
+phyai_status phyai_set_prefill_weights(phyai_ctx* ctx, const phyai_prefill_weights* w);
+
+/* Compute the prefix K/V from the prefix tokens and install it (PhyAI reading Sec. 5.1:
+ * the vision-language prefix is computed once per observation; Sec. 8.2 check 1).  tokens:
+ * dev [batch][prefix_len][width] in the weight element type (the prefix network's input
+ * embeddings).  Runs the prefix network's L layers over the batch x prefix_len rows on the
+ * context stream; every layer's K/V lands in the cache rows the cached loop reads, replacing
+ * any previous prefix (the invalidation point, as phyai_set_prefix_kv).  Requires
+ * phyai_set_prefill_weights; 1 <= batch <= max_batch, 1 <= prefix_len <= max_prefix_len.
+ * Overwrites the loop's activation buffers (a denoise call after it starts afresh). */
+phyai_status phyai_prefill(phyai_ctx* ctx, const void* tokens, int batch, int prefix_len);
 
 /* Precompute the timestep / modulation tables of a schedule (PhyAI reading
  * Sec. 5.1: fixed tables over the fixed schedule).  t_host: host float[n_steps], the

@@ -125,6 +125,20 @@ def expert_param_shapes(d: ExpertDims) -> dict:
 EXPERT_LINEARS = ("w_qkv", "w_o", "w_gu", "w_d")
 
 
+def make_prefix_inputs(d: ExpertDims, seed: int = 1, batch: int | None = None) -> dict:
+    """Synthetic prefix network (the four linears of its L layers, N(0, weight_std)) and its
+    input tokens [B][P][D] (N(0, 1), one stream per sample), float32; bf16 values for the
+    bf16 workloads.  Keys: w_qkv, w_o, w_gu, w_d, tokens."""
+    B = d.batch if batch is None else batch
+    L, D, F = d.n_layers, d.width, d.mlp_dim
+    shapes = {"w_qkv": (L, d.qkv_dim, D), "w_o": (L, D, d.n_q_heads * d.head_dim),
+              "w_gu": (L, 2 * F, D), "w_d": (L, D, F)}
+    rnd = bf16_values if d.weight_dtype == "bf16" else (lambda a: a)
+    out = {k: rnd(normal(seed, "p_" + k, shp, d.weight_std)) for k, shp in shapes.items()}
+    out["tokens"] = rnd(np.stack([normal(seed, "p_tokens", (d.prefix_len, D), 1.0, sample=s) for s in range(B)]))
+    return out
+
+
 def make_expert_inputs(d: ExpertDims, seed: int = 0, batch: int | None = None,
                        prefix_len: int | None = None, samples=None) -> dict:
     """All inputs of one workload as float32 arrays.

@@ -74,12 +74,17 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(rope_theta=float("nan")))[0] == 1
     assert _create(lib, _cfg(gated_residual=2))[0] == 1
     assert _create(lib, _cfg(time_mlp=-1))[0] == 1
+    assert _create(lib, _cfg(prefill=2))[0] == 1
+    assert _create(lib, _cfg(prefill=1, weight_dtype=fm.INT4_G128))[0] == 5  # no int4 prefix network
+    assert _create(lib, _cfg(prefill=1, max_prefix_len=100))[0] == 5        # > 64 prefix rows need bf16
     st, h = _create(lib, _cfg(n_layers=0))
     assert h.value is None
 
 
 def test_null_context_calls_fail_cleanly(lib):
     assert lib.phyai_set_prefix_kv(None, None, None, 1, 1) == 1
+    assert lib.phyai_set_prefill_weights(None, None) == 1
+    assert lib.phyai_prefill(None, None, 1, 1) == 1
     assert lib.phyai_denoise(None, None, 1, 1, None) == 1
     assert lib.phyai_sync(None) == 1
     assert lib.phyai_set_weights(None, None) == 1

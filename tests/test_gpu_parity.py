@@ -267,3 +267,48 @@ def test_int4_lossless_weights_match_bf16_path():
     # one bf16 step apart and the difference grows through the layers and steps (1.0e-3 to
     # 1.4e-3 observed).  A mis-decoded nibble, scale or correction gives errors of order 1.
     assert rel_err(got4, gotb) <= 5e-3
+
+
+# ---------------------------------------------------------------- prefix prefill
+def _prefill_case(d, seeds):
+    """GPU: prefill from the prefix tokens, then denoise; oracle: the prefix network's K/V
+    (joint.prefix_kv, the same network the cached-vs-recomputed pin uses), then the cached
+    loop.  Each seed is a new observation (the prefill replaces the previous prefix)."""
+    from oracle import joint
+    inp = synth.make_expert_inputs(d, 0)
+    t = ex.schedule(d.n_steps)
+    dev = device_inputs(d, inp)
+    el = torch.float32 if d.weight_dtype == "f32" else torch.bfloat16
+    e = make_expert(d, dev, t, prefill=True)
+    outs = []
+    for seed in seeds:
+        pre = synth.make_prefix_inputs(d, seed)
+        e.set_prefill_weights({k: torch.from_numpy(pre[k]).cuda().to(el).contiguous()
+                               for k in ("w_qkv", "w_o", "w_gu", "w_d")})
+        e.prefill(torch.from_numpy(pre["tokens"]).cuda().to(el).contiguous())
+        got = e.denoise(dev["noise"]).cpu().numpy()
+        e.sync()
+        pp = {k: np.asarray(pre[k], np.float64) for k in ("w_qkv", "w_o", "w_gu", "w_d")}
+        kv = [joint.prefix_kv(pre["tokens"][b], pp, d) for b in range(d.batch)]
+        ref_inp = dict(inp, k_pre=np.stack([k for k, _ in kv]), v_pre=np.stack([v for _, v in kv]))
+        outs.append((got, ex.denoise(ref_inp, d)))
+    e.close()
+    return outs
+
+
+def test_tiny_prefill_then_denoise_matches_oracle():
+    """64 prefix tokens through the weight-streaming kernels (fp32): parity 1e-4, and a new
+    observation (other prefix network and tokens) changes the chunk accordingly."""
+    (g1, r1), (g2, r2) = _prefill_case(TINY, [1, 2])
+    _say(f"tiny prefill rel err {rel_err(g1, r1):.3e}, {rel_err(g2, r2):.3e}")
+    assert rel_err(g1, r1) <= 1e-4 and rel_err(g2, r2) <= 1e-4
+    assert rel_err(r2, r1) > 1e-3
+
+
+def test_pi05_prefill_then_denoise_matches_oracle():
+    """816 prefix tokens through the tiled GEMMs and many-row attention (bf16)."""
+    _say("case: pi05 prefill 816 tokens")
+    ((g, r),) = _prefill_case(PI05, [1])
+    err = rel_err(g, r)
+    _say(f"pi05 prefill rel err {err:.3e}")
+    assert err <= 2e-2
