@@ -18,6 +18,7 @@ dominant kernel, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
 import json
 import os
@@ -178,9 +179,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,gated,prefill,b32,wam",
+    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam",
                     help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, "
-                         "prefill, b32, wam")
+                         "prefill, capsule, b32, wam")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -368,6 +369,41 @@ def main():
         variants["prefill_816_batch1"] = {"ms_per_prefix": round(msp, 4), "algorithmic_tflop": round(pf / 1e12, 4),
                                           "mfma_frac": round(pf / (msp * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         print(f"[bench] prefill variant: {msp:.4f} ms per prefix", file=sys.stderr, flush=True)
+
+    if "capsule" in todo:
+        # execution-state capsules of the 816-token prefix: save (async kernels), restore
+        # (waits for the stream, reads the header, copies back) and fork at batch 1 -> slot 0
+        ec = fm.ActionExpert.from_dims(d)
+        ec.set_weights(w)
+        ec.set_prefix_kv(kp, vp)
+        nbytes = ec._lib.phyai_capsule_bytes(ec._h)
+        cap = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        capp = ctypes.c_void_p(cap.data_ptr())
+        for _ in range(max(args.warmup, 1)):
+            ec._check(ec._lib.phyai_capsule_save(ec._h, capp, nbytes))
+            ec._check(ec._lib.phyai_capsule_restore(ec._h, capp, nbytes))
+        torch.cuda.synchronize()
+        reps = max(args.steps, 10)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            ec._check(ec._lib.phyai_capsule_save(ec._h, capp, nbytes))
+        b.record()
+        torch.cuda.synchronize()
+        ms_save = a.elapsed_time(b) / reps
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            ec._check(ec._lib.phyai_capsule_restore(ec._h, capp, nbytes))
+        torch.cuda.synchronize()
+        ms_restore = (time.perf_counter() - t0) * 1e3 / reps
+        ec.close()
+        del cap
+        moved = 2 * (nbytes - 256)  # payload read once and written once
+        variants["capsule_816_batch1"] = {
+            "capsule_bytes": int(nbytes), "ms_per_save": round(ms_save, 4), "ms_per_restore": round(ms_restore, 4),
+            "save_hbm_frac": round(moved / (ms_save * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] capsule variant: save {ms_save:.4f} ms, restore {ms_restore:.4f} ms for {nbytes} B",
+              file=sys.stderr, flush=True)
 
     if "b32" in todo:
         # batch 32: each sample its own prefix and noise; bf16 MFMA GEMMs

@@ -26,6 +26,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "bad state", 3: "out of memory", 4:
 
 EXPORTED = (
     "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_prefill_weights", "phyai_prefill",
+    "phyai_capsule_bytes", "phyai_capsule_save", "phyai_capsule_restore", "phyai_capsule_fork",
     "phyai_set_timestep_tables",
     "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
@@ -93,6 +94,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_set_prefix_kv.argtypes = [vp, vp, vp, ci, ci]
     lib.phyai_set_prefill_weights.argtypes = [vp, ctypes.POINTER(PrefillWeights)]
     lib.phyai_prefill.argtypes = [vp, vp, ci, ci]
+    lib.phyai_capsule_bytes.argtypes = [vp]
+    lib.phyai_capsule_save.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.phyai_capsule_restore.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.phyai_capsule_fork.argtypes = [vp, ci, ci]
     lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
     lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
     lib.phyai_set_graph_mode.argtypes = [vp, ci]
@@ -114,6 +119,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in EXPORTED:
         if name not in ("phyai_last_error", "phyai_status_string", "phyai_destroy", "phyai_version"):
             getattr(lib, name).restype = ci
+    lib.phyai_capsule_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -223,6 +229,22 @@ class ActionExpert(_Context):
         assert tokens.is_contiguous() and tokens.dim() == 3
         self._check(self._lib.phyai_prefill(self._h, _ptr(tokens), int(tokens.shape[0]), int(tokens.shape[1])))
         self._batch = int(tokens.shape[0])
+
+    def capsule_save(self):
+        """Snapshot the installed prefix into a new uint8 cuda tensor (the capsule)."""
+        import torch
+        n = self._lib.phyai_capsule_bytes(self._h)
+        if n == 0:
+            raise PhyaiError(2, "no prefix installed")
+        cap = torch.empty(n, dtype=torch.uint8, device="cuda")
+        self._check(self._lib.phyai_capsule_save(self._h, _ptr(cap), n))
+        return cap
+
+    def capsule_restore(self, cap):
+        self._check(self._lib.phyai_capsule_restore(self._h, _ptr(cap), cap.numel()))
+
+    def capsule_fork(self, src: int, dst: int):
+        self._check(self._lib.phyai_capsule_fork(self._h, int(src), int(dst)))
 
     def set_prefix_kv(self, k, v):
         """k, v: cuda [B][L][P][Hkv][dh] in the weight element type."""

@@ -81,6 +81,14 @@ Dims prefill_dims(const Dims& base, int batch, int prefix_len);
 hipError_t enqueue_prefill(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, const void* tokens,
                            hipStream_t stream);
 
+// Execution-state capsule payload: the prefix rows [0, P) of the K and V^T caches of `batch`
+// samples, packed as K [batch][L][Hkv][P][dh] then V^T [batch][L][Hkv][dh][P] (elements of
+// elem_bytes).  save: cache -> capsule; restore: capsule -> cache.
+// Writes a capsule header (n <= 16 32-bit words, passed by value) at dst, stream-ordered.
+hipError_t enqueue_capsule_header(const uint32_t* words, int n, void* dst, hipStream_t stream);
+hipError_t enqueue_capsule_copy(const Dims& d, void* kc, void* vt, void* payload, int batch, int prefix_len,
+                                size_t elem_bytes, bool save, hipStream_t stream);
+
 // Joint video/action denoiser (bf16): whole guided loop, and one launch of a loop kernel.
 hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipStream_t stream);
 hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,

@@ -566,6 +566,87 @@ phyai_status phyai_prefill(phyai_ctx* c, const void* tokens, int batch, int pref
   return PHYAI_OK;
 }
 
+// ---------------------------------------------------------------- execution-state capsules
+// Page "FlashRT-PAI speeds physical AI inference up to 12.66x", its account of the three
+// mechanisms: execution-state capsules snapshot, restore and fork persistent state.
+// The persistent state of this runner is the installed prefix (batch, prefix length and the
+// cache rows [0, P) of every layer); a capsule is a device buffer: a 256-byte header, then
+// the payload of enqueue_capsule_copy.
+namespace {
+struct CapsuleHeader {
+  uint64_t magic;
+  int32_t version, batch, prefix_len, L, Hkv, dh, elem_bytes, pad;
+};
+constexpr uint64_t kCapsuleMagic = 0x5048594149434150ull;  // "PHYAICAP"
+constexpr size_t kCapsuleHeader = 256;
+size_t capsule_payload(const Dims& d, int batch, int prefix_len, size_t es) {
+  return 2 * (size_t)batch * d.L * d.Hkv * prefix_len * d.dh * es;
+}
+}  // namespace
+
+size_t phyai_capsule_bytes(const phyai_ctx* c) {
+  if (!c || c->joint || !c->have_prefix) return 0;
+  return kCapsuleHeader + capsule_payload(c->base, c->batch, c->prefix_len, c->es_act);
+}
+
+phyai_status phyai_capsule_save(phyai_ctx* c, void* capsule, size_t bytes) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "capsule_save: joint denoiser context");
+  if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "capsule_save: no prefix installed");
+  if (!capsule || bytes < phyai_capsule_bytes(c))
+    return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_save: null capsule or fewer bytes than phyai_capsule_bytes");
+  CapsuleHeader h{kCapsuleMagic, 1, c->batch, c->prefix_len, c->base.L, c->base.Hkv, c->base.dh, (int)c->es_act, 0};
+  static_assert(sizeof(CapsuleHeader) % 4 == 0 && sizeof(CapsuleHeader) <= 64, "header words");
+  uint32_t words[sizeof(CapsuleHeader) / 4];
+  std::memcpy(words, &h, sizeof(h));
+  HIPCHK(c, enqueue_capsule_header(words, (int)(sizeof(h) / 4), capsule, c->stream));
+  HIPCHK(c, enqueue_capsule_copy(c->base, c->b.kc, c->b.vt, static_cast<char*>(capsule) + kCapsuleHeader, c->batch,
+                                 c->prefix_len, c->es_act, true, c->stream));
+  return PHYAI_OK;
+}
+
+phyai_status phyai_capsule_restore(phyai_ctx* c, const void* capsule, size_t bytes) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "capsule_restore: joint denoiser context");
+  if (!capsule || bytes < kCapsuleHeader) return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_restore: null or short capsule");
+  CapsuleHeader h{};
+  HIPCHK(c, hipStreamSynchronize(c->stream));  // the capsule may have been written on this stream
+  HIPCHK(c, hipMemcpy(&h, capsule, sizeof(h), hipMemcpyDeviceToHost));
+  if (h.magic != kCapsuleMagic || h.version != 1)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_restore: not a capsule of this library");
+  if (h.L != c->base.L || h.Hkv != c->base.Hkv || h.dh != c->base.dh || h.elem_bytes != (int)c->es_act ||
+      h.batch < 1 || h.batch > c->base.B || h.prefix_len < 1 || h.prefix_len > c->cfg.max_prefix_len)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_restore: capsule shape does not fit this context");
+  if (bytes < kCapsuleHeader + capsule_payload(c->base, h.batch, h.prefix_len, c->es_act))
+    return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_restore: capsule shorter than its header says");
+  HIPCHK(c, enqueue_capsule_copy(c->base, c->b.kc, c->b.vt,
+                                 const_cast<char*>(static_cast<const char*>(capsule)) + kCapsuleHeader, h.batch,
+                                 h.prefix_len, c->es_act, false, c->stream));
+  c->have_prefix = true;  // the restored prefix replaces the installed one (invalidation point)
+  c->batch = h.batch;
+  c->prefix_len = h.prefix_len;
+  return PHYAI_OK;
+}
+
+phyai_status phyai_capsule_fork(phyai_ctx* c, int src_sample, int dst_sample) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "capsule_fork: joint denoiser context");
+  if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "capsule_fork: no prefix installed");
+  if (src_sample < 0 || src_sample >= c->batch || dst_sample < 0 || dst_sample >= c->batch)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "capsule_fork: sample index outside the installed batch");
+  if (src_sample == dst_sample) return PHYAI_OK;
+  const Dims& d = c->base;
+  const size_t per = (size_t)d.L * d.Hkv * d.KS * d.dh * c->es_act;  // one sample's K (or V^T) region
+  char* kc = static_cast<char*>(c->b.kc);
+  char* vt = static_cast<char*>(c->b.vt);
+  HIPCHK(c, hipMemcpyAsync(kc + dst_sample * per, kc + src_sample * per, per, hipMemcpyDeviceToDevice, c->stream));
+  HIPCHK(c, hipMemcpyAsync(vt + dst_sample * per, vt + src_sample * per, per, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
+}
+
 phyai_status phyai_sync(phyai_ctx* c) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   HIPCHK(c, hipStreamSynchronize(c->stream));

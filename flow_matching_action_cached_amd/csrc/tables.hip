@@ -185,6 +185,84 @@ __global__ void k_install_prefix(Dims d, const T* k, const T* v, int B, int P, T
   }
 }
 
+// ------------------------------------------------------------------ execution-state capsules
+// Prefix rows of the caches <-> packed capsule payload (K [B][L][Hkv][P][dh], then V^T
+// [B][L][Hkv][dh][P]).  Both halves are pitched row copies: K has B*L*Hkv rows of P*dh
+// elements at cache pitch KS*dh, V^T has B*L*Hkv*dh rows of P elements at pitch KS.  The
+// copy moves U-sized units (16 bytes when every row, pitch and base allows it), one unit per
+// thread per grid-stride pass; blockIdx.y picks the half.
+struct RowCopy {
+  const char* src;
+  char* dst;
+  size_t rows, units, spitch, dpitch;  // units per row and pitches in units of U
+};
+
+template <class U>
+__global__ __launch_bounds__(256) void k_capsule_rows(RowCopy k, RowCopy v) {
+  const RowCopy& c = blockIdx.y == 0 ? k : v;
+  const U* src = reinterpret_cast<const U*>(c.src);
+  U* dst = reinterpret_cast<U*>(c.dst);
+  const size_t total = c.rows * c.units;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / c.units, u = i - r * c.units;
+    dst[r * c.dpitch + u] = src[r * c.spitch + u];
+  }
+}
+
+struct CapsuleWords {
+  uint32_t w[16];
+};
+__global__ void k_capsule_header(CapsuleWords h, int n, uint32_t* dst) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = h.w[threadIdx.x];
+}
+
+hipError_t enqueue_capsule_header(const uint32_t* words, int n, void* dst, hipStream_t st) {
+  if (n < 1 || n > 16) return hipErrorInvalidValue;
+  CapsuleWords h{};
+  for (int i = 0; i < n; ++i) h.w[i] = words[i];
+  hipLaunchKernelGGL(k_capsule_header, dim3(1), dim3(64), 0, st, h, n, static_cast<uint32_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t enqueue_capsule_copy(const Dims& d, void* kc, void* vt, void* payload, int batch, int prefix_len,
+                                size_t es, bool save, hipStream_t st) {
+  const size_t heads = (size_t)batch * d.L * d.Hkv;
+  if (heads == 0 || prefix_len == 0) return hipSuccess;
+  char* pay = static_cast<char*>(payload);
+  // byte geometry of the two halves: {rows, row bytes, cache pitch}
+  const size_t kb = (size_t)prefix_len * d.dh * es, kp = (size_t)d.KS * d.dh * es;
+  const size_t vb = (size_t)prefix_len * es, vp = (size_t)d.KS * es;
+  char* pk = pay;
+  char* pv = pay + heads * kb;
+  size_t unit = 16;
+  for (; unit > es; unit /= 2) {
+    const size_t m = unit - 1;
+    if (!((kb | kp | vb | vp) & m) && !(((uintptr_t)kc | (uintptr_t)vt | (uintptr_t)pk | (uintptr_t)pv) & m)) break;
+  }
+  auto plan = [&](char* cache, char* packed, size_t rows, size_t rb, size_t pitch) {
+    RowCopy r;
+    r.rows = rows;
+    r.units = rb / unit;
+    r.src = save ? cache : packed;
+    r.dst = save ? packed : cache;
+    r.spitch = (save ? pitch : rb) / unit;
+    r.dpitch = (save ? rb : pitch) / unit;
+    return r;
+  };
+  const RowCopy ck = plan(static_cast<char*>(kc), pk, heads, kb, kp);
+  const RowCopy cv = plan(static_cast<char*>(vt), pv, heads * d.dh, vb, vp);
+  const size_t units = ck.rows * ck.units;  // the same for both halves
+  const int blocks = (int)std::min<size_t>((units + 255) / 256, 4096);
+  const dim3 grid(blocks, 2);
+  switch (unit) {
+    case 16: hipLaunchKernelGGL(k_capsule_rows<uint4>, grid, dim3(256), 0, st, ck, cv); break;
+    case 8: hipLaunchKernelGGL(k_capsule_rows<uint2>, grid, dim3(256), 0, st, ck, cv); break;
+    case 4: hipLaunchKernelGGL(k_capsule_rows<uint32_t>, grid, dim3(256), 0, st, ck, cv); break;
+    default: hipLaunchKernelGGL(k_capsule_rows<uint16_t>, grid, dim3(256), 0, st, ck, cv); break;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ int4 quantiser and repack
 // One wave per (row, 128-column group); lane i quantises columns 2i, 2i+1 and writes one byte.
 __global__ __launch_bounds__(256) void k_quantize_int4(const float* w, int64_t rows, int64_t cols,

@@ -153,6 +153,33 @@ phyai_status phyai_set_prefill_weights(phyai_ctx* ctx, const phyai_prefill_weigh
  * Overwrites the loop's activation buffers (a denoise call after it starts afresh). */
 phyai_status phyai_prefill(phyai_ctx* ctx, const void* tokens, int batch, int prefix_len);
 
+/* Execution-state capsules (page "FlashRT-PAI speeds physical AI inference up to 12.66x",
+ * its account of the three mechanisms: capsules snapshot, restore and fork persistent
+ * state).  The persistent state of an action-expert context is its installed prefix:
+ * batch, prefix length and every layer's cached prefix K/V (each denoise starts from the
+ * noise it is given, so nothing else carries over between predictions).
+ * A capsule is caller-owned device memory of phyai_capsule_bytes(ctx) bytes (0: no prefix
+ * installed, a joint context, or ctx NULL); the library keeps no pointer to it.  Layout:
+ * a 256-byte header (uint64 magic, then int32 version, batch, prefix_len, layers, KV heads,
+ * head_dim, element bytes), then K [batch][layers][KV heads][prefix_len][head_dim] and
+ * V^T [batch][layers][KV heads][head_dim][prefix_len] in the activation element type.
+ *   save:    snapshot the installed prefix into the capsule; header and payload are
+ *            written by kernels, asynchronous on the stream.  PHYAI_ERR_BAD_STATE without
+ *            a prefix, PHYAI_ERR_INVALID_ARG for a NULL or short buffer.
+ *   restore: install the prefix a capsule holds, replacing the current one (the
+ *            invalidation point, as phyai_set_prefix_kv); the capsule may come from any
+ *            context with the same layers, KV heads, head_dim and element type whose
+ *            max_batch and max_prefix_len it fits.  Waits for the stream, then reads the
+ *            header; a foreign or short buffer or a shape that does not fit is
+ *            PHYAI_ERR_INVALID_ARG and leaves the installed prefix unchanged.
+ *   fork:    copy sample src's prefix into sample slot dst of the installed batch, so that
+ *            several rollouts share one observation (stream-ordered); indices outside
+ *            [0, batch) are PHYAI_ERR_INVALID_ARG. */
+size_t phyai_capsule_bytes(const phyai_ctx* ctx);
+phyai_status phyai_capsule_save(phyai_ctx* ctx, void* capsule, size_t capsule_bytes);
+phyai_status phyai_capsule_restore(phyai_ctx* ctx, const void* capsule, size_t capsule_bytes);
+phyai_status phyai_capsule_fork(phyai_ctx* ctx, int src_sample, int dst_sample);
+
 /* Precompute the timestep / modulation tables of a schedule (PhyAI reading
  * Sec. 5.1: fixed tables over the fixed schedule).  t_host: host float[n_steps], the
  * times at which the velocity is evaluated; step k advances by dt_k = t_{k+1} - t_k

@@ -85,6 +85,10 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.phyai_set_prefix_kv(None, None, None, 1, 1) == 1
     assert lib.phyai_set_prefill_weights(None, None) == 1
     assert lib.phyai_prefill(None, None, 1, 1) == 1
+    assert lib.phyai_capsule_bytes(None) == 0
+    assert lib.phyai_capsule_save(None, None, 0) == 1
+    assert lib.phyai_capsule_restore(None, None, 0) == 1
+    assert lib.phyai_capsule_fork(None, 0, 1) == 1
     assert lib.phyai_denoise(None, None, 1, 1, None) == 1
     assert lib.phyai_sync(None) == 1
     assert lib.phyai_set_weights(None, None) == 1
