@@ -496,3 +496,117 @@ def test_time_mlp_wiring():
     full = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"], tuple(inp[k] for k in ("w_tm1", "b_tm1", "w_tm2", "b_tm2")))
     plain = ex.modulation_tables(t, inp["w_mod"], inp["b_mod"])
     assert np.max(np.abs(full - plain)) > 1e-3
+
+
+# ---------------------------------------------------------------- UniPC (joint denoiser solver)
+def _flow_exact_linear_m(x_s, s, t, c0, c1):
+    """Exact solution of dx/dt = (x - m(lambda(t))) / t (data prediction m = c0 + c1 lambda,
+    independent of x), lambda = log((1-t)/t): x_t = (t/s) x_s + t [e^lam (c0 + c1 (lam - 1))]_{lam_s}^{lam_t}."""
+    lam = lambda u: np.log((1 - u) / u)  # noqa: E731
+    prim = lambda u: (1 - u) / u * (c0 + c1 * (lam(u) - 1))  # noqa: E731
+    return (t / s) * x_s + t * (prim(t) - prim(s))
+
+
+def test_unipc_moments_match_quadrature():
+    from scipy.integrate import quad
+    from oracle import wam
+    for h in (0.05, 0.7, 3.0):
+        j = wam.exp_moments(h, 3)
+        for k in range(4):
+            q = quad(lambda u: np.exp(-(h - u)) * u ** k, 0, h, epsabs=1e-15, epsrel=1e-13)[0]
+            assert abs(j[k] - q) <= 1e-9 * abs(q)
+
+
+def test_unipc_first_order_update_is_the_euler_step():
+    """No neighbours: x_t = (sigma_t/sigma_s) x_s + alpha_t (1 - e^{-h}) m_s equals
+    x_s + (t - s) v for the flow's data prediction m = x - s v (also from t = 1 and to t = 0)."""
+    from oracle import wam
+    rng = np.random.default_rng(11)
+    x, v = rng.normal(size=40), rng.normal(size=40)
+    for s, t in ((0.7, 0.55), (1.0, 0.8), (0.3, 0.0), (0.95, 0.05)):
+        got = wam.unipc_update(x, s, t, x - s * v, [])
+        assert np.max(np.abs(got - (x + (t - s) * v))) <= 1e-12
+
+
+def test_unipc_update_is_exact_for_polynomial_data_predictions():
+    """One update with n points integrates any data prediction of degree n-1 in lambda exactly
+    (reference: the ODE's integral by quadrature); one point fewer is not exact."""
+    from scipy.integrate import quad
+    from oracle import wam
+    lam = lambda u: np.log((1 - u) / u)  # noqa: E731
+    coef = np.array([0.3, -0.8, 0.45])    # m(lam) = c0 + c1 lam + c2 lam^2 (scalar state)
+    m = lambda u, deg: sum(coef[i] * lam(u) ** i for i in range(deg + 1))  # noqa: E731
+    s, t, x_s = 0.6, 0.45, 1.7
+    for deg, others in ((1, [0.75]), (2, [0.75, t]), (2, [0.9, 0.75])):
+        integral = quad(lambda l: np.exp(l) * sum(coef[i] * l ** i for i in range(deg + 1)),
+                        lam(s), lam(t), epsabs=1e-14, epsrel=1e-13)[0]
+        exact = (t / s) * x_s + t * integral
+        got = wam.unipc_update(np.array([x_s]), s, t, m(s, deg), [(u, m(u, deg)) for u in others])[0]
+        assert abs(got - exact) <= 1e-10
+    low = wam.unipc_update(np.array([x_s]), s, t, m(s, 2), [(0.75, m(0.75, 2))])[0]
+    integral = quad(lambda l: np.exp(l) * sum(coef[i] * l ** i for i in range(3)), lam(s), lam(t))[0]
+    assert abs(low - ((t / s) * x_s + t * integral)) > 1e-5
+    # base at t = 1 with a constant data prediction: the exact solution t x_1 + (1 - t) m
+    got = wam.unipc_update(np.array([2.0]), 1.0, 0.8, 0.4, [])[0]
+    assert abs(got - (0.8 * 2.0 + 0.2 * 0.4)) <= 1e-15
+
+
+def test_unipc_loop_tracks_the_exact_trajectory():
+    """Data prediction linear in lambda and independent of x, schedule starting below t = 1:
+    every corrector (two points) is exact, so with predictor order 2 every evaluated state from
+    the third on lies on the exact trajectory; with order 1 each evaluated state is the
+    first-order step from the exact corrected state before it."""
+    from oracle import wam
+    c0, c1 = np.array([0.2, -1.1, 0.5]), np.array([0.7, 0.1, -0.4])
+    lam = lambda u: np.log((1 - u) / u)  # noqa: E731
+    ts = np.array([0.9, 0.75, 0.6, 0.45, 0.3, 0.2])
+    x0 = np.array([1.3, -0.2, 0.8])
+    for order in (1, 2):
+        seen = []
+
+        def vel(z, k):
+            seen.append(np.array(z))
+            return (z - (c0 + c1 * lam(ts[k]))) / ts[k]
+
+        wam.unipc_loop(x0, ts, order, vel)
+        for k in range(2, len(ts)):
+            if order == 2:
+                ref = _flow_exact_linear_m(x0, ts[0], ts[k], c0, c1)
+            else:
+                xk1 = _flow_exact_linear_m(x0, ts[0], ts[k - 1], c0, c1)
+                ref = (ts[k] / ts[k - 1]) * xk1 + (1 - ts[k] - (1 - ts[k - 1]) * ts[k] / ts[k - 1]) * (
+                    c0 + c1 * lam(ts[k - 1]))
+            assert np.max(np.abs(seen[k] - ref)) <= 1e-11, (order, k)
+        # the first predicted state is not exact (the pin bites)
+        assert np.max(np.abs(seen[1] - _flow_exact_linear_m(x0, ts[0], ts[1], c0, c1))) > 1e-4
+
+
+def test_unipc_loop_converges_faster_than_euler_on_gaussian_data():
+    """Gaussian data N(mu, s^2): the exact flow maps x_1 to mu + s x_1.  Halving the step
+    halves Euler's error and cuts UniPC's (orders 1 and 2, corrector on) about fourfold."""
+    from oracle import wam
+    rng = np.random.default_rng(3)
+    mu, sd, x1 = rng.normal(size=64), rng.uniform(0.2, 2.0, 64), rng.normal(size=64)
+    exact = mu + sd * x1
+
+    def vel_for(ts):
+        def vel(x, k):
+            t = ts[k]
+            var = (1 - t) ** 2 * sd ** 2 + t ** 2
+            return (t - (1 - t) * sd ** 2) / var * (x - (1 - t) * mu) - mu
+        return vel
+
+    err = {}
+    for n in (16, 32, 64):
+        ts = np.array([1 - k / n for k in range(n)])
+        x = x1.copy()
+        v = vel_for(ts)
+        for k, dt in enumerate(ex.step_sizes(ts)):
+            x = x + dt * v(x, k)
+        err["euler", n] = np.max(np.abs(x - exact))
+        for o in (1, 2):
+            err[o, n] = np.max(np.abs(wam.unipc_loop(x1, ts, o, v) - exact))
+    assert 1.8 <= err["euler", 32] / err["euler", 64] <= 2.2
+    for o in (1, 2):
+        assert err[o, 16] / err[o, 32] >= 2.8 and err[o, 32] / err[o, 64] >= 2.8
+        assert err[o, 32] <= err["euler", 32] / 10
