@@ -179,9 +179,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam",
+    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam,wam_unipc",
                     help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, "
-                         "prefill, capsule, b32, wam")
+                         "prefill, capsule, b32, wam, wam_unipc (needs wam)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -460,6 +460,28 @@ def main():
         msw = a.elapsed_time(b) / nw
         ktw = kernel_times(jd, 5, torch)
         jd.close()
+        if "wam_unipc" in todo:
+            # the same chunk with the UniPC solver (predictor order 2, corrector on)
+            ju = fm.JointDenoiser.from_dims(dw, solver_order=2)
+            ju.set_weights(wdev)
+            ju.set_conditions(wdev["c_cond"], wdev["c_uncond"], dw.guidance)
+            ju.set_timestep_tables(schedule(dw.n_steps))
+            for _ in range(2):
+                ju.denoise(wdev["z_lat"], wdev["z_act"], ol, oa)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(nw):
+                ju.denoise(wdev["z_lat"], wdev["z_act"], ol, oa)
+            b.record()
+            torch.cuda.synchronize()
+            msu = a.elapsed_time(b) / nw
+            ktu = kernel_times(ju, 5, torch, names=("out_euler",))
+            ju.close()
+            variants["wam_joint_cfg_pair_unipc2"] = {
+                "ms_per_chunk": round(msu, 3), "chunks_per_s": round(1000.0 / msu, 3),
+                "out_update_us": round(ktu["out_euler"], 1), "out_update_us_euler": round(ktw["out_euler"], 1),
+                "mfma_frac": round(wam_flops(dw) / (msu * 1e-3) / MFMA_PEAK_TFLOPS / 1e12, 4)}
+            print(f"[bench] joint UniPC variant: {msu:.2f} ms per chunk", file=sys.stderr, flush=True)
         del wdev
         flw = wam_flops(dw)
         kfl = wam_kernel_flops(dw)

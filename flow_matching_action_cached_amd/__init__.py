@@ -66,7 +66,7 @@ class WamConfig(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int), ("width", ctypes.c_int), ("n_heads", ctypes.c_int),
                 ("head_dim", ctypes.c_int), ("mlp_dim", ctypes.c_int), ("latent_tokens", ctypes.c_int),
                 ("latent_dim", ctypes.c_int), ("action_tokens", ctypes.c_int), ("action_dim", ctypes.c_int),
-                ("rms_eps", ctypes.c_float), ("max_arena_bytes", ctypes.c_size_t)]
+                ("rms_eps", ctypes.c_float), ("max_arena_bytes", ctypes.c_size_t), ("solver_order", ctypes.c_int)]
 
 
 _WAM_WFIELDS = ("w_in_lat", "b_in_lat", "w_in_act", "b_in_act", "w_out_lat", "b_out_lat", "w_out_act",
@@ -271,10 +271,10 @@ class JointDenoiser(_Context):
     """Joint video/action denoiser context with a guided branch pair (see include/phyai.h)."""
 
     def __init__(self, *, n_layers, width, n_heads, head_dim, mlp_dim, latent_tokens, latent_dim,
-                 action_tokens, action_dim, rms_eps=1e-6, max_arena_bytes=0, stream=None):
+                 action_tokens, action_dim, rms_eps=1e-6, max_arena_bytes=0, stream=None, solver_order=0):
         self._lib = load_library()
         cfg = WamConfig(n_layers, width, n_heads, head_dim, mlp_dim, latent_tokens, latent_dim, action_tokens,
-                        action_dim, rms_eps, max_arena_bytes)
+                        action_dim, rms_eps, max_arena_bytes, int(solver_order))
         self.cfg = cfg
         h = ctypes.c_void_p()
         st = self._lib.phyai_wam_create(ctypes.byref(cfg), _stream_handle(stream), ctypes.byref(h))

@@ -26,6 +26,7 @@ struct Dims {
   float rope_theta;                // > 0: rotary embedding of the chunk's Q/K at positions P + t
   int gated;                       // 1: each norm's map also yields a residual gate (3 D rows per norm)
   int tmlp;                        // 1: the timestep embedding passes the time MLP first
+  int solver;                      // joint denoiser: 0 Euler, 1 or 2 UniPC predictor order
 };
 
 // Device pointers of one context.  Element types depend on the weight dtype:
@@ -41,6 +42,8 @@ struct Bufs {
   void *kc, *vt;          // K cache [Bmax][L][Hkv][KS][dh], V^T cache [Bmax][L][Hkv][dh][KS] (act)
   const float* mod;       // [N][ntab][nmod][2][D] (scale, shift)
   const float* gate;      // [N][ntab][nmod][D] residual gates (gated variant; null otherwise)
+  const float* uni;       // UniPC: [N][8] per step t_k, corrector (A, w_new, w_k-1, w_k-2), predictor (A, w_k, w_k-1)
+  float* ust;             // UniPC state: corrected z_{k-1}, then two data-prediction slots (3 x E floats)
   const float* cvec;      // [N][ntab][cv_stride]: W_qkv shift_2l | W_gu shift_2l+1 | W_out shift_2L
   const float* dt;        // [N]
   int cv_stride, cv_gu_off, cv_out_off;

@@ -1225,7 +1225,28 @@ __global__ __launch_bounds__(256) void k_wam_out(Dims d, Bufs bf, int k_prev, in
         v[br] = rinv * vres[br][a] + cv[ooff] + to_f32(bo[a]);
       }
       const float vg = v[1] + d.gamma * (v[0] - v[1]);
-      const float zn = z[a] + bf.dt[k_prev] * vg;
+      float zn;
+      if (d.solver) {  // UniPC: corrector of the step into k_prev, then the predictor out of it
+        const float* cf = bf.uni + (size_t)k_prev * 8;
+        const size_t ne = (size_t)d.Tl * d.Cl + (size_t)(d.H - d.Tl) * d.A;
+        const size_t e = lat ? (size_t)t * d.Cl + a : (size_t)d.Tl * d.Cl + (size_t)(t - d.Tl) * d.A + a;
+        float* xp = bf.ust;                                          // corrected z_{k-1} -> z_k
+        float* m_new = bf.ust + ne * (1 + (k_prev & 1));             // holds m_{k-2}, takes m_k
+        const float* m_km1 = bf.ust + ne * (1 + ((k_prev + 1) & 1));  // m_{k-1}
+        const float zk = z[a];
+        const float m = zk - cf[0] * vg;
+        float xc = zk, m1 = 0.f;
+        if (k_prev >= 1) {
+          m1 = m_km1[e];
+          const float m2 = k_prev >= 2 ? m_new[e] : 0.f;
+          xc = cf[1] * xp[e] + cf[2] * m + cf[3] * m1 + cf[4] * m2;
+        }
+        zn = cf[5] * xc + cf[6] * m + cf[7] * m1;
+        xp[e] = xc;
+        m_new[e] = m;
+      } else {
+        zn = z[a] + bf.dt[k_prev] * vg;
+      }
       z[a] = zn;
       xs[a] = zn;
     }

@@ -131,6 +131,93 @@ phyai_status run_loop(phyai_ctx* c, const Dims& d, const Plan& plan, const char*
   return PHYAI_OK;
 }
 
+// ---------------------------------------------------------------- UniPC step weights
+// Flow x_t = (1 - t) x_0 + t eps: alpha = 1 - t, sigma = t, lambda = log(alpha / sigma).  The
+// exact step from s to t is x_t = (sigma_t/sigma_s) x_s + alpha_t int_0^h e^{-(h-u)} m(lambda_s + u) du
+// (h = lambda_t - lambda_s).  Writing m at the neighbour points as m_s + sum_k (u_j)^k / k! m^(k)
+// and matching the terms k = 1..n against the moments phi_k(h) = (1/k!) int_0^h e^{-(h-u)} u^k du
+// (phi_0 = 1 - e^{-h}, phi_k = h^k/k! - phi_{k-1}) gives the n x n system sum_j c_j u_j^k / k! =
+// phi_k; the step is x_t = A x_s + w_s m_s + sum_j w_j m_j with A = sigma_t/sigma_s,
+// w_j = alpha_t c_j, w_s = alpha_t (phi_0 - sum_j c_j).  Limits: to t = 0 the step is m_s; from
+// t = 1 (lambda_s = -inf) it is sigma_t x_s + alpha_t m_new with the new point (or m_s without
+// one); a neighbour at t = 1 has weight 0.
+struct StepW {
+  double A = 0, ws = 0, w[2] = {0, 0};
+};
+
+StepW unipc_step(double s, double t, const double* nb, int n) {
+  StepW r;
+  const double as = 1.0 - s, ss = s, at = 1.0 - t, st = t;
+  if (st == 0.0) {  // to t = 0
+    r.ws = 1.0;
+    return r;
+  }
+  r.A = st / ss;
+  if (as == 0.0) {  // from t = 1: the only neighbour can be the new point t
+    if (n == 0) r.ws = at;
+    else r.w[0] = at;
+    return r;
+  }
+  const double ls = std::log(as / ss), h = std::log(at / st) - ls;
+  double phi[3];
+  phi[0] = -std::expm1(-h);
+  phi[1] = h - phi[0];
+  phi[2] = h * h / 2.0 - phi[1];
+  int idx[2], m = 0;
+  double u[2];
+  for (int j = 0; j < n; ++j)
+    if (nb[j] < 1.0) {
+      idx[m] = j;
+      u[m++] = std::log((1.0 - nb[j]) / nb[j]) - ls;
+    }
+  double c[2] = {0, 0};
+  if (m == 1) {
+    c[0] = phi[1] / u[0];
+  } else if (m == 2) {  // [u0 u1; u0^2/2 u1^2/2] c = [phi1; phi2]
+    const double a11 = u[0], a12 = u[1], a21 = u[0] * u[0] / 2, a22 = u[1] * u[1] / 2;
+    const double det = a11 * a22 - a12 * a21;
+    c[0] = (phi[1] * a22 - a12 * phi[2]) / det;
+    c[1] = (a11 * phi[2] - a21 * phi[1]) / det;
+  }
+  r.ws = at * (phi[0] - c[0] - c[1]);
+  for (int k = 0; k < m; ++k) r.w[idx[k]] = at * c[k];
+  return r;
+}
+
+// Per step k: {t_k, corrector A, w_new, w_{k-1}, w_{k-2}, predictor A, w_k, w_{k-1}} (float).
+std::vector<float> unipc_weights(const float* t_host, int n, int order) {
+  std::vector<double> t(t_host, t_host + n);
+  t.push_back(0.0);
+  std::vector<float> out((size_t)n * 8, 0.f);
+  std::vector<int> pred_nb(n, 0);  // 1: the predictor of step k used the point k-1
+  for (int k = 0; k < n; ++k) {
+    float* o = &out[(size_t)k * 8];
+    o[0] = (float)t[k];
+    if (k >= 1) {  // corrector of the step k-1 -> k: neighbours (k-2 if used) and the new point k
+      double nb[2];
+      int nn = 0, slot_km2 = -1;
+      if (pred_nb[k - 1]) {
+        slot_km2 = nn;
+        nb[nn++] = t[k - 2];
+      }
+      const int slot_new = nn;
+      nb[nn++] = t[k];
+      const StepW c = unipc_step(t[k - 1], t[k], nb, nn);
+      o[1] = (float)c.A;
+      o[2] = (float)c.w[slot_new];
+      o[3] = (float)c.ws;
+      o[4] = slot_km2 >= 0 ? (float)c.w[slot_km2] : 0.f;
+    }
+    pred_nb[k] = (order >= 2 && k >= 1 && t[k + 1] > 0.0) ? 1 : 0;
+    const double nb = k >= 1 ? t[k - 1] : 0.0;
+    const StepW p = unipc_step(t[k], t[k + 1], &nb, pred_nb[k]);
+    o[5] = (float)p.A;
+    o[6] = (float)p.ws;
+    o[7] = (float)p.w[0];
+  }
+  return out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +499,11 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
     return fail(c, PHYAI_ERR_BAD_STATE, "set_timestep_tables: branch conditions not set");
   for (int i = 0; i < n_steps; ++i)
     if (!std::isfinite(t_host[i])) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: non-finite time");
+  if (c->base.solver) {
+    bool ok = t_host[0] <= 1.f && t_host[n_steps - 1] > 0.f;
+    for (int i = 1; i < n_steps; ++i) ok = ok && t_host[i] < t_host[i - 1];
+    if (!ok) return fail(c, PHYAI_ERR_INVALID_ARG, "set_timestep_tables: UniPC needs 1 >= t_0 > ... > t_{N-1} > 0");
+  }
   Dims d = c->base;
   d.N = n_steps;
   const size_t mod_f = (size_t)n_steps * d.ntab * d.nmod * 2 * d.D;
@@ -427,7 +519,7 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
     const size_t gate_f = d.gated ? (size_t)n_steps * d.ntab * d.nmod * d.D : 0;
     const size_t e_f = (size_t)n_steps * d.D * (d.tmlp ? 3 : 1);  // embedding (+ time-MLP hidden, output)
     const size_t bytes = align256(mod_f * 4) + align256(cv_f * 4) + align256((size_t)n_steps * 4) * 2 +
-                         align256(e_f * 8) + align256(gate_f * 4);
+                         align256(e_f * 8) + align256(gate_f * 4) + align256((size_t)n_steps * 8 * 4);
     if (hipMalloc(&c->tab, bytes) != hipSuccess) return fail(c, PHYAI_ERR_OOM, "set_timestep_tables: hipMalloc");
     c->tab_cap = n_steps;
   }
@@ -445,6 +537,10 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   c->e_dev = reinterpret_cast<double*>(p);
   p += align256((size_t)cap * d.D * (d.tmlp ? 3 : 1) * 8);
   float* gate = d.gated ? reinterpret_cast<float*>(p) : nullptr;  // [cap][ntab][nmod][D]
+  p += align256(d.gated ? (size_t)cap * d.ntab * d.nmod * d.D * 4 : 0);
+  float* uni = reinterpret_cast<float*>(p);  // [cap][8] UniPC weights
+  std::vector<float> unih;
+  if (d.solver) unih = unipc_weights(t_host, n_steps, d.solver);
   // step sizes dt_k = t_{k+1} - t_k with t_N = 0
   std::vector<float> dth(n_steps);
   for (int i = 0; i < n_steps; ++i) {
@@ -453,6 +549,8 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   }
   HIPCHK(c, hipMemcpyAsync(c->t_dev, t_host, (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
   HIPCHK(c, hipMemcpyAsync(dt, dth.data(), (size_t)n_steps * 4, hipMemcpyHostToDevice, c->stream));
+  if (d.solver) HIPCHK(c, hipMemcpyAsync(uni, unih.data(), unih.size() * 4, hipMemcpyHostToDevice, c->stream));
+  c->b.uni = d.solver ? uni : nullptr;
   c->b.mod = mod;
   c->b.gate = gate;
   c->b.cvec = cvec;
@@ -684,7 +782,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   const phyai_wam_config& g = *cfg;
   if (g.n_layers < 1 || g.width < 1 || g.n_heads < 1 || g.head_dim < 1 || g.mlp_dim < 1 || g.latent_tokens < 0 ||
       g.action_tokens < 0 || g.latent_tokens + g.action_tokens < 1 || g.latent_dim < 1 || g.action_dim < 1 ||
-      !(g.rms_eps > 0.f))
+      !(g.rms_eps > 0.f) || g.solver_order < 0 || g.solver_order > 2)
     return PHYAI_ERR_INVALID_ARG;
   if (g.width % 256 || g.width > 2048 || g.mlp_dim % 128 || (g.n_heads * g.head_dim) % 128 ||
       (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) || g.latent_dim > 256 ||
@@ -722,6 +820,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   d.rope_theta = 0.f;
   d.gated = 0;
   d.tmlp = 0;
+  d.solver = g.solver_order;
   // mirror into cfg the fields the shared calls read
   c->cfg.n_layers = g.n_layers; c->cfg.width = g.width; c->cfg.n_q_heads = g.n_heads; c->cfg.n_kv_heads = g.n_heads;
   c->cfg.head_dim = g.head_dim; c->cfg.mlp_dim = g.mlp_dim; c->cfg.action_dim = g.action_dim;
@@ -743,6 +842,8 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   const size_t zero_begin = o_kc;
   const size_t o_x = lay.take(std::max<size_t>((size_t)d.Tl * Cl, 1) * 4);
   const size_t o_x2 = lay.take(std::max<size_t>((size_t)(d.H - d.Tl) * A, 1) * 4);
+  const size_t n_state = (size_t)d.Tl * Cl + (size_t)(d.H - d.Tl) * A;  // latent then action elements
+  const size_t o_ust = lay.take(d.solver ? 3 * n_state * 4 : 4);
   const size_t o_h = lay.take((size_t)d.M * D * 4), o_ssq = lay.take((size_t)(D / 16) * d.Mst * 4);
   const size_t mpad = (size_t)(d.M + 15) / 16 * 16;
   const size_t o_hs = lay.take(mpad * D * 2), o_q = lay.take((size_t)d.M * qd * 2);
@@ -775,6 +876,7 @@ phyai_status phyai_wam_create(const phyai_wam_config* cfg, void* hip_stream, phy
   b.kc = base + o_kc; b.vt = base + o_vt;
   b.x = reinterpret_cast<float*>(base + o_x);
   b.x2 = reinterpret_cast<float*>(base + o_x2);
+  b.ust = d.solver ? reinterpret_cast<float*>(base + o_ust) : nullptr;
   b.h = reinterpret_cast<float*>(base + o_h);
   b.ssq = reinterpret_cast<float*>(base + o_ssq);
   b.hs = base + o_hs; b.q = base + o_q; b.o = base + o_o; b.act = base + o_act;

@@ -243,7 +243,7 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, i
  *   per branch b (condition c_b) the layer stack of the action expert with Hq = Hkv heads,
  *   modulation [scale_j; shift_j](t) = W_mod[j] (e(t) + c_b) + b_mod[j], keys = the T tokens;
  *   v_b = adaRMS(h; 2L) W_out_type^T + b_out_type  (latent rows: *_lat, action rows: *_act)
- *   v  = v_u + gamma (v_c - v_u),   z += dt_k v
+ *   v  = v_u + gamma (v_c - v_u),   z += dt_k v   (or the UniPC update of solver_order 1, 2)
  * The same context calls apply: phyai_set_timestep_tables, phyai_set_graph_mode, phyai_sync,
  * phyai_last_error, phyai_get_modulation ([n_steps][2][2L+1][2][D], branch-major: cond then
  * uncond), phyai_enqueue_kernel_repeat (which 0..4 and 7 as for the expert, 5 out-projections +
@@ -260,6 +260,8 @@ typedef struct {
   int latent_tokens, latent_dim, action_tokens, action_dim;
   float rms_eps;              /* > 0 */
   size_t max_arena_bytes;     /* 0 = no limit */
+  int solver_order;           /* 0: Euler (z += dt_k v); 1 or 2: UniPC with this predictor order and
+                               * its corrector (see phyai_wam_denoise); else PHYAI_ERR_INVALID_ARG */
 } phyai_wam_config;
 
 /* bf16 dev pointers, row-major [out][in]:
@@ -287,7 +289,21 @@ phyai_status phyai_wam_set_weights(phyai_ctx* ctx, const phyai_wam_weights* w);
 phyai_status phyai_wam_set_conditions(phyai_ctx* ctx, const void* c_cond, const void* c_uncond,
                                       float guidance);
 
-/* Run the guided Euler loop from z = (z_lat, z_act) at t_0 to t = 0.  z_lat, z_lat_out: dev
+/* UniPC (solver_order 1 or 2; the multistep solver the PhyAI reading names for the
+ * video/action states, Figure 4 and its parallelism section, read as the published UniPC
+ * predictor-corrector): with alpha_t = 1 - t, sigma_t = t, lambda_t = log(alpha_t / sigma_t)
+ * and the data prediction m_k = z_k - t_k v_k of the guided velocity at the evaluated
+ * state z_k, a step s -> t sets
+ *   z_t = (sigma_t / sigma_s) z_s + alpha_t * sum_j w_j m_j,
+ * the weights integrating e^{-(lambda_t - lambda)} against the polynomial in lambda through
+ * the data predictions used: the predictor (t_k -> t_{k+1}) uses m_k and, at order 2,
+ * m_{k-1}; after the model is evaluated at z_{k+1}, the corrector redoes the step from the
+ * corrected z_k with m_{k+1} added.  Points at t = 1 enter only as a step's base, and the
+ * step to t = 0 is first order (z_N = m_{N-1}).  The weights are computed in float64 by
+ * phyai_set_timestep_tables, which then requires 1 >= t_0 > t_1 > ... > t_{N-1} > 0
+ * (else PHYAI_ERR_INVALID_ARG); solver order 0 keeps the Euler update below. */
+
+/* Run the guided loop from z = (z_lat, z_act) at t_0 to t = 0.  z_lat, z_lat_out: dev
  * float [latent_tokens][latent_dim]; z_act, z_act_out: dev float [action_tokens][action_dim]
  * (a pointer may be NULL when its token count is 0).  n_steps must equal the table length.
  * Asynchronous on the context stream, one hipGraph launch (captured once per n_steps). */

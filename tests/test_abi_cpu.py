@@ -129,6 +129,8 @@ def test_joint_create_rejects_bad_config_without_a_device(lib):
     assert _wcreate(lib, _wcfg(n_heads=3))[0] == 5                         # 3 x 64 not a multiple of 128
     assert _wcreate(lib, _wcfg(latent_dim=300))[0] == 5
     assert _wcreate(lib, _wcfg(mlp_dim=1000))[0] == 5
+    assert _wcreate(lib, _wcfg(solver_order=3))[0] == 1                    # UniPC orders 1, 2 only
+    assert _wcreate(lib, _wcfg(solver_order=-1))[0] == 1
     st, h = _wcreate(lib, _wcfg(n_layers=0))
     assert h.value is None
 
