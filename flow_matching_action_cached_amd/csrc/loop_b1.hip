@@ -842,7 +842,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = d.Hq / d.Hkv;
   const int QT = (gq * d.H + 15) / 16, QG = (QT + NW * QPW - 1) / (NW * QPW);
+  // Consecutive workgroups go to different XCDs (round robin over 8); with a grid that is a
+  // multiple of 8, each XCD takes a contiguous run of the ordinal order instead, so the key
+  // splits and query groups of one (sample, KV head) share that XCD's L2 for their K/V.
   int idx = blockIdx.x;
+  if ((gridDim.x & 7) == 0) idx = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int s = idx % S;
   idx /= S;
   const int qg = idx % QG;
