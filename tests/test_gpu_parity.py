@@ -305,6 +305,17 @@ def test_tiny_prefill_then_denoise_matches_oracle():
     assert rel_err(r2, r1) > 1e-3
 
 
+def test_tiny_bf16_batch2_prefill_then_denoise_matches_oracle():
+    """Two observations prefilled at once (2 x 64 rows: the tiled GEMMs and many-row
+    attention, bf16), each sample's chunk against its own prefix network K/V."""
+    _say("case: tiny bf16 prefill, batch 2")
+    ((g, r),) = _prefill_case(dataclasses.replace(TINY, weight_dtype="bf16", batch=2), [3])
+    err = rel_err(g, r)
+    _say(f"tiny bf16 batch-2 prefill rel err {err:.3e}")
+    assert err <= 2e-2
+    assert rel_err(g[1], g[0]) > 0.1                 # the two samples differ
+
+
 def test_pi05_prefill_then_denoise_matches_oracle():
     """816 prefix tokens through the tiled GEMMs and many-row attention (bf16)."""
     _say("case: pi05 prefill 816 tokens")

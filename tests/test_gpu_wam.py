@@ -261,3 +261,45 @@ def test_joint_unipc_rejects_schedules_it_cannot_take():
         with pytest.raises(fm.PhyaiError):
             jd.set_timestep_tables(np.array(bad, np.float32))
     jd.close()
+
+
+@pytest.mark.slow
+def test_joint_unipc_full_width_one_layer_matches_oracle():
+    """Full width, heads, MLP and token count at one layer, UniPC order 2 over three steps
+    from t = 0.9 (every predictor and corrector weight non-zero): the displacement z_N - z_0
+    is the oracle's, and more than ten times closer to it than the Euler loop's."""
+    d = dataclasses.replace(FULL, n_layers=1, n_steps=3)
+    inp = synth.make_wam_inputs(d, 6)
+    t = np.array([0.9, 0.6, 0.3], np.float32)
+    dev = _dev(inp)
+    ju = _make_solver(d, dev, t, 2)
+    gu = _run(ju, dev)
+    ju.close()
+    je = _make(d, dev, t)
+    ge = _run(je, dev)
+    je.close()
+    rl, ra = owam.denoise(inp, d, t, solver_order=2)
+    z0 = np.concatenate([inp["z_lat"].ravel(), inp["z_act"].ravel()]).astype(np.float64)
+    got = np.concatenate([gu[0].ravel(), gu[1].ravel()]) - z0
+    eul = np.concatenate([ge[0].ravel(), ge[1].ravel()]) - z0
+    ref = np.concatenate([rl.ravel(), ra.ravel()]) - z0
+    err = rel_err(got, ref)
+    print(f"joint UniPC full width, 1 layer, 3 steps: displacement rel err {err:.3e}, "
+          f"Euler {rel_err(eul, ref):.3e}", flush=True)
+    assert err <= TOL
+    assert rel_err(eul, ref) > 10 * err
+
+
+@pytest.mark.slow
+def test_joint_unipc_single_step_equals_euler_at_full_shape():
+    """One step from t = 1 to 0 is first order for both solvers (z_1 = z_0 - v): at the full
+    28-layer shape the UniPC context returns the Euler context's result bit for bit."""
+    d = dataclasses.replace(FULL, n_steps=1)
+    dev = synth.wam_device_inputs(d, 0)
+    t = ex.schedule(1)
+    je, ju = _make(d, dev, t), _make_solver(d, dev, t, 2)
+    a, b = _run(je, dev), _run(ju, dev)
+    je.close()
+    ju.close()
+    assert np.isfinite(a[0]).all() and np.isfinite(a[1]).all()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
