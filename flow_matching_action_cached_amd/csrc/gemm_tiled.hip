@@ -34,10 +34,13 @@ __device__ __forceinline__ void wait_stage(int after) {
 }
 
 // WGM x WGN waves, each owning a 16*WMT x 16*WNT sub-tile; NSTG stages of 32*BKB
-// k-columns in LDS, up to NSTG-1 of them in flight while one feeds the MFMAs.
+// k-columns in LDS, up to NSTG-1 of them in flight while one feeds the MFMAs.  With
+// ksplit > 1 the K range is cut into ksplit equal parts, one workgroup each: every part
+// stores its fp32 tile (agent scope) and the last to arrive adds the parts in split order
+// before the epilogue.
 template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, GemmLaunch g, int tilesN,
-                                                               int tilesM) {
+                                                               int tilesM, int ksplit) {
   typedef bf16 AT;
   constexpr int NW = WGM * WGN;
   constexpr int BMT = WGM * WMT, BNT = WGN * WNT;  // 16-row / 16-column tiles per workgroup
@@ -69,10 +72,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
   constexpr int GM = 8;
   const int ntiles = tilesM * tilesN;
   int t = blockIdx.x;
-  if ((ntiles & 7) == 0) t = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  if ((gridDim.x & 7) == 0) t = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int split = t / ntiles;  // K part (outermost in the ordinal order)
+  t -= split * ntiles;
   const int gi = t / (GM * tilesN), rows_g = min(GM, tilesM - gi * GM), within = t - gi * GM * tilesN;
   const int tm = gi * GM + within % rows_g, tn = within / rows_g;
-  const int nstage = g.K / 32 / BKB;
+  const int nstage = g.K / 32 / BKB / ksplit;
+  const int ks_off = split * nstage;  // first stage of this K part
   const int mtiles = (d.M + 15) / 16;  // 16-row tiles present in the activation buffer
   const AT* A = static_cast<const AT*>(g.A);
   const AT* W = static_cast<const AT*>(g.W);
@@ -91,10 +97,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
       const AT* src;
       if (blk < LA) {
         const int rt = min(tm * BMT + blk / BKB, mtiles - 1);  // past the last rows: any valid tile
-        src = A + sw_frag(rt, ks * BKB + blk % BKB, g.K, lane);
+        src = A + sw_frag(rt, (ks_off + ks) * BKB + blk % BKB, g.K, lane);
       } else {
         const int b2 = blk - LA;
-        src = W + sw_frag(wtile(tn * BNT + b2 / BKB), ks * BKB + b2 % BKB, g.K, lane);
+        src = W + sw_frag(wtile(tn * BNT + b2 / BKB), (ks_off + ks) * BKB + b2 % BKB, g.K, lane);
       }
       __builtin_amdgcn_global_load_lds((const void PHYAI_GLOBAL_AS*)src, (void PHYAI_LDS_AS*)&stage(buf)[blk][0], 16,
                                        0, 0);
@@ -153,6 +159,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
         }
       }
     }
+  }
+
+  if (ksplit > 1) {  // cross-workgroup K split: the last arrival sums the parts in split order
+    __shared__ unsigned flag;
+    constexpr uint32_t part_bytes = (uint32_t)NW * WMT * WNT * 1024;
+    const __amdgpu_buffer_rsrc_t ws =
+        agent_rsrc(bf.gemm_ws + (size_t)t * ksplit * (part_bytes / 4), part_bytes * (uint32_t)ksplit);
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+        st_agent16(ws, split * part_bytes + ((w * WMT * WNT + i * WNT + j) * 64 + lane) * 16, acc[i][j]);
+    if (!split_arrive_wg(bf.gemm_cnt + t, (unsigned)ksplit, &flag)) return;
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < ksplit; ++s2)
+          sum += (s2 == split) ? acc[i][j]
+                               : ld_agent16(ws, s2 * part_bytes + ((w * WMT * WNT + i * WNT + j) * 64 + lane) * 16);
+        acc[i][j] = sum;
+      }
   }
 
   // ---- epilogues: acc[i][j][e] is row rowbase + 16 i + 4 grp + e, virtual column tile vt0 + j.
@@ -227,14 +256,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
 //   otherwise (few output tiles) QKV: 64 x 128 with 8 waves and three stages; O / down:
 //   64 x 128 with 16 waves and 128-wide stages
 template <int WMT, int WNT, int WGM, int WGN, int NSTG, int BKB, int EPI>
-static hipError_t launch_cfg(const Dims& d, const Bufs& b, const GemmLaunch& g, int n_cols, hipStream_t st) {
+static hipError_t launch_cfg(const Dims& d, const Bufs& b, const GemmLaunch& g, int n_cols, hipStream_t st,
+                             int ksplit = 1) {
   constexpr int BM = 16 * WGM * WMT, BN = 16 * WGN * WNT;
-  if (n_cols % BN || g.K % (32 * BKB)) return hipErrorInvalidValue;
+  if (n_cols % BN || g.K % (32 * BKB * ksplit)) return hipErrorInvalidValue;
   const int tilesN = n_cols / BN, tilesM = (d.M + BM - 1) / BM;
-  hipLaunchKernelGGL((k_gemm_tiled<WMT, WNT, WGM, WGN, NSTG, BKB, EPI>), dim3(tilesM * tilesN), dim3(64 * WGM * WGN),
-                     0, st, d, b, g, tilesN, tilesM);
+  if (ksplit > 1 && (!b.gemm_ws || !b.gemm_cnt)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_tiled<WMT, WNT, WGM, WGN, NSTG, BKB, EPI>), dim3(tilesM * tilesN * ksplit),
+                     dim3(64 * WGM * WGN), 0, st, d, b, g, tilesN, tilesM, ksplit);
   return hipGetLastError();
 }
+
+// K split of the residual GEMMs (O and down) when their 64 x 128 output tiles are few.
+// That configuration holds 144 KB of LDS, one workgroup per CU, so splitting pays only
+// while tiles x splits still fit one round of 256 CUs (e.g. an 816-row prefill: 104 tiles,
+// two parts); with more tiles (batch 32: 200) the second round costs more than the split
+// saves.  Needs the split scratch (not kept by the joint denoiser, whose shapes take the
+// 128 x 128 configuration).
+static int resid_ksplit(const Dims& d, int n_cols, int K) {
+  const int tiles128 = (d.M + 127) / 128 * (n_cols / 128);
+  if (d.joint || tiles128 >= 512) return 1;
+  const int tiles = (d.M + 63) / 64 * (n_cols / 128);
+  int ks = 1;
+  while (ks < 4 && tiles * ks * 2 <= 256 && K % (128 * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+// Scratch for every call of a context: a call may run fewer rows than the capacity d.M, and
+// fewer tiles take more parts, but parts x tiles never exceed 256 (one round), each part a
+// 64 x 128 fp32 tile.
+size_t tiled_split_ws_floats(const Dims& d) {
+  if (d.joint || d.M <= 64) return 0;
+  return (size_t)256 * 64 * 128;
+}
+
+size_t tiled_split_counters(const Dims& d) { return (size_t)((d.M + 63) / 64) * (d.D / 128); }
 
 hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, int epi, int n_cols,
                              hipStream_t st) {
@@ -245,7 +301,8 @@ hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, 
     case EPI_RESID: {
       const int tiles128 = (d.M + 127) / 128 * (n_cols / 128);
       if (tiles128 >= 512) return launch_cfg<2, 2, 4, 4, 4, 1, EPI_RESID>(d, b, g, n_cols, st);
-      return launch_cfg<1, 2, 4, 4, 3, 4, EPI_RESID>(d, b, g, n_cols, st);
+      const int ks = resid_ksplit(d, n_cols, g.K);
+      return launch_cfg<1, 2, 4, 4, 3, 4, EPI_RESID>(d, b, g, n_cols, st, ks > 1 && b.gemm_ws ? ks : 1);
     }
     case EPI_GEGLU:
       return launch_cfg<4, 4, 4, 4, 2, 2, EPI_GEGLU>(d, b, g, n_cols, st);

@@ -66,6 +66,8 @@ size_t attn_ws_floats(const Dims& d, const Plan& p);
 size_t attn_counters(const Dims& d);
 size_t gemm_ws_floats(const Dims& d, const Plan& p);
 size_t gemm_counters(const Dims& d);
+size_t tiled_split_ws_floats(const Dims& d);  // split scratch of the tiled residual GEMMs (floats)
+size_t tiled_split_counters(const Dims& d);
 Plan make_plan(const Dims& d, WDtype wt);
 
 // Enqueue the whole Euler loop (N steps) on `stream`.  x must already hold the noise.

@@ -1292,6 +1292,7 @@ size_t gemm_counters(const Dims& d) {
   size_t n = d.qkv / 16;
   if ((size_t)d.D / 16 > n) n = d.D / 16;
   if ((size_t)d.F / 16 > n) n = d.F / 16;
+  if (d.M > 64) n = std::max(n, tiled_split_counters(d));
   return n;
 }
 size_t gemm_ws_floats(const Dims& d, const Plan& p) {
@@ -1304,6 +1305,7 @@ size_t gemm_ws_floats(const Dims& d, const Plan& p) {
   upd(d.D / 16, p.s_o, 1);
   upd(d.F / 16, p.s_gu, 2);
   upd(d.D / 16, p.s_d, 1);
+  if (d.M > 64) n = std::max(n, tiled_split_ws_floats(d));
   return n;
 }
 

@@ -346,7 +346,7 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
   const size_t o_attn_ws = lay.take(attn_ws * 4);
   const size_t o_attn_cnt = lay.take(attn_cnt_n * 4);
   const size_t o_gemm_ws = lay.take(gemm_ws_n * 4);
-  const size_t o_gemm_cnt = lay.take(gemm_counters(d) * 4);
+  const size_t o_gemm_cnt = lay.take((c->prefill ? std::max(gemm_counters(d), gemm_counters(dp)) : gemm_counters(d)) * 4);
   // prefill: the prefix network's four linears (same shapes as the expert's) and zero tables
   const size_t pw = c->prefill ? 1 : 0;
   const size_t o_pw_qkv = lay.take(pw * wrow_bytes(c->wt, D) * d.qkv * L);

@@ -55,6 +55,20 @@ def test_tiny_bf16_many_rows(batch):
         assert rel_err(got[b], ref[b]) <= 2e-2
 
 
+def test_tiny_bf16_call_smaller_than_capacity_splits_k():
+    """A context sized for 32 samples (512 rows) running 5 (80 rows): the call's few
+    residual tiles take a K split that the capacity's row count would not, so its scratch
+    must cover any call; parity with the oracle and with a context sized for 5."""
+    d = dataclasses.replace(TINY_BF16, batch=5)
+    inp = synth.make_expert_inputs(d, 4)
+    big = _run(d, inp, max_batch=32)
+    exact = _run(d, inp)
+    err = rel_err(big, ex.denoise(inp, d))
+    _say(f"tiny bf16 batch 5 in a batch-32 context: rel err {err:.3e}")
+    assert err <= 2e-2
+    assert np.array_equal(big, exact)                # same kernels, same split, same sums
+
+
 def test_tiny_bf16_many_rows_rope():
     """The rotary variant through the tiled QKV epilogue (272 rows, ragged last tile)."""
     d = dataclasses.replace(TINY_BF16, batch=17, rope_theta=1e4)
