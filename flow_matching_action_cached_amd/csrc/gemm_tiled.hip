@@ -304,8 +304,13 @@ hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, 
       const int ks = resid_ksplit(d, n_cols, g.K);
       return launch_cfg<1, 2, 4, 4, 3, 4, EPI_RESID>(d, b, g, n_cols, st, ks > 1 && b.gemm_ws ? ks : 1);
     }
-    case EPI_GEGLU:
+    case EPI_GEGLU: {
+      // 256 x 256 tiles; 128 x 256 when those would leave half the CUs or more idle and
+      // the smaller tiles still fit one round (an 816-row prefill: 128 -> 224 workgroups)
+      const int t256 = (d.M + 255) / 256 * (n_cols / 256), t128 = (d.M + 127) / 128 * (n_cols / 256);
+      if (t256 <= 128 && t128 <= 256) return launch_cfg<2, 4, 4, 4, 2, 2, EPI_GEGLU>(d, b, g, n_cols, st);
       return launch_cfg<4, 4, 4, 4, 2, 2, EPI_GEGLU>(d, b, g, n_cols, st);
+    }
   }
   return hipErrorInvalidValue;
 }
