@@ -241,6 +241,10 @@ class ActionExpert(_Context):
         return cap
 
     def capsule_restore(self, cap):
+        """cap: a contiguous uint8 cuda tensor holding a capsule (as capsule_save returns)."""
+        import torch
+        if cap.dtype != torch.uint8 or not cap.is_contiguous():
+            raise ValueError("a capsule is a contiguous uint8 tensor")
         self._check(self._lib.phyai_capsule_restore(self._h, _ptr(cap), cap.numel()))
 
     def capsule_fork(self, src: int, dst: int):
