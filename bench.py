@@ -206,9 +206,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam,wam_unipc",
+    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam,wam_unipc,wam_tp4",
                     help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, "
-                         "prefill, capsule, b32, wam, wam_unipc (needs wam)")
+                         "prefill, capsule, b32, wam, wam_unipc (needs wam), wam_tp4")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -528,6 +528,41 @@ def main():
                        "branches": 2, "guidance": dw.guidance, "euler_steps": dw.n_steps},
         }
         print(f"[bench] joint variant: {msw:.2f} ms per chunk", file=sys.stderr, flush=True)
+
+    if "wam_tp4" in todo:
+        # the shapes of one rank of a 4-way tensor-parallel split of each guidance branch: 4 of
+        # the 16 heads and a quarter of the MLP (column-parallel QKV and gate/up, row-parallel
+        # O and down) over all 4128 tokens, both branches as one batch of two (the matching
+        # rank pair); the all-reduces after O and down are not run
+        dr = dataclasses.replace(synth.WAM_CONFIGS["wam"], n_heads=4, mlp_dim=2048)
+        rdev = synth.wam_device_inputs(dr, 0)
+        jr = fm.JointDenoiser.from_dims(dr)
+        jr.set_weights(rdev)
+        jr.set_conditions(rdev["c_cond"], rdev["c_uncond"], dr.guidance)
+        jr.set_timestep_tables(schedule(dr.n_steps))
+        ol, oa = torch.empty_like(rdev["z_lat"]), torch.empty_like(rdev["z_act"])
+        for _ in range(2):
+            jr.denoise(rdev["z_lat"], rdev["z_act"], ol, oa)
+        torch.cuda.synchronize()
+        nr = max(3, args.steps // 10)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(nr):
+            jr.denoise(rdev["z_lat"], rdev["z_act"], ol, oa)
+        b.record()
+        torch.cuda.synchronize()
+        msr = a.elapsed_time(b) / nr
+        ktr = kernel_times(jr, 5, torch)
+        jr.close()
+        del rdev
+        flr = wam_flops(dr)
+        variants["wam_tp4_rank_shard"] = {
+            "ms_per_chunk": round(msr, 3), "algorithmic_tflop": round(flr / 1e12, 2),
+            "mfma_frac": round(flr / (msr * 1e-3) / MFMA_PEAK_TFLOPS / 1e12, 4),
+            "kernel_us": {k: round(v, 1) for k, v in ktr.items()},
+            "note": "compute of the matching conditional / unconditional rank pair of a 4-way tensor-parallel "
+                    "split of each branch, run as one batch of two; all-reduces and the CFG exchange not run"}
+        print(f"[bench] joint TP-4 rank shard: {msr:.2f} ms per chunk", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -303,3 +303,24 @@ def test_joint_unipc_single_step_equals_euler_at_full_shape():
     ju.close()
     assert np.isfinite(a[0]).all() and np.isfinite(a[1]).all()
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.slow
+def test_joint_tp4_rank_shard_one_layer_velocity_matches_oracle():
+    """The shapes one rank of a 4-way tensor-parallel branch computes (4 of 16 heads, a
+    quarter of the MLP: QKV 2048 -> 1536, O 512 -> 2048, gate/up 2048 -> 4096, down
+    2048 -> 2048, attention over all 4128 tokens), one layer and one step vs the oracle."""
+    d = dataclasses.replace(FULL, n_layers=1, n_steps=1, n_heads=4, mlp_dim=2048)
+    inp = synth.make_wam_inputs(d, 7)
+    t = ex.schedule(d.n_steps)
+    dt = float(ex.step_sizes(t)[0])
+    jd = _make(d, _dev(inp), t)
+    zl, za = _run(jd, _dev(inp))
+    jd.close()
+    rl, ra = owam.denoise(inp, d, t)
+    z0 = np.concatenate([inp["z_lat"].ravel(), inp["z_act"].ravel()]).astype(np.float64)
+    got = (np.concatenate([zl.ravel(), za.ravel()]) - z0) / dt
+    ref = (np.concatenate([rl.ravel(), ra.ravel()]) - z0) / dt
+    err = rel_err(got, ref)
+    print(f"joint TP-4 rank shard, 1 layer: velocity rel err {err:.3e}", flush=True)
+    assert err <= TOL
