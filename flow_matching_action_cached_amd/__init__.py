@@ -27,6 +27,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "bad state", 3: "out of memory", 4:
 EXPORTED = (
     "phyai_create", "phyai_set_weights", "phyai_set_prefix_kv", "phyai_set_prefill_weights", "phyai_prefill",
     "phyai_capsule_bytes", "phyai_capsule_save", "phyai_capsule_restore", "phyai_capsule_fork",
+    "phyai_unipc_weights",
     "phyai_set_timestep_tables",
     "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
@@ -98,6 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_capsule_save.argtypes = [vp, vp, ctypes.c_size_t]
     lib.phyai_capsule_restore.argtypes = [vp, vp, ctypes.c_size_t]
     lib.phyai_capsule_fork.argtypes = [vp, ci, ci]
+    lib.phyai_unipc_weights.argtypes = [vp, ci, ci, vp]
     lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
     lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
     lib.phyai_set_graph_mode.argtypes = [vp, ci]
@@ -320,6 +322,18 @@ class JointDenoiser(_Context):
     def get_modulation(self):
         c = self.cfg
         return self._modulation((self.n_steps, 2, 2 * c.n_layers + 1, 2, c.width))
+
+
+def unipc_weights(t, order):
+    """UniPC step weights of a schedule (host only, as phyai_unipc_weights): float32 [N][8]."""
+    import numpy as np
+    lib = load_library()
+    tt = np.ascontiguousarray(np.asarray(t, dtype=np.float32))
+    out = np.zeros((tt.size, 8), dtype=np.float32)
+    st = lib.phyai_unipc_weights(tt.ctypes.data, int(tt.size), int(order), out.ctypes.data)
+    if st != 0:
+        raise PhyaiError(st, "phyai_unipc_weights: invalid schedule or order")
+    return out
 
 
 def quantize_int4_g128(w, stream=None):

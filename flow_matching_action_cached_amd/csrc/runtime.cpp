@@ -745,6 +745,16 @@ phyai_status phyai_capsule_fork(phyai_ctx* c, int src_sample, int dst_sample) {
   return PHYAI_OK;
 }
 
+phyai_status phyai_unipc_weights(const float* t_host, int n_steps, int order, float* out_host) {
+  if (!t_host || !out_host || n_steps < 1 || (order != 1 && order != 2)) return PHYAI_ERR_INVALID_ARG;
+  bool ok = t_host[0] <= 1.f && t_host[n_steps - 1] > 0.f;
+  for (int i = 1; i < n_steps; ++i) ok = ok && t_host[i] < t_host[i - 1];
+  if (!ok) return PHYAI_ERR_INVALID_ARG;
+  const std::vector<float> w = unipc_weights(t_host, n_steps, order);
+  std::memcpy(out_host, w.data(), w.size() * sizeof(float));
+  return PHYAI_OK;
+}
+
 phyai_status phyai_sync(phyai_ctx* c) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   HIPCHK(c, hipStreamSynchronize(c->stream));

@@ -303,6 +303,14 @@ phyai_status phyai_wam_set_conditions(phyai_ctx* ctx, const void* c_cond, const 
  * phyai_set_timestep_tables, which then requires 1 >= t_0 > t_1 > ... > t_{N-1} > 0
  * (else PHYAI_ERR_INVALID_ARG); solver order 0 keeps the Euler update below. */
 
+/* Host helper, no device needed: the UniPC step weights that phyai_set_timestep_tables
+ * computes for the schedule t_host[0..n_steps) at predictor order 1 or 2, written to
+ * out_host[8 * n_steps] as, per step k: t_k; the corrector of the step into t_k (A on the
+ * corrected z_{k-1}, w on m_k, w on m_{k-1}, w on m_{k-2}; zeros at k = 0); the predictor out
+ * of t_k (A on the corrected z_k, w on m_k, w on m_{k-1}).  PHYAI_ERR_INVALID_ARG for a null
+ * pointer, n_steps < 1, another order, or a schedule not strictly decreasing in (0, 1]. */
+phyai_status phyai_unipc_weights(const float* t_host, int n_steps, int order, float* out_host);
+
 /* Run the guided loop from z = (z_lat, z_act) at t_0 to t = 0.  z_lat, z_lat_out: dev
  * float [latent_tokens][latent_dim]; z_act, z_act_out: dev float [action_tokens][action_dim]
  * (a pointer may be NULL when its token count is 0).  n_steps must equal the table length.
