@@ -163,3 +163,33 @@ def test_pi05_capsule_restore_after_prefix_change():
     assert rel_err(b, a) > 1e-2
     assert np.array_equal(a2, a)
     e.close()
+
+
+def test_tiny_capsule_restores_into_a_larger_context_and_self_fork_is_a_no_op():
+    """A batch-1 capsule restored into a context with room for 2 samples and 128 prefix
+    rows installs batch 1 there (the chunk equals the source context's bit for bit only up
+    to the attention split of the other capacity: 1e-5); forking a sample onto itself
+    changes nothing."""
+    _say("case: tiny fp32 capsule into a larger context")
+    inp = synth.make_expert_inputs(TINY, 0)
+    t = ex.schedule(TINY.n_steps)
+    dev = device_inputs(TINY, inp)
+    e = make_expert(TINY, dev, t)
+    a = e.denoise(dev["noise"]).cpu().numpy()
+    cap = e.capsule_save()
+    e.capsule_fork(0, 0)
+    a2 = e.denoise(dev["noise"]).cpu().numpy()
+    e.sync()
+    assert np.array_equal(a2, a)
+    d2 = dataclasses.replace(TINY, batch=2)
+    dev2 = device_inputs(d2, synth.make_expert_inputs(d2, 1))
+    big = make_expert(d2, dict(dev2, **{k: dev[k] for k in dev if k not in ("k_pre", "v_pre", "noise")}), t,
+                      max_prefix_len=128)
+    big.capsule_restore(cap)
+    assert big._lib.phyai_capsule_bytes(big._h) == cap.numel()   # now holds batch 1, 64 rows
+    b = big.denoise(dev["noise"]).cpu().numpy()
+    big.sync()
+    assert rel_err(b, a) <= 1e-5
+    assert rel_err(a, ex.denoise(inp, TINY)) <= 1e-4
+    e.close()
+    big.close()
