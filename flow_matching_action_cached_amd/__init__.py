@@ -11,11 +11,6 @@ from __future__ import annotations
 import ctypes
 import os
 
-# Kernel arguments in device memory: each of the loop's ~900 launches per chunk reads its
-# arguments before issuing any load, and host-resident arguments add about half a
-# microsecond to that first access on MI355X.  Only effective if HIP is not initialised yet.
-os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
-
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libphyai.so")
 

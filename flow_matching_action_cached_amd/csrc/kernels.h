@@ -1,5 +1,5 @@
 // Internal interface between the host runtime (runtime.cpp) and the HIP kernels
-// (kernels.hip).  Not part of the public C ABI.
+// (loop_b1.hip, gemm_tiled.hip, tables.hip).  Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -98,6 +98,9 @@ hipError_t enqueue_capsule_copy(const Dims& d, void* kc, void* vt, void* payload
 hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipStream_t stream);
 hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int which, int k, int l,
                            hipStream_t stream);
+
+// Zero n floats at p (stream-ordered kernel; no memset node when a caller captures it).
+hipError_t enqueue_zero_f32(float* p, size_t n, hipStream_t stream);
 
 // One-off kernels.  With Dims::tmlp, e_scratch holds 3 N D doubles (embedding, hidden, MLP output).
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -46,7 +47,13 @@ struct phyai_ctx {
   bool have_weights = false, have_prefix = false, have_tables = false, have_cond = false;
   int batch = 0, prefix_len = 0, n_steps = 0;
   int use_graph = 1;
-  std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
+  // captured loops per (bucket batch, prefix length, steps), least recently used evicted
+  struct GraphEntry {
+    hipGraphExec_t exec;
+    uint64_t last_use;
+  };
+  std::map<std::tuple<int, int, int>, GraphEntry> graphs;
+  uint64_t graph_clock = 0;
   // single-kernel repeat graphs for measurement: (which, layer, reps, batch, prefix, steps)
   std::map<std::tuple<int, int, int, int, int, int>, hipGraphExec_t> kgraphs;
 };
@@ -78,8 +85,10 @@ struct Layout {
 
 size_t wrow_bytes(WDtype wt, int K) { return wt == W_F32 ? (size_t)K * 4 : wt == W_BF16 ? (size_t)K * 2 : (size_t)K / 2; }
 
+constexpr size_t kMaxGraphs = 16;  // captured loops kept per context
+
 void drop_graphs(phyai_ctx* c) {
-  for (auto& kv : c->graphs) hipGraphExecDestroy(kv.second);
+  for (auto& kv : c->graphs) hipGraphExecDestroy(kv.second.exec);
   c->graphs.clear();
   for (auto& kv : c->kgraphs) hipGraphExecDestroy(kv.second);
   c->kgraphs.clear();
@@ -111,6 +120,14 @@ phyai_status run_loop(phyai_ctx* c, const Dims& d, const Plan& plan, const char*
   auto key = std::make_tuple(d.B, d.P, d.N);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
+    if (c->graphs.size() >= kMaxGraphs) {  // evict the least recently used loop
+      auto lru = c->graphs.begin();
+      for (auto j = c->graphs.begin(); j != c->graphs.end(); ++j)
+        if (j->second.last_use < lru->second.last_use) lru = j;
+      HIPCHK(c, hipStreamSynchronize(c->stream));  // a launch of it may still be queued
+      hipGraphExecDestroy(lru->second.exec);
+      c->graphs.erase(lru);
+    }
     hipGraph_t graph = nullptr;
     HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
     hipError_t e = enqueue(c->cap_stream);
@@ -125,10 +142,21 @@ phyai_status run_loop(phyai_ctx* c, const Dims& d, const Plan& plan, const char*
     hipGraphDestroy(graph);
     if (e != hipSuccess)
       return fail(c, PHYAI_ERR_DEVICE, std::string(who) + ": graph instantiate: " + hipGetErrorString(e));
-    it = c->graphs.emplace(key, exec).first;
+    it = c->graphs.emplace(key, phyai_ctx::GraphEntry{exec, 0}).first;
   }
-  HIPCHK(c, hipGraphLaunch(it->second, c->stream));
+  it->second.last_use = ++c->graph_clock;
+  HIPCHK(c, hipGraphLaunch(it->second.exec, c->stream));
   return PHYAI_OK;
+}
+
+// Graph bucket of a batch (PhyAI reading Sec. 8.1, Appendix D: a local graph batch with
+// padding for incomplete batches).  Batches on the weight-streaming path (<= 64 token rows)
+// run at their own size, since padding them could push them onto the tiled path; larger
+// ones round up to a multiple of 8 within the context's capacity.
+int graph_bucket(const phyai_ctx* c, int batch) {
+  const int H = c->base.H;
+  if (batch * H <= 64) return batch;
+  return std::min(c->base.B, (batch + 7) / 8 * 8);
 }
 
 // ---------------------------------------------------------------- UniPC step weights
@@ -260,6 +288,19 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
     return PHYAI_ERR_UNSUPPORTED;
   if (g.head_dim != 32 && g.head_dim != 64 && g.head_dim != 128 && g.head_dim != 256) return PHYAI_ERR_UNSUPPORTED;
   if (g.prefill != 0 && g.prefill != 1) return PHYAI_ERR_INVALID_ARG;
+  // The weight-streaming GEMMs (batches of at most 64 token rows; the prefill of a short
+  // prefix) deal each wave a power-of-two run of k-blocks: every linear's input count K
+  // (width, n_q_heads * head_dim, mlp_dim) needs K / 128 a power of two <= 64.
+  auto pow2_quads = [](int K) {
+    const int q = K / 128;
+    return K % 128 == 0 && q >= 1 && q <= 64 && (q & (q - 1)) == 0;
+  };
+  if ((g.chunk_len <= 64 || g.prefill) &&
+      (!pow2_quads(g.width) || !pow2_quads(g.n_q_heads * g.head_dim) || !pow2_quads(g.mlp_dim)))
+    return PHYAI_ERR_UNSUPPORTED;
+  // The prefix network stores its K/V without positions (the cached loop's convention for a
+  // given prefix); a rotated chunk would then mix encoded and unencoded positions.
+  if (g.prefill && g.rope_theta != 0.f) return PHYAI_ERR_UNSUPPORTED;
   // the prefill runs the loop's kernels over batch x prefix rows: no int4 prefix network, and
   // more than 64 rows need the bf16 tiled GEMMs
   if (g.prefill && (g.weight_dtype == PHYAI_INT4_G128 ||
@@ -581,11 +622,17 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
   if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: prefix KV not set");
   if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: timestep tables not set");
   if (n_steps != c->n_steps) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: n_steps differs from the tables");
-  if (batch != c->batch) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: batch differs from the installed prefix");
-  const Dims d = launch_dims(c, batch, c->prefix_len, n_steps);
+  if (batch < 1 || batch > c->batch)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: batch outside [1, batch of the installed prefix]");
+  // the loop runs at the bucket's batch; pad slots start from x = 0 on their (stale but
+  // finite) cache rows, and samples never interact, so the real rows are those of the
+  // bucket's run
+  const int bucket = graph_bucket(c, batch);
+  const Dims d = launch_dims(c, bucket, c->prefix_len, n_steps);
   const Plan plan = make_plan(d, c->wt);
-  const size_t xbytes = (size_t)d.M * d.A * 4;
+  const size_t xbytes = (size_t)batch * d.H * d.A * 4, xbucket = (size_t)d.M * d.A * 4;
   HIPCHK(c, hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  if (xbucket > xbytes) HIPCHK(c, enqueue_zero_f32(c->b.x + xbytes / 4, (xbucket - xbytes) / 4, c->stream));
   const phyai_status st = run_loop(c, d, plan, "denoise");
   if (st != PHYAI_OK) return st;
   HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
@@ -604,6 +651,11 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
   auto key = std::make_tuple(which, layer, reps, c->batch, c->prefix_len, c->n_steps);
   auto it = c->kgraphs.find(key);
   if (it == c->kgraphs.end()) {
+    if (c->kgraphs.size() >= kMaxGraphs) {  // measurement graphs: drop them all
+      HIPCHK(c, hipStreamSynchronize(c->stream));
+      for (auto& kv : c->kgraphs) hipGraphExecDestroy(kv.second);
+      c->kgraphs.clear();
+    }
     hipGraph_t graph = nullptr;
     HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
     hipError_t e = hipSuccess;

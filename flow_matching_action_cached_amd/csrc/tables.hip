@@ -224,6 +224,19 @@ hipError_t enqueue_capsule_header(const uint32_t* words, int n, void* dst, hipSt
   return hipGetLastError();
 }
 
+// Zero-fill of a float range (pad slots of a bucketed batch): a kernel rather than a memset,
+// so that a caller capturing the denoise call into a graph records no memset node.
+__global__ __launch_bounds__(256) void k_zero_f32(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0.f;
+}
+
+hipError_t enqueue_zero_f32(float* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 hipError_t enqueue_capsule_copy(const Dims& d, void* kc, void* vt, void* payload, int batch, int prefix_len,
                                 size_t es, bool save, hipStream_t st) {
   const size_t heads = (size_t)batch * d.L * d.Hkv;

@@ -69,9 +69,12 @@ typedef enum {
 /* Model and capacity.  Constraints (else PHYAI_ERR_UNSUPPORTED): width a multiple of 256
  * and <= 2048; mlp_dim and n_q_heads*head_dim multiples of 128; head_dim 32, 64, 128 or
  * 256; n_q_heads a multiple of n_kv_heads; action_dim a multiple of 8 and <= 256.  Up to
- * 64 token rows (batch x chunk_len) run on weight-streaming kernels (any weight dtype);
- * more rows run on LDS-tiled MFMA GEMMs, which need PHYAI_BF16 and (Hq+2Hkv)*head_dim a
- * multiple of 128. */
+ * 64 token rows (batch x chunk_len) run on weight-streaming kernels (any weight dtype),
+ * which deal each wave a power-of-two run of k-blocks: when chunk_len <= 64 or prefill = 1,
+ * width / 128, n_q_heads*head_dim / 128 and mlp_dim / 128 must each be a power of two
+ * <= 64.  More rows run on LDS-tiled MFMA GEMMs, which need PHYAI_BF16 and
+ * (Hq+2Hkv)*head_dim a multiple of 128.  The activation element type follows the weight
+ * dtype (fp32 for PHYAI_F32, bf16 otherwise), so no separate activation dtype is taken. */
 typedef struct {
   int n_layers, width, n_q_heads, n_kv_heads, head_dim, mlp_dim;
   int action_dim, chunk_len, max_prefix_len, max_batch;
@@ -93,7 +96,8 @@ typedef struct {
                                  swish(z) = z / (1 + exp(-z)); a reading) */
   int prefill;                /* 1: the context also holds a prefix network and can compute the
                                  prefix K/V itself (phyai_prefill); fp32 or bf16 weights, bf16 when
-                                 max_batch * max_prefix_len > 64 */
+                                 max_batch * max_prefix_len > 64; not with rope_theta > 0 (the
+                                 prefix network stores its K/V without positions) */
 } phyai_config;
 
 /* Device pointers to the weights.  Element type: fp32 for PHYAI_F32, bf16 otherwise,
@@ -115,14 +119,24 @@ typedef struct {
   const void *w_tm1, *b_tm1, *w_tm2, *b_tm2;   /* time_mlp only: [D][D], [D], [D][D], [D] (io type) */
 } phyai_weights;
 
-/* Create a context on the current HIP device.  hip_stream: the hipStream_t every
- * call is ordered on (NULL = the null stream).  Allocates the whole device arena
- * (weights, KV cache for max_batch x (max_prefix_len + chunk_len) keys, buffers) at
- * once.  *out receives the context, or NULL on error (no message is kept then). */
+/* Create a context on the current HIP device (PhyAI reading, Figure 3 and the Sec. 5.5
+ * item on separating request state from computation: a stateful runner owns the KV cache,
+ * the buffers and the graph buckets, so cached tensors have a defined lifetime).
+ * hip_stream: the hipStream_t every call is ordered on (NULL = the null stream).
+ * Allocates the whole device arena (weights, KV cache for max_batch x (max_prefix_len +
+ * chunk_len) keys, buffers) at once; nothing on the denoise path allocates afterwards.
+ * *out receives the context, or NULL on error (no message is kept then): INVALID_ARG for a
+ * null pointer or a non-positive size, UNSUPPORTED for shapes outside the constraints
+ * above, OOM when the arena exceeds max_arena_bytes or the allocation fails, DEVICE when
+ * no HIP device is usable. */
 phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx** out);
 
-/* Copy the weights (dev pointers, layouts above) into the arena.  Must precede
- * phyai_set_timestep_tables (the tables fold the weights' response to the shift). */
+/* Copy the weights (dev pointers, layouts above) into the arena (PhyAI reading Sec. 5.4
+ * and Figure 3: weights are prepared offline and loaded once by the runner).  The expert
+ * linears are re-laid out for the kernels on the way in.  Must precede
+ * phyai_set_timestep_tables (the tables fold the weights' response to the shift) and
+ * invalidates any tables and captured graphs.  INVALID_ARG for a null pointer (int4: the
+ * four scale arrays too; time_mlp: its four tensors); the pointers are only read. */
 phyai_status phyai_set_weights(phyai_ctx* ctx, const phyai_weights* w);
 
 /* Install the cached prefix K/V (PhyAI reading Sec. 5.1: computed once per
@@ -186,11 +200,21 @@ phyai_status phyai_capsule_fork(phyai_ctx* ctx, int src_sample, int dst_sample);
  * with t_{n_steps} = 0 (uniform: t_k = 1 - k/N, dt = -1/N).  Requires weights. */
 phyai_status phyai_set_timestep_tables(phyai_ctx* ctx, const float* t_host, int n_steps);
 
-/* Run the whole Euler loop: actions_out = x at t = 0 starting from x = noise at t_0.
- * noise, actions_out: dev float [batch][chunk_len][action_dim]; batch must equal the
- * batch of the installed prefix; n_steps must equal the table length.  Asynchronous
- * on the context stream; the whole loop is one hipGraph launch (captured on first use
- * for each (batch, prefix_len, n_steps)). */
+/* Run the whole Euler loop (PhyAI reading Sec. 5.1: the chunk is denoised by a fixed
+ * number of Euler steps over the cached prefix, and the loop is replayed as one captured
+ * graph): actions_out = x at t = 0 starting from x = noise at t_0.
+ * noise, actions_out: dev float [batch][chunk_len][action_dim] (caller-owned; noise is
+ * only read).  1 <= batch <= the batch of the installed prefix: sample b uses prefix
+ * sample b, and samples never interact.  A batch that does not fill its graph bucket is
+ * padded (PhyAI reading Sec. 8.1, Appendix D: local graph batch and padding): the graph
+ * of the bucket runs, the pad slots compute on whatever their cache rows hold, and only
+ * the first `batch` samples are written to actions_out.  Buckets: the exact batch while
+ * batch x chunk_len <= 64 (the weight-streaming path), else the batch rounded up to a
+ * multiple of 8, capped at the installed batch.  n_steps must equal the table length.
+ * Asynchronous on the context stream; one hipGraph launch, captured on first use for
+ * each (bucket, prefix_len, n_steps); at most 16 graphs are kept (least recently used
+ * evicted).  BAD_STATE before weights, prefix or tables; INVALID_ARG for null pointers,
+ * a batch outside [1, installed batch] or n_steps different from the tables. */
 phyai_status phyai_denoise(phyai_ctx* ctx, const float* noise, int batch, int n_steps,
                            float* actions_out);
 
@@ -198,16 +222,23 @@ phyai_status phyai_denoise(phyai_ctx* ctx, const float* noise, int batch, int n_
  * Both run the same kernels in the same order and give bitwise identical results. */
 phyai_status phyai_set_graph_mode(phyai_ctx* ctx, int use_graph);
 
-/* Wait for the context stream; reports asynchronous device errors. */
+/* Wait for the context stream; reports asynchronous device errors (DEVICE, with the
+ * HIP message in phyai_last_error).  The reading of the pages' request life cycle
+ * (PhyAI reading Sec. 5.4: a request ends when its action chunk is ready) is this call:
+ * after it returns OK, actions_out holds the chunk. */
 phyai_status phyai_sync(phyai_ctx* ctx);
 
-/* Message of the last failed call on ctx ("" if none).  Valid until the next call. */
+/* Message of the last failed call on ctx ("" if none; "null context" for NULL).  Valid
+ * until the next call on ctx.  Errors are values, never aborts (PhyAI reading Sec. 8.2
+ * check 1 asks failures to be reported; the runner's state survives a rejected call). */
 const char* phyai_last_error(const phyai_ctx* ctx);
 
 /* Static name of a status code. */
 const char* phyai_status_string(phyai_status s);
 
-/* Free the context and its arena (synchronises its stream first).  NULL is a no-op. */
+/* Free the context, its arena, tables and graphs (synchronises its stream first), which
+ * ends the lifetime of every cached tensor the context owned (PhyAI reading Figure 3).
+ * NULL is a no-op. */
 void phyai_destroy(phyai_ctx* ctx);
 
 /* Offline round-to-nearest int4 quantiser (PhyAI reading Sec. 5.4 and Figure 3:

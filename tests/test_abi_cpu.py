@@ -77,6 +77,16 @@ def test_create_rejects_bad_config_without_a_device(lib):
     assert _create(lib, _cfg(prefill=2))[0] == 1
     assert _create(lib, _cfg(prefill=1, weight_dtype=fm.INT4_G128))[0] == 5  # no int4 prefix network
     assert _create(lib, _cfg(prefill=1, max_prefix_len=100))[0] == 5        # > 64 prefix rows need bf16
+    # weight-streaming GEMMs: every linear's K / 128 must be a power of two <= 64
+    for kw in (dict(width=768), dict(width=1280), dict(width=1536), dict(width=1792),
+               dict(mlp_dim=384), dict(mlp_dim=640), dict(mlp_dim=1152), dict(mlp_dim=3072),
+               dict(mlp_dim=6144), dict(mlp_dim=16384), dict(n_q_heads=6, head_dim=64),
+               dict(n_q_heads=3, n_kv_heads=1, head_dim=256)):
+        assert _create(lib, _cfg(**kw))[0] == 5, kw
+    # ... unless no batch or prefill ever fits 64 rows (then only the tiled GEMMs run)
+    assert _create(lib, _cfg(chunk_len=100, mlp_dim=3072, weight_dtype=fm.BF16))[0] != 5
+    # the prefix network stores unrotated K/V: no prefill together with rotary positions
+    assert _create(lib, _cfg(prefill=1, rope_theta=1e4))[0] == 5
     st, h = _create(lib, _cfg(n_layers=0))
     assert h.value is None
 

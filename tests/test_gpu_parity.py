@@ -213,16 +213,34 @@ PI05_I4 = synth.CONFIGS["pi05_int4"]
 
 def test_int4_quantiser_bit_exact():
     """The library's GPU quantiser produces exactly the oracle's codes and scales
-    (integer work: bit-exact), including an all-zero group and a ragged row count."""
+    (integer work: bit-exact), including an all-zero group, a ragged row count and exact
+    ties: groups whose scale is a power of two (7 * 2^e as the largest magnitude) holding
+    every half-integer multiple (n + 1/2) 2^e, so W / s is an exact tie that round half to
+    even must settle, plus the hand-worked golden row (scale 1)."""
+    import json
+    import os
     import flow_matching_action_cached_amd as fm
     from oracle import int4 as q4
     w = synth.normal(0, "w_qkv", (37, 1024), 0.02)
     w[3, 128:256] = 0.0
-    w[5, :8] = [2.5e-3, 3.5e-3, -2.5e-3, 7e-3, -7e-3, 0.5e-3, 1.5e-3, -1e-3]
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "int4_nibbles.json")))
+    w[5, :128] = 0.0
+    w[5, :8] = g["row_head"]                                   # scale 1, ties 2.5, 3.5, -2.5, 0.5
+    halves = np.array([n + 0.5 for n in range(-7, 7)], np.float32)   # -6.5 .. 6.5: 14 ties
+    for row, e in ((6, 0), (7, -7), (8, -9), (9, 3)):
+        grp = np.zeros(128, np.float32)
+        grp[:14] = halves
+        grp[14], grp[15] = 7.0, -7.0                           # largest magnitude 7: s = 2^e exactly
+        w[row, 256:384] = grp * np.float32(2.0 ** e)
     packed, scales = fm.quantize_int4_g128(torch.from_numpy(w).cuda())
     ref_p, ref_s = q4.quantize(w)
-    assert np.array_equal(packed.cpu().numpy(), ref_p)
-    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_s)
+    got_p, got_s = packed.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+    assert got_s[5, 0] == g["scale_bits"] and got_p[5, :4].tolist() == g["bytes_head"]
+    codes = q4.unpack_codes(got_p)
+    for row in (6, 7, 8, 9):                                   # half to even: -6.5 -> -6, 0.5 -> 0, ...
+        assert codes[row, 256:270].tolist() == [int(2 * round(x / 2)) for x in halves]
+    assert np.array_equal(got_p, ref_p)
+    assert np.array_equal(got_s, ref_s)
 
 
 def test_tiny_int4_matches_oracle():

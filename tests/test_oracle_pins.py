@@ -610,3 +610,32 @@ def test_unipc_loop_converges_faster_than_euler_on_gaussian_data():
     for o in (1, 2):
         assert err[o, 16] / err[o, 32] >= 2.8 and err[o, 32] / err[o, 64] >= 2.8
         assert err[o, 32] <= err["euler", 32] / 10
+
+
+def test_int4_decode_mistakes_exceed_the_lossless_bound():
+    """The GPU test that compares the int4 path with the bf16 path on lossless weights uses a
+    bound of 5e-3: about 4x the difference two bf16-activation paths show from summation
+    order alone (1.0e-3 to 1.4e-3 measured), and far below what a wrong decode does.  Planted
+    in the oracle here (tiny workload, all four linears): swapped nibbles, the neighbouring
+    group's scale, or offset-binary codes read as two's complement each move the chunk by
+    more than 20 times the bound."""
+    import dataclasses as dc
+    d4 = dc.replace(synth.CONFIGS["tiny"], weight_dtype="int4")
+    inp = synth.make_expert_inputs(d4, 0)
+    lin = ("w_qkv", "w_o", "w_gu", "w_d")
+    qs = {k: q4.quantize_stack(inp[k]) for k in lin}
+    ref = ex.denoise(inp, d4, linears={k: q4.dequantize_stack(*qs[k]) for k in lin})
+
+    def swap(p):
+        return ((p >> 4) | (p << 4)).astype(np.uint8)
+
+    def sign(p):
+        return (((p & 15) ^ 8) | (((p >> 4) ^ 8) << 4)).astype(np.uint8)
+
+    mistakes = {
+        "swapped nibbles": {k: q4.dequantize_stack(swap(qs[k][0]), qs[k][1]) for k in lin},
+        "neighbour scale": {k: q4.dequantize_stack(qs[k][0], np.roll(qs[k][1], 1, axis=-1)) for k in lin},
+        "sign convention": {k: q4.dequantize_stack(sign(qs[k][0]), qs[k][1]) for k in lin},
+    }
+    for name, lins in mistakes.items():
+        assert ex.rel_err(ex.denoise(inp, d4, linears=lins), ref) > 20 * 5e-3, name
