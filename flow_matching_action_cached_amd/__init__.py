@@ -24,7 +24,7 @@ EXPORTED = (
     "phyai_capsule_bytes", "phyai_capsule_save", "phyai_capsule_restore", "phyai_capsule_fork",
     "phyai_unipc_weights",
     "phyai_set_timestep_tables",
-    "phyai_denoise", "phyai_set_graph_mode", "phyai_sync", "phyai_last_error", "phyai_status_string",
+    "phyai_denoise", "phyai_set_graph_mode", "phyai_set_persistent", "phyai_loop_form", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
     "phyai_enqueue_kernel_repeat", "phyai_wam_create", "phyai_wam_set_weights", "phyai_wam_set_conditions",
     "phyai_wam_denoise",
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
     lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
     lib.phyai_set_graph_mode.argtypes = [vp, ci]
+    lib.phyai_set_persistent.argtypes = [vp, ci]
+    lib.phyai_loop_form.argtypes = [vp, ci]
     lib.phyai_sync.argtypes = [vp]
     lib.phyai_last_error.argtypes = [vp]
     lib.phyai_last_error.restype = ctypes.c_char_p
@@ -147,6 +149,14 @@ class _Context:
 
     def set_graph_mode(self, use_graph: bool):
         self._check(self._lib.phyai_set_graph_mode(self._h, int(bool(use_graph))))
+
+    def set_persistent(self, enable: bool):
+        """Use the persistent one-kernel loop where the shape supports it (see phyai.h)."""
+        self._check(self._lib.phyai_set_persistent(self._h, int(bool(enable))))
+
+    def loop_form(self, batch: int) -> int:
+        """1: a denoise of `batch` samples runs the persistent kernel; 0: the graph; -1: not runnable."""
+        return int(self._lib.phyai_loop_form(self._h, int(batch)))
 
     def enqueue_kernel_repeat(self, which: int, layer: int, reps: int):
         """One graph replay of `reps` launches of a single loop kernel (see phyai.h)."""

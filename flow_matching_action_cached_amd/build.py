@@ -15,8 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphyai.so")
 
-SOURCES = [os.path.join(CSRC, n) for n in ("loop_b1.hip", "gemm_tiled.hip", "tables.hip", "runtime.cpp")]
-HEADERS = [os.path.join(CSRC, n) for n in ("common.h", "kernels.h", "epilogue.h")] + [os.path.join(INCLUDE, "phyai.h")]
+SOURCES = [os.path.join(CSRC, n)
+           for n in ("loop_b1.hip", "loop_persistent.hip", "gemm_tiled.hip", "tables.hip", "runtime.cpp")]
+HEADERS = [os.path.join(CSRC, n) for n in ("common.h", "kernels.h", "epilogue.h", "persistent.h")] + \
+    [os.path.join(INCLUDE, "phyai.h")]
 
 # Packed-fp32 VALU forms are kept out of every code object (they are not needed here and
 # the build stays on plain fp32 instructions).

@@ -1,0 +1,1105 @@
+// Persistent Euler loop for few token rows (batch x chunk <= 64, bf16), gfx950.
+//
+// The same step as the per-layer launches (PhyAI reading "PhyAI: Real-Time Physical AI at
+// the Edge, Scalable Rollouts in the Cloud", Sec. 5.1 and 5.5: QKV with the adaptive norm
+// folded in, attention over the cached prefix and the chunk, output projection, GeGLU MLP,
+// final norm, out-projection and the Euler update), but the whole N-step loop is one kernel
+// of co-resident workgroups, one per compute unit.  Each former launch boundary becomes a
+// hand-off between workgroups, and every workgroup issues the next phase's weight loads
+// before it waits for that hand-off, so the weight stream leaves the dependency chain (the
+// page "FlashRT-PAI speeds physical AI inference up to 12.66x": deep kernel fusion with
+// launch overlap removes the gaps between operations).
+//
+// Placement.  Workgroups go to the 8 XCDs round robin (workgroup w on XCD w mod 8; checked
+// at start against HW_REG_XCC_ID).  XCD x owns the query heads [x hpx, (x+1) hpx): it
+// computes their queries and, redundantly, the chunk's keys and values, runs their attention
+// and split merge, and their slice of the output projection's inputs; it owns the MLP columns
+// [x F/8, (x+1) F/8) of gate/up and the same slice of the down projection's inputs.  The two
+// residual sums (output projection over the 8 head groups, down projection over the 8 column
+// groups) are the only hand-offs between XCDs; the others stay inside one XCD's L2.
+//
+// Hand-offs.  A workgroup publishes a monotonic epoch flag when it has finished a phase (all
+// its stores performed); a consumer polls exactly the flags of what it reads: its XCD's 32
+// workgroups, the tile pairs of a residual sum, or the token rows of the out-projection.  The
+// last of the 8 partial sums of a residual tile pair to arrive adds them in XCD order and
+// writes the residual, the next norm's input and its statistics.  Every wait is bounded: on
+// overrun a sticky abort word is set, every workgroup leaves at its next wait, and the host
+// reports a device error.
+//
+// Visibility.  Data that many workgroups read (norm inputs, statistics, q, o, act) is written
+// with agent-scope stores into per-(step, layer) buffers that nothing has read before in this
+// launch, so plain loads (served by L1 and L2) cannot meet stale lines; data read once (split
+// partials, the residual, the state, the chunk's own K/V rows) is read with agent-scope loads.
+#include "epilogue.h"
+#include "persistent.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace phyai {
+
+#ifdef PHYAI_PHASE_TRACE
+// Trace build only: per workgroup and phase, the real-time counter (100 MHz) when the wait
+// for the phase begins, when it ends, and when the phase's flag is published.
+constexpr int kTracePhases = 4096;
+__device__ uint64_t g_ptrace[256 * kTracePhases * 6];
+__device__ int g_ptrace_phase;  // not used for indexing; the phase index travels in a register
+#define PTRACE(phase, slot)                                                                        \
+  do {                                                                                             \
+    if (threadIdx.x == 0 && (phase) < kTracePhases)                                                \
+      g_ptrace[((size_t)blockIdx.x * kTracePhases + (phase)) * 6 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define PTRACE(phase, slot) ((void)0)
+#endif
+
+namespace {
+
+constexpr unsigned kSpinMax = 1u << 21;  // polls per wait before the loop gives up (about 1 s)
+constexpr int kSC1 = 16;                  // buffer-instruction cache policy: agent scope (sc1)
+
+__device__ __forceinline__ uint64_t ld_flag(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_u32_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_bf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, byte_off, 0, kSC1);
+}
+__device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, byte_off, 0, kSC1);
+}
+__device__ __forceinline__ float ld_f32_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSC1));
+}
+__device__ __forceinline__ u32x4 ld_16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSC1));
+}
+__device__ __forceinline__ void st_16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kSC1);
+}
+// 16-byte buffer load: uniform resource and soffset, per-lane voffset (in the fragment-native
+// layout the per-lane part of every fragment address is lane * 16, so one VGPR serves all
+// loads of a wave).  aux: 0 plain, kNT non-temporal (weights, read once per step), kSC1.
+constexpr int kNT = 2;
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+template <int AUX = 0>
+__device__ __forceinline__ bf16x8 bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8, bload16<AUX>(r, voff, soff));
+}
+
+// ------------------------------------------------------------------ hand-off waits
+// Lanes of wave 0 poll flags base[i * stride] (i < n) until each reaches epoch e; every wave
+// then meets at the workgroup barrier.  False once the loop is aborted (by this wait's
+// overrun or by another workgroup): the caller leaves the kernel.
+__device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int n, uint64_t e, int* lds_ok) {
+  const int tid = threadIdx.x;
+  PTRACE((int)(e - a.epoch0) + 1, 0);
+  if (tid < 64) {
+    int ok = 1;
+    for (int i = tid; i < n && ok; i += 64) {
+      const uint64_t* f = base + (size_t)i * stride;
+      unsigned spins = 0;
+      while ((int64_t)(ld_flag(f) - e) < 0) {
+        ++spins;
+        if ((spins & 255) == 0 && ld_u32_agent(a.ctl) != 0) {
+          ok = 0;
+          break;
+        }
+        if (spins > kSpinMax) {
+          st_u32_agent(a.ctl, 1u);
+          st_u32_agent(a.ctl + 1, (unsigned)(e - a.epoch0));
+          ok = 0;
+          break;
+        }
+      }
+    }
+    ok = __all(ok) ? 1 : 0;
+    if (tid == 0) *lds_ok = ok;
+  }
+  __syncthreads();
+  PTRACE((int)(e - a.epoch0) + 1, 1);
+  return *lds_ok != 0;
+}
+
+// All of this workgroup's stores are performed; then its flag takes epoch e.
+__device__ __forceinline__ void publish(uint64_t* flag, uint64_t e) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) st_flag(flag, e);
+}
+__device__ __forceinline__ void publish_wg(const PArgs& a, uint64_t* flag, uint64_t e) {
+  publish(flag, e);
+  PTRACE((int)(e - a.epoch0), 2);
+}
+
+// ------------------------------------------------------------------ weight-streaming GEMM unit
+// One unit: output column tiles rt0 and rt1 (rt1 < 0: only rt0) over the k-blocks
+// [kb0, kb0 + 4 KBW) of the activation A (swizzled [64][K]); wave w owns k-blocks
+// kb0 + w KBW + [0, KBW).  The weight fragments are loaded ahead of the hand-off (WFr).
+template <int KBW>
+struct WFr {
+  bf16x8 f[KBW][2];
+};
+
+// W: one layer's swizzled [rows][K] matrix.
+template <int KBW>
+__device__ __forceinline__ void load_w(WFr<KBW>& wr, const bf16* W, int rows, int K, int rt0, int rt1, int kb0) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(W, (uint32_t)((size_t)rows * K * 2));
+  const uint32_t vo = (threadIdx.x & 63) * 16;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r1 = rt1 < 0 ? rt0 : rt1;
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    const int kb = kb0 + w * KBW + i;
+    wr.f[i][0] = bload_frag<kNT>(r, vo, (uint32_t)(rt0 * (K / 32) + kb) * 1024u);
+    wr.f[i][1] = bload_frag<kNT>(r, vo, (uint32_t)(r1 * (K / 32) + kb) * 1024u);
+  }
+}
+
+// Products of the unit, reduced over the four waves in a fixed order; wave w returns m-tile w
+// (tot[nt], nt = 0, 1).  With norm, rinv_s[m] = 1 / sqrt(mean(h_m^2) + eps) from the row
+// statistics ssq [64][D/16] is also left in LDS.
+template <int MT, int KBW, bool NORM>
+__device__ __forceinline__ void gemm_unit(const Dims& d, const WFr<KBW>& wr, const bf16* A, int K, int kb0,
+                                          const float* ssq, f32x4 (&tot)[2], char* lds, int tph) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4(*red)[2][MT][64] = reinterpret_cast<f32x4(*)[2][MT][64]>(lds);
+  float* rinv_s = reinterpret_cast<float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
+  bf16x8 af[KBW][MT];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint32_t)(64 * K * 2));
+  const uint32_t vo = lane * 16;
+#pragma unroll
+  for (int i = 0; i < KBW; ++i)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      af[i][mt] = bload_frag(ra, vo, (uint32_t)(mt * (K / 32) + kb0 + w * KBW + i) * 1024u);
+  f32x4 ssv[8];
+  const int srow = min(tid >> 2, d.M - 1), squart = tid & 3, n4 = d.D / 256;
+  if constexpr (NORM) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(ssq, (uint32_t)(64 * (d.D / 16) * 4));
+    const uint32_t so = (uint32_t)(srow * (d.D / 16) + squart * (d.D / 64)) * 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ssv[j] = __builtin_bit_cast(f32x4, bload16(rs, so, (uint32_t)min(j, n4 - 1) * 16u));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KBW; ++i)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma(af[i][mt], wr.f[i][nt], acc[nt][mt]);
+  PTRACE(tph, 3);
+  if constexpr (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < n4) ss += ((ssv[j][0] + ssv[j][1]) + ssv[j][2]) + ssv[j][3];
+    const float s1 = __shfl_xor(ss, 1, 64), s2 = __shfl_xor(ss, 2, 64), s3 = __shfl_xor(ss, 3, 64);
+    const float q0 = squart == 0 ? ss : squart == 1 ? s1 : squart == 2 ? s2 : s3;
+    const float q1 = squart == 1 ? ss : squart == 0 ? s1 : squart == 3 ? s2 : s3;
+    const float q2 = squart == 2 ? ss : squart == 3 ? s1 : squart == 0 ? s2 : s3;
+    const float q3 = squart == 3 ? ss : squart == 2 ? s1 : squart == 1 ? s2 : s3;
+    if (squart == 0) rinv_s[tid >> 2] = 1.0f / sqrtf((((q0 + q1) + q2) + q3) / (float)d.D + d.eps);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[w][nt][mt][lane] = acc[nt][mt];
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    tot[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (w < MT) tot[nt] = ((red[0][nt][w][lane] + red[1][nt][w][lane]) + red[2][nt][w][lane]) + red[3][nt][w][lane];
+  }
+  PTRACE(tph, 4);
+}
+
+// ------------------------------------------------------------------ attention unit
+// (sample b, query head `head`, key split s): wave j owns the head's query tile j (chunk
+// tokens 16 j .. 16 j + 15) and all four share the split's K/V, staged block by block in LDS.
+// The first block may come from registers loaded before the hand-off (pre).  Blocks that hold
+// chunk rows (written this step) are read with agent-scope loads.  The split leaves a partial
+// (O / l in bf16, m and l in fp32) for the merge, or with a single split the output itself.
+template <int DH>
+struct KVPre {
+  static constexpr int CPT = (32 * DH / 8 + DH * 4) / 256;  // 16-byte chunks per thread per block
+  u32x4 c[CPT];
+};
+
+template <int DH>
+__device__ __forceinline__ void kv_load(const PArgs& a, KVPre<DH>& kv, int b, int l, int r, int blk, bool agent) {
+  const Dims& d = a.d;
+  constexpr int KCPR = DH / 8, KCH = 32 * KCPR, VCPR = 4;
+  const size_t kvbase = ((size_t)b * d.Lc + l) * d.Hkv + r;
+  const bf16* Kc = static_cast<const bf16*>(a.b.kc) + kvbase * d.KS * DH;
+  const bf16* Vt = static_cast<const bf16*>(a.b.vt) + kvbase * DH * d.KS;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(Kc, (uint32_t)((size_t)d.KS * DH * 2));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(Vt, (uint32_t)((size_t)d.KS * DH * 2));
+  // chunk c = tid + 256 i: K rows hold KCPR chunks (256 threads cover 256 / KCPR rows per i),
+  // V^T rows VCPR chunks (256 / VCPR rows per i); per lane the offset is fixed, the rest uniform
+  const int tid = threadIdx.x;
+  const uint32_t vk = (uint32_t)((tid / KCPR) * DH * 2 + (tid % KCPR) * 16);
+  const uint32_t vv = (uint32_t)(((tid / VCPR) * d.KS + (tid % VCPR) * 8) * 2);
+  const int aux = agent ? kSC1 : 0;
+#pragma unroll
+  for (int i = 0; i < KVPre<DH>::CPT; ++i) {
+    if (256 * i < KCH) {
+      const uint32_t so = (uint32_t)((blk * 32 + i * (256 / KCPR)) * DH * 2);
+      kv.c[i] = aux ? bload16<kSC1>(rk, vk, so) : bload16(rk, vk, so);
+    } else {
+      const uint32_t so = (uint32_t)(((i - KCH / 256) * (256 / VCPR) * d.KS + blk * 32) * 2);
+      kv.c[i] = aux ? bload16<kSC1>(rv, vv, so) : bload16(rv, vv, so);
+    }
+  }
+}
+
+template <int DH>
+__device__ void attn_unit(const PArgs& a, const char* blk_kl, int k, int l, int b, int head, int s,
+                          const KVPre<DH>& pre, bool pre_valid, char* lds) {
+  const Dims& d = a.d;
+  typedef bf16x8 Frag;
+  constexpr int KROW = DH + 8, VROW = 32 + 4, KCPR = DH / 8, KCH = 32 * KCPR, VCPR = 4;
+  bf16* ks = reinterpret_cast<bf16*>(lds);
+  bf16* vs = ks + 32 * KROW;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);  // query tile of this wave
+  const int qd = d.Hq * DH, r = head / (d.Hq / d.Hkv);
+  const int T = d.P + d.H, nblk = (T + 31) / 32;
+  const int blk0 = s * a.bps, blk1 = min(nblk, blk0 + a.bps);
+  const int kend = min(T, blk1 * 32);
+  const bool active = j * 16 < d.H;
+  const int tok = j * 16 + r16;
+  const bool qvalid = tok < d.H;
+  const int m = b * d.H + (qvalid ? tok : 0);
+
+  Frag qf[DH / 32];
+  {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(blk_kl + a.o_q, (uint32_t)(64 * qd * 2));
+    const uint32_t vq = (uint32_t)((m * qd + grp * 8) * 2);
+#pragma unroll
+    for (int jj = 0; jj < DH / 32; ++jj) qf[jj] = bload_frag(rq, vq, (uint32_t)(head * DH + 32 * jj) * 2u);
+  }
+  const float sc = 1.4426950408889634f / sqrtf((float)DH);
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[DH / 16];
+#pragma unroll
+  for (int t = 0; t < DH / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int g = blk0; g < blk1; ++g) {
+    KVPre<DH> kv;
+    if (g == blk0 && pre_valid) kv = pre;
+    else kv_load<DH>(a, kv, b, l, r, g, (g + 1) * 32 > d.P);
+    __syncthreads();  // the previous block's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < KVPre<DH>::CPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < KCH) {
+        *reinterpret_cast<u32x4*>(ks + (c / KCPR) * KROW + (c % KCPR) * 8) = kv.c[i];
+      } else {
+        bf16* dst = vs + ((c - KCH) / VCPR) * VROW + ((c - KCH) % VCPR) * 8;
+        reinterpret_cast<u32x2*>(dst)[0] = u32x2{kv.c[i][0], kv.c[i][1]};
+        reinterpret_cast<u32x2*>(dst)[1] = u32x2{kv.c[i][2], kv.c[i][3]};
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < DH / 32; ++jj) {
+      s0 = mma(load_frag(ks + r16 * KROW + 32 * jj + grp * 8), qf[jj], s0);
+      s1 = mma(load_frag(ks + (16 + r16) * KROW + 32 * jj + grp * 8), qf[jj], s1);
+    }
+    float sv[8];
+    float mx = -INFINITY;
+    const int kb = g * 32 + grp * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = kb + i < kend ? s0[i] : -INFINITY;
+      sv[4 + i] = kb + 16 + i < kend ? s1[i] : -INFINITY;
+      mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_cand = fmaxf(m_run, mx * sc);
+    if (g == blk0) {
+      m_run = m_cand;
+    } else if (__any(m_cand > m_run + 8.f)) {
+      const float alpha = fast_exp2(m_run - m_cand);
+      l_part *= alpha;
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
+      m_run = m_cand;
+    }
+    Frag pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(fmaf(sv[e], sc, -m_run));
+      l_part += p;
+      pf[e] = (bf16)p;
+    }
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) {
+      const bf16* vp = vs + (t * 16 + r16) * VROW + grp * 4;
+      o[t] = mma(load_frag_split4(vp, vp + 16), pf, o[t]);
+    }
+  }
+  if (!active) return;
+  float l_row = l_part;
+  l_row += __shfl_xor(l_row, 16, 64);
+  l_row += __shfl_xor(l_row, 32, 64);
+  const int QTh = (d.H + 15) / 16;
+  const int S = a.S;
+  if (S == 1) {  // single split: the normalised output goes straight to o
+    if (!qvalid) return;
+    const __amdgpu_buffer_rsrc_t ro = rsrc(blk_kl + a.o_o, (uint32_t)(64 * qd * 2));
+    const float inv = 1.0f / l_row;
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) {
+      const bf16x4 v4 = {(bf16)(o[t][0] * inv), (bf16)(o[t][1] * inv), (bf16)(o[t][2] * inv), (bf16)(o[t][3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+                                            (uint32_t)(sw_idx(m, head * DH + t * 16 + grp * 4, qd) * 2), 0, kSC1);
+    }
+    return;
+  }
+  constexpr int PAY = DH / 32;
+  constexpr uint32_t STRIDE = PAY * 1024 + 128;
+  const size_t item = ((size_t)b * d.Hq + head) * QTh + j;
+  const __amdgpu_buffer_rsrc_t ws = rsrc(a.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
+  const float inv_l = 1.0f / l_row;
+#pragma unroll
+  for (int u = 0; u < PAY; ++u) {
+    const f32x4 x0 = o[2 * u] * inv_l, x1 = o[2 * u + 1] * inv_l;
+    const bf16x8 pk = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
+                       (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+    st_16_sc1(ws, s * STRIDE + (u * 64 + lane) * 16, __builtin_bit_cast(u32x4, pk));
+  }
+  if (grp == 0) {
+    st_f32(ws, s * STRIDE + PAY * 1024 + r16 * 4, m_run);
+    st_f32(ws, s * STRIDE + PAY * 1024 + 64 + r16 * 4, l_row);
+  }
+}
+
+// Merge of the key splits, one wave per (sample, head, query tile, 16-byte slot u): weights
+// 2^(m_s - M) l_s in split order, output columns 32 u + 16 t + 4 grp + i of the head.
+template <int DH>
+__device__ void merge_wave(const PArgs& a, const char* blk_kl, int b, int head, int jt, int u) {
+  const Dims& d = a.d;
+  constexpr int PAY = DH / 32, SM = 32;
+  constexpr uint32_t STRIDE = PAY * 1024 + 128;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const int QTh = (d.H + 15) / 16, S = a.S, qd = d.Hq * DH;
+  const int tok = jt * 16 + r16;
+  const size_t item = ((size_t)b * d.Hq + head) * QTh + jt;
+  const __amdgpu_buffer_rsrc_t ws = rsrc(a.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
+  float ms[SM], ls[SM];
+  u32x4 pv[SM];
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2) {  // every split's statistics and payload in one round trip
+    const uint32_t sp = (uint32_t)min(s2, S - 1) * STRIDE;
+    ms[s2] = ld_f32_sc1(ws, sp + PAY * 1024 + r16 * 4);
+    ls[s2] = ld_f32_sc1(ws, sp + PAY * 1024 + 64 + r16 * 4);
+    pv[s2] = ld_16_sc1(ws, sp + (u * 64 + lane) * 16);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2)
+    if (s2 < S) M = fmaxf(M, ms[s2]);
+  float den = 0.f;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s2 = 0; s2 < SM; ++s2) {
+    const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+    den += wgt;
+    const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2]);
+    acc[0] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
+    acc[1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
+  }
+  if (tok >= d.H) return;
+  const int m = b * d.H + tok;
+  const float inv = 1.0f / den;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(blk_kl + a.o_o, (uint32_t)(64 * qd * 2));
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int col = head * DH + 32 * u + 16 * t + grp * 4;
+    const bf16x4 v4 = {(bf16)(acc[t][0] * inv), (bf16)(acc[t][1] * inv), (bf16)(acc[t][2] * inv),
+                       (bf16)(acc[t][3] * inv)};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro, (uint32_t)(sw_idx(m, col, qd) * 2), 0, kSC1);
+  }
+}
+
+// ------------------------------------------------------------------ out-projection + Euler + in-projection
+// One workgroup per token row m (as the launch-per-kernel form).  k_prev >= 0: final norm of
+// step k_prev (its input and statistics from that step's final buffers), v, x += dt v.
+// k_next >= 0: h = x W_in^T + b_in, and the first norm's input and statistics of step k_next.
+__device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds) {
+  const Dims& d = a.d;
+  const Bufs& bf = a.b;
+  float* xs = reinterpret_cast<float*>(lds);
+  float* vres = xs + 256;
+  float* wred = vres + 256;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(bf.x, (uint32_t)(d.M * d.A * 4));
+  if (k_prev >= 0) {
+    const char* fin = a.fin + (size_t)k_prev * a.k_bytes;
+    const float* ssq = reinterpret_cast<const float*>(fin + a.o_ssqf);
+    const bf16* hsr = reinterpret_cast<const bf16*>(fin + a.o_hsf);
+    const bf16* wo = static_cast<const bf16*>(bf.w_out);
+    const int n16 = d.D / 16;
+    float ss = 0.f;
+    if (w == 0) {
+      const float a0 = ssq[(size_t)m * n16 + min(lane, n16 - 1)];
+      const float a1 = ssq[(size_t)m * n16 + min(lane + 64, n16 - 1)];
+      ss = (lane < n16 ? a0 : 0.f) + (lane + 64 < n16 ? a1 : 0.f);
+    }
+    bf16x8 hv[4];
+    float hmask[4];
+    const __amdgpu_buffer_rsrc_t rhs = rsrc(hsr, (uint32_t)(64 * d.D * 2));
+    const __amdgpu_buffer_rsrc_t rwo = rsrc(wo, (uint32_t)(d.A * d.D * 2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = lane * 8 + 512 * j;
+      hmask[j] = kk < d.D ? 1.f : 0.f;
+      hv[j] = bload_frag(rhs, (uint32_t)(sw_idx(m, min(kk, d.D - 8), d.D) * 2), 0u);
+    }
+    for (int a0 = w; a0 < d.A; a0 += 8) {  // outputs a0 and a0 + 4 per pass
+      bf16x8 wv[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int aa = min(a0 + 4 * u, d.A - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wv[u][j] = bload_frag(rwo, (uint32_t)min(lane * 8 + 512 * j, d.D - 8) * 2u, (uint32_t)(aa * d.D * 2));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part += (float)hv[j][e] * (float)wv[u][j][e];
+          acc += hmask[j] * part;
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && a0 + 4 * u < d.A) vres[a0 + 4 * u] = acc;
+      }
+    }
+    if (w == 0) {
+      ss = wave_sum(ss);
+      if (lane == 0) wred[0] = ss;
+    }
+    __syncthreads();
+    const float rinv = 1.0f / sqrtf(wred[0] / (float)d.D + d.eps);
+    for (int aa = tid; aa < d.A; aa += 256) {
+      const bf16* bo = static_cast<const bf16*>(bf.b_out);
+      const float* cv = bf.cvec + (size_t)k_prev * bf.cv_stride + bf.cv_out_off;
+      const float v = rinv * vres[aa] + cv[aa] + (float)bo[aa];
+      const uint32_t xo = (uint32_t)(((size_t)m * d.A + aa) * 4);
+      const float xn = ld_f32_sc1(rx, xo) + bf.dt[k_prev] * v;
+      st_f32(rx, xo, xn);
+      xs[aa] = xn;
+    }
+    __syncthreads();
+  } else {
+    for (int aa = tid; aa < d.A; aa += 256) xs[aa] = ld_f32_sc1(rx, (uint32_t)(((size_t)m * d.A + aa) * 4));
+    __syncthreads();
+  }
+  if (k_next < 0) return;
+  const bf16* wi = static_cast<const bf16*>(bf.w_in);
+  const bf16* bi = static_cast<const bf16*>(bf.b_in);
+  const float* scl = bf.mod + (size_t)k_next * d.nmod * 2 * d.D;  // norm 0, scale row
+  char* blk = a.act + (size_t)k_next * d.L * a.kl_bytes;            // (k_next, layer 0)
+  const __amdgpu_buffer_rsrc_t rh = rsrc(bf.h, (uint32_t)(64 * d.D * 4));
+  const __amdgpu_buffer_rsrc_t rhs = rsrc(blk + a.o_hsa, (uint32_t)(64 * d.D * 2));
+  const __amdgpu_buffer_rsrc_t rss = rsrc(blk + a.o_ssqa, (uint32_t)(64 * (d.D / 16) * 4));
+  const int na = d.A / 8;
+  const __amdgpu_buffer_rsrc_t rwi = rsrc(wi, (uint32_t)(d.D * d.A * 2));
+  for (int n0 = 0; n0 < d.D; n0 += 256) {
+    const int n = n0 + tid;
+    float hn = (float)bi[n];
+    const float sc1 = 1.0f + scl[n];
+    for (int c0 = 0; c0 < na; c0 += 8) {
+      bf16x8 wv[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        wv[c] = bload_frag(rwi, (uint32_t)(tid * d.A * 2), (uint32_t)((n0 * d.A + 8 * min(c0 + c, na - 1)) * 2));
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c0 + c < na)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hn += xs[8 * (c0 + c) + e] * (float)wv[c][e];
+    }
+    st_f32(rh, (uint32_t)(((size_t)m * d.D + n) * 4), hn);
+    st_bf16(rhs, (uint32_t)(sw_idx(m, n, d.D) * 2), hn * sc1);
+    const float sq = sum16(hn * hn);
+    if ((tid & 15) == 0) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + n / 16) * 4), sq);
+  }
+}
+
+// ------------------------------------------------------------------ residual sums across XCDs
+// Tile pair p of a residual linear has one partial per XCD (its split of the input columns).
+// The partials travel as 8-byte words (value, epoch tag): every XCD but one stores its partial
+// and moves on; the reducer (XCD p mod 8) polls the seven others' words until each carries
+// this phase's tag, adds the eight partials in XCD order, and writes the residual
+// h += sum, the next norm's input hs = h (1 + scale_next) and its statistics, then the pair's
+// epoch flag.  No counter and no wait for store acknowledgements on the contributors' side.
+struct ResidPre {
+  float sc1[2];   // 1 + scale of the norm that consumes h, at this lane's column of tile nt
+  float h[2][4];  // residual rows of this wave's m-tile (reducer only)
+};
+
+__device__ __forceinline__ size_t ll_index(int pair, int x, int nt, int w, int i, int lane) {
+  return (((((size_t)pair * 8 + x) * 2 + nt) * 4 + w) * 4 + i) * 64 + lane;
+}
+
+// Loads ahead of the phase's wait: the static scale of both tiles' columns.
+__device__ __forceinline__ void resid_pre_static(ResidPre& rp, const float* scale_next, int pair) {
+  const int r16 = threadIdx.x & 15;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) rp.sc1[nt] = 1.0f + scale_next[(2 * pair + nt) * 16 + r16];
+}
+// After the wait (the residual is written by the previous residual sum of the pair).
+template <int MT>
+__device__ __forceinline__ void resid_pre_h(const PArgs& a, ResidPre& rp, int pair) {
+  const Dims& d = a.d;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = min(w * 16 + grp * 4 + i, d.M - 1);
+      rp.h[nt][i] = w < MT ? ld_f32_sc1(rh, (uint32_t)(((size_t)m * d.D + (2 * pair + nt) * 16 + r16) * 4)) : 0.f;
+    }
+}
+
+// Returns false if the loop was aborted while polling.
+template <int MT>
+__device__ bool resid_sum(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp, char* hs_next,
+                          char* ssq_next, uint64_t e, int* lds_ok) {
+  const Dims& d = a.d;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Each word is built as (value bits, tag) lanes of a u32x2 and moved with one 8-byte buffer
+  // access (single-copy atomic for an aligned 8-byte location).
+  const __amdgpu_buffer_rsrc_t rl = rsrc(a.part, (uint32_t)((size_t)(d.D / 32) * 8 * 2 * 4 * 4 * 64 * 8));
+  const uint32_t tag = (uint32_t)e;
+  const int rx = pair & 7;
+  if (x != rx) {
+    if (w < MT)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, tot[nt][i]), tag}, rl,
+                                                (uint32_t)(ll_index(pair, x, nt, w, i, lane) * 8), 0, kSC1);
+    return true;
+  }
+  int ok = 1;
+  if (w < MT) {
+    float v[8][2][4];
+    unsigned spins = 0;
+    while (true) {
+      bool got = true;
+#pragma unroll
+      for (int x2 = 0; x2 < 8; ++x2)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (x2 == rx) continue;
+            const u32x2 wd = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)(ll_index(pair, x2, nt, w, i, lane) * 8), 0, kSC1));
+            got = got && wd[1] == tag;
+            v[x2][nt][i] = __builtin_bit_cast(float, wd[0]);
+          }
+      if (__all(got)) break;
+      ++spins;
+      if ((spins & 63) == 0 && ld_u32_agent(a.ctl) != 0) {
+        ok = 0;
+        break;
+      }
+      if (spins > kSpinMax / 64) {
+        st_u32_agent(a.ctl, 1u);
+        st_u32_agent(a.ctl + 1, (unsigned)(e - a.epoch0));
+        ok = 0;
+        break;
+      }
+    }
+    if (ok) {
+      const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
+      const __amdgpu_buffer_rsrc_t rhs = rsrc(hs_next, (uint32_t)(64 * d.D * 2));
+      const __amdgpu_buffer_rsrc_t rss = rsrc(ssq_next, (uint32_t)(64 * (d.D / 16) * 4));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int tile = 2 * pair + nt, col = tile * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sum = 0.f;
+#pragma unroll
+          for (int x2 = 0; x2 < 8; ++x2) sum += x2 == rx ? tot[nt][i] : v[x2][nt][i];
+          const int m = w * 16 + grp * 4 + i;
+          float hn = 0.f;
+          if (m < d.M) {
+            hn = rp.h[nt][i] + sum;
+            st_f32(rh, (uint32_t)(((size_t)m * d.D + col) * 4), hn);
+            st_bf16(rhs, (uint32_t)(sw_idx(m, col, d.D) * 2), hn * rp.sc1[nt]);
+          }
+          const float sq = sum16(hn * hn);
+          if (r16 == 0 && m < d.M) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + tile) * 4), sq);
+        }
+      }
+    }
+  }
+  if (tid == 0) *lds_ok = 1;
+  __syncthreads();
+  if (w < MT && lane == 0 && !ok) *lds_ok = 0;
+  __syncthreads();
+  if (*lds_ok == 0) return false;
+  publish(a.flag_pair + pair, e);
+  return true;
+}
+
+template <int MT>
+__device__ void resid_split(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], char* hs_next, char* ssq_next,
+                            uint64_t e, unsigned* lds_flag, const ResidPre& rp) {
+  const Dims& d = a.d;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t part_bytes = 2 * MT * 1024;
+  const __amdgpu_buffer_rsrc_t ws = rsrc(a.part + (size_t)pair * 8 * (part_bytes / 4), part_bytes * 8);
+  if (w < MT)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      st_16_sc1(ws, x * part_bytes + ((nt * MT + w) * 64 + lane) * 16, __builtin_bit_cast(u32x4, tot[nt]));
+  if (!split_arrive_wg(a.cnt + pair, 8u, lds_flag)) return;
+  if (w < MT) {
+    const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
+    const __amdgpu_buffer_rsrc_t rhs = rsrc(hs_next, (uint32_t)(64 * d.D * 2));
+    const __amdgpu_buffer_rsrc_t rss = rsrc(ssq_next, (uint32_t)(64 * (d.D / 16) * 4));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      u32x4 pv[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) pv[s2] = ld_16_sc1(ws, s2 * part_bytes + ((nt * MT + w) * 64 + lane) * 16);
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) sum += __builtin_bit_cast(f32x4, pv[s2]);
+      const int tile = 2 * pair + nt, col = tile * 16 + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = w * 16 + grp * 4 + i;
+        float hn = 0.f;
+        if (m < d.M) {
+          hn = rp.h[nt][i] + sum[i];
+          st_f32(rh, (uint32_t)(((size_t)m * d.D + col) * 4), hn);
+          st_bf16(rhs, (uint32_t)(sw_idx(m, col, d.D) * 2), hn * rp.sc1[nt]);
+        }
+        const float sq = sum16(hn * hn);
+        if (r16 == 0 && m < d.M) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + tile) * 4), sq);
+      }
+    }
+  }
+  publish(a.flag_pair + pair, e);
+}
+
+// ------------------------------------------------------------------ the loop
+template <int DH, int MT, int KQ, int KO, int KD>
+__global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
+  const Dims& d = a.d;
+  const Bufs& bf = a.b;
+  __shared__ __attribute__((aligned(16))) char lds[40960];
+  __shared__ int lds_ok;
+  __shared__ unsigned lds_flag;
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x, x = wg & 7, c = wg >> 3;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (ld_u32_agent(a.ctl) != 0) return;  // an earlier launch aborted: the host must reset first
+  // Every hand-off is made at agent scope, so a placement other than round robin costs only
+  // L2 locality; it is recorded for the host.
+  if (tid == 0 && (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xF) != x)
+    st_u32_agent(a.ctl + 2, 0x80000000u | (unsigned)wg);
+  // lines cached by an earlier launch (same per-step buffers) must not be served
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  const int L = d.L, qd = d.Hq * DH, hpx = a.hpx;
+  const int nq_t = hpx * DH / 16, nkv_t = 2 * d.Hkv * DH / 16;   // QKV tiles of this XCD
+  const int qkv_pairs = (nq_t + nkv_t + 1) / 2;
+  const int npair = d.D / 32;                                      // residual tile pairs
+  const int gu_units = d.F / 128;                                  // gate/up tiles per XCD
+  const int QTh = (d.H + 15) / 16;
+  const int att_units = d.B * hpx * a.S;
+  const int mrg_waves = d.B * hpx * QTh * (DH / 32);
+  const uint64_t e0 = a.epoch0;
+  const uint64_t per_step = 6 * (uint64_t)L + 1;
+  auto E = [&](int k, int l, int ph) { return e0 + 1 + (uint64_t)k * per_step + 6 * (uint64_t)l + ph; };
+  auto E_out = [&](int k) { return e0 + 1 + (uint64_t)k * per_step + 6 * (uint64_t)L; };
+  uint64_t* myflag = a.flag_wg + wg;
+  const uint64_t* local_flags = a.flag_wg + x;                     // stride 8: this XCD's workgroups
+
+  // QKV tile pair pp of this XCD -> global column tiles
+  auto qkv_tile = [&](int t) { return t < nq_t ? x * nq_t + t : qd / 16 + (t - nq_t); };
+  auto qkv_rts = [&](int pp, int& rt0, int& rt1) {
+    rt0 = qkv_tile(2 * pp);
+    rt1 = 2 * pp + 1 < nq_t + nkv_t ? qkv_tile(2 * pp + 1) : -1;
+  };
+  WFr<KQ> wq;   // QKV or gate/up weights of the next unit
+  WFr<KO> wo;
+  WFr<KD> wd;
+  KVPre<DH> kvp;
+  bool kvp_valid = false;
+  float cq[2];  // norm-folded bias of the QKV unit's two tiles at this lane's column (or gate, up)
+  ResidPre ro, rd;
+  const int r16 = tid & 15;
+  // weights and the static epilogue operands of this workgroup's first QKV unit of (k, l)
+  auto pre_qkv = [&](int k, int l) {
+    if (c < qkv_pairs) {
+      int rt0, rt1;
+      qkv_rts(c, rt0, rt1);
+      load_w<KQ>(wq, static_cast<const bf16*>(bf.w_qkv) + (size_t)l * d.qkv * d.D, d.qkv, d.D, rt0, rt1, 0);
+      const float* cv = bf.cvec + (size_t)k * bf.cv_stride + (size_t)l * d.qkv;
+      cq[0] = cv[rt0 * 16 + r16];
+      cq[1] = cv[(rt1 < 0 ? rt0 : rt1) * 16 + r16];
+    }
+  };
+
+  // ---- in-projection of step 0
+  if (wg < d.M) out_row(a, wg, -1, 0, lds);
+  publish_wg(a, myflag, e0);
+  pre_qkv(0, 0);
+
+  for (int k = 0; k < d.N; ++k) {
+    for (int l = 0; l < L; ++l) {
+      char* blk = a.act + ((size_t)k * L + l) * a.kl_bytes;
+      // ---------------- QKV (+ the chunk's K/V into the cache)
+      {
+        const uint64_t e = E(k, l, 0);
+        bool ok = l == 0 ? wait_flags(a, a.flag_wg, 1, d.M, k == 0 ? e0 : E_out(k - 1), &lds_ok)
+                         : wait_flags(a, a.flag_pair, 1, npair, E(k, l - 1, 5), &lds_ok);
+        if (!ok) return;
+        const float* cv = bf.cvec + (size_t)k * bf.cv_stride + (size_t)l * d.qkv;
+        const bf16* W = static_cast<const bf16*>(bf.w_qkv) + (size_t)l * d.qkv * d.D;
+        for (int pp = c; pp < qkv_pairs; pp += 32) {
+          int rt[2];
+          qkv_rts(pp, rt[0], rt[1]);
+          if (pp != c) {
+            load_w<KQ>(wq, W, d.qkv, d.D, rt[0], rt[1], 0);
+            cq[0] = cv[rt[0] * 16 + r16];
+            cq[1] = cv[(rt[1] < 0 ? rt[0] : rt[1]) * 16 + r16];
+          }
+          f32x4 tot[2];
+          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsa), d.D, 0,
+                                  reinterpret_cast<const float*>(blk + a.o_ssqa), tot, lds, (int)(e - e0));
+          const float* rinv_s = reinterpret_cast<const float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
+          if (w < MT) {
+            const int lane = tid & 63, grp = lane >> 4;
+            const __amdgpu_buffer_rsrc_t rq = rsrc(blk + a.o_q, (uint32_t)(64 * qd * 2));
+            const uint32_t cache_bytes = (uint32_t)((size_t)d.B * d.Lc * d.Hkv * d.KS * DH * 2);
+            const __amdgpu_buffer_rsrc_t rkc = rsrc(bf.kc, cache_bytes), rvt = rsrc(bf.vt, cache_bytes);
+            const int kd = d.Hkv * DH;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              if (rt[nt] < 0) continue;
+              const int col = rt[nt] * 16 + r16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int m = w * 16 + grp * 4 + i;
+                if (m >= d.M) continue;
+                const float y = rinv_s[m] * tot[nt][i] + cq[nt];
+                const int b = m / d.H, t = m - b * d.H;
+                if (col < qd) {
+                  st_bf16(rq, (uint32_t)(((size_t)m * qd + col) * 2), y);
+                } else if (col < qd + kd) {
+                  const int r = (col - qd) / DH, dd = (col - qd) % DH;
+                  st_bf16(rkc, (uint32_t)((((((size_t)b * d.Lc + l) * d.Hkv + r) * d.KS + d.P + t) * DH + dd) * 2), y);
+                } else {
+                  const int r = (col - qd - kd) / DH, dd = (col - qd - kd) % DH;
+                  st_bf16(rvt, (uint32_t)((((((size_t)b * d.Lc + l) * d.Hkv + r) * DH + dd) * d.KS + d.P + t) * 2), y);
+                }
+              }
+            }
+          }
+          __syncthreads();  // LDS (partials, rinv) reused by the next unit
+        }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+        // the first block of this workgroup's attention unit, when it holds prefix rows only
+        kvp_valid = false;
+        if (c < att_units) {
+          const int s = c % a.S, hl = (c / a.S) % hpx, b = c / a.S / hpx;
+          const int head = x * hpx + hl;
+          if ((s * a.bps + 1) * 32 <= d.P) {
+            kv_load<DH>(a, kvp, b, l, head / (d.Hq / d.Hkv), s * a.bps, false);
+            kvp_valid = true;
+          }
+        }
+      }
+      // ---------------- attention over the cached prefix and the chunk
+      {
+        const uint64_t e = E(k, l, 1);
+        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 0), &lds_ok)) return;
+        for (int u = c; u < att_units; u += 32) {
+          const int s = u % a.S, hl = (u / a.S) % hpx, b = u / a.S / hpx;
+          attn_unit<DH>(a, blk, k, l, b, x * hpx + hl, s, kvp, kvp_valid && u == c, lds);
+          __syncthreads();
+        }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+        // output projection: weights of tile pair c over this XCD's heads, the next norm's scale
+        if (c < npair) {
+          load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * c, 2 * c + 1,
+                     x * hpx * DH / 32);
+          resid_pre_static(ro, bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D, c);
+        }
+      }
+      // ---------------- merge of the key splits
+      {
+        const uint64_t e = E(k, l, 2);
+        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 1), &lds_ok)) return;
+        if (a.S > 1)
+          for (int iw = c * 4 + w; iw < mrg_waves; iw += 128) {
+            const int u = iw % (DH / 32), jt = (iw / (DH / 32)) % QTh, hl = iw / (DH / 32) / QTh % hpx;
+            const int b = iw / (DH / 32) / QTh / hpx;
+            merge_wave<DH>(a, blk, b, x * hpx + hl, jt, u);
+          }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+      }
+      // ---------------- output projection (this XCD's heads) + residual across XCDs
+      {
+        const uint64_t e = E(k, l, 3);
+        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 2), &lds_ok)) return;
+        const float* scale_next = bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D;
+        for (int pp = c; pp < npair; pp += 32) {
+          const bool red = (pp & 7) == x;
+          if (pp != c) {
+            load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * pp, 2 * pp + 1,
+                       x * hpx * DH / 32);
+            resid_pre_static(ro, scale_next, pp);
+          }
+          resid_pre_h<MT>(a, ro, pp);
+          f32x4 tot[2];
+          gemm_unit<MT, KO, false>(d, wo, reinterpret_cast<const bf16*>(blk + a.o_o), qd, x * hpx * DH / 32, nullptr,
+                                   tot, lds, (int)(e - e0));
+          resid_split<MT>(a, pp, x, tot, blk + a.o_hsm, blk + a.o_ssqm, e, &lds_flag, ro);
+          __syncthreads();
+        }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+        if (c < gu_units) {
+          const int j = x * gu_units + c;  // gate tile j, up tile F/16 + j
+          load_w<KQ>(wq, static_cast<const bf16*>(bf.w_gu) + (size_t)l * 2 * d.F * d.D, 2 * d.F, d.D, j, d.F / 16 + j, 0);
+          const float* cv = bf.cvec + (size_t)k * bf.cv_stride + bf.cv_gu_off + (size_t)l * 2 * d.F;
+          cq[0] = cv[j * 16 + r16];
+          cq[1] = cv[d.F + j * 16 + r16];
+        }
+      }
+      // ---------------- gate/up + GeGLU (this XCD's MLP columns)
+      {
+        const uint64_t e = E(k, l, 4);
+        if (!wait_flags(a, a.flag_pair, 1, npair, E(k, l, 3), &lds_ok)) return;
+        const float* cv = bf.cvec + (size_t)k * bf.cv_stride + bf.cv_gu_off + (size_t)l * 2 * d.F;
+        const __amdgpu_buffer_rsrc_t ract = rsrc(blk + a.o_act, (uint32_t)(64 * d.F * 2));
+        for (int u = c; u < gu_units; u += 32) {
+          const int j = x * gu_units + u;
+          if (u != c) {
+            load_w<KQ>(wq, static_cast<const bf16*>(bf.w_gu) + (size_t)l * 2 * d.F * d.D, 2 * d.F, d.D, j, d.F / 16 + j,
+                       0);
+            cq[0] = cv[j * 16 + r16];
+            cq[1] = cv[d.F + j * 16 + r16];
+          }
+          f32x4 tot[2];
+          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsm), d.D, 0,
+                                  reinterpret_cast<const float*>(blk + a.o_ssqm), tot, lds, (int)(e - e0));
+          const float* rinv_s = reinterpret_cast<const float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
+          if (w < MT) {
+            const int grp = (tid & 63) >> 4;
+            const int f = j * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = w * 16 + grp * 4 + i;
+              if (m >= d.M) continue;
+              const float yg = rinv_s[m] * tot[0][i] + cq[0], yu = rinv_s[m] * tot[1][i] + cq[1];
+              st_bf16(ract, (uint32_t)(sw_idx(m, f, d.F) * 2), gelu_tanh(yg) * yu);
+            }
+          }
+          __syncthreads();
+        }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+        if (c < npair) {
+          load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * c, 2 * c + 1,
+                     x * (d.F / 256));
+          const int jn = (l + 1 < L) ? 2 * (l + 1) : 2 * L;
+          resid_pre_static(rd, bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D, c);
+        }
+      }
+      // ---------------- down projection (this XCD's MLP columns) + residual across XCDs
+      {
+        const uint64_t e = E(k, l, 5);
+        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 4), &lds_ok)) return;
+        const int jn = (l + 1 < L) ? 2 * (l + 1) : 2 * L;
+        const float* scale_next = bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D;
+        char* nblk = l + 1 < L ? a.act + ((size_t)k * L + l + 1) * a.kl_bytes : nullptr;
+        char* fin = a.fin + (size_t)k * a.k_bytes;
+        char* hs_next = nblk ? nblk + a.o_hsa : fin + a.o_hsf;
+        char* ssq_next = nblk ? nblk + a.o_ssqa : fin + a.o_ssqf;
+        for (int pp = c; pp < npair; pp += 32) {
+          const bool red = (pp & 7) == x;
+          if (pp != c) {
+            load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * pp, 2 * pp + 1,
+                       x * (d.F / 256));
+            resid_pre_static(rd, scale_next, pp);
+          }
+          resid_pre_h<MT>(a, rd, pp);
+          f32x4 tot[2];
+          gemm_unit<MT, KD, false>(d, wd, reinterpret_cast<const bf16*>(blk + a.o_act), d.F, x * (d.F / 256), nullptr,
+                                   tot, lds, (int)(e - e0));
+          resid_split<MT>(a, pp, x, tot, hs_next, ssq_next, e, &lds_flag, rd);
+          __syncthreads();
+        }
+        PTRACE((int)(e - e0), 5);
+        publish_wg(a, myflag, e);
+        if (l + 1 < L) pre_qkv(k, l + 1);
+      }
+    }
+    // ---------------- final norm, out-projection, Euler update, next in-projection
+    {
+      const uint64_t e = E_out(k);
+      if (!wait_flags(a, a.flag_pair, 1, npair, E(k, L - 1, 5), &lds_ok)) return;
+      if (wg < d.M) out_row(a, wg, k, k + 1 < d.N ? k + 1 : -1, lds);
+      PTRACE((int)(e - e0), 5);
+      publish_wg(a, myflag, e);
+      if (k + 1 < d.N) pre_qkv(k + 1, 0);
+    }
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host side
+bool persistent_supported(const Dims& d, WDtype wt) {
+  if (wt != W_BF16 || d.joint || d.M > 64 || d.rope_theta > 0.f || d.gated) return false;
+  if (d.Hq % 8 || d.Hq % d.Hkv) return false;
+  const int hpx = d.Hq / 8;
+  if ((hpx * d.dh) % 128 || d.D % 256 || d.F % 1024 || d.A > 256) return false;
+  const int MT = (d.M + 15) / 16;
+  const int KQ = d.D / 128, KO = hpx * d.dh / 128, KD = d.F / 1024;
+  if (d.dh == 256 && MT == 4 && KQ == 8 && KO == 2 && KD == 4) return true;   // pi0.5-shaped expert
+  if (d.dh == 128 && KQ == 2 && KO == 1 && KD == 1) return true;              // small test shapes, any MT
+  return false;
+}
+
+PersistLayout persistent_layout(const Dims& d) {
+  PersistLayout p{};
+  auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t qd = (size_t)d.Hq * d.dh;
+  size_t off = 0;
+  p.o_hsa = off; off = a256(off + 64 * d.D * 2);
+  p.o_ssqa = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.o_q = off; off = a256(off + 64 * qd * 2);
+  p.o_o = off; off = a256(off + 64 * qd * 2);
+  p.o_hsm = off; off = a256(off + 64 * d.D * 2);
+  p.o_ssqm = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.o_act = off; off = a256(off + 64 * (size_t)d.F * 2);
+  p.kl_bytes = off;
+  off = 0;
+  p.o_hsf = off; off = a256(off + 64 * d.D * 2);
+  p.o_ssqf = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.k_bytes = off;
+  return p;
+}
+
+// Key splits of the attention (sample, head) units: as many one-block splits as the XCD's
+// 32 workgroups hold (a merge of up to 32 partials), else longer splits.
+static void attn_split(const Dims& d, int hpx, int& S, int& bps) {
+  const int nblk = (d.P + d.H + 31) / 32;
+  const int per = std::max(1, 32 / std::max(1, d.B * hpx));
+  S = std::min(nblk, std::min(per, 32));
+  bps = (nblk + S - 1) / S;
+  S = (nblk + bps - 1) / bps;
+}
+
+size_t persistent_part_floats(const Dims& d) { return (size_t)(d.D / 32) * 8 * 2 * 4 * 4 * 64 * 2; }
+
+size_t persistent_attn_floats(const Dims& d) {
+  int S, bps;
+  attn_split(d, d.Hq / 8, S, bps);
+  const size_t items = (size_t)d.B * d.Hq * ((d.H + 15) / 16);
+  return items * S * ((size_t)(d.dh / 32) * 256 + 32);
+}
+
+hipError_t enqueue_denoise_persistent(const Dims& d, const Bufs& b, const PersistBufs& pb, uint64_t epoch0,
+                                      hipStream_t st) {
+  if (!persistent_supported(d, W_BF16)) return hipErrorInvalidValue;
+  PArgs a{};
+  a.d = d;
+  a.b = b;
+  const PersistLayout lay = persistent_layout(d);
+  a.act = pb.act;
+  a.kl_bytes = (uint32_t)lay.kl_bytes;
+  a.o_hsa = (uint32_t)lay.o_hsa; a.o_ssqa = (uint32_t)lay.o_ssqa; a.o_q = (uint32_t)lay.o_q; a.o_o = (uint32_t)lay.o_o;
+  a.o_hsm = (uint32_t)lay.o_hsm; a.o_ssqm = (uint32_t)lay.o_ssqm; a.o_act = (uint32_t)lay.o_act;
+  a.fin = pb.fin;
+  a.k_bytes = (uint32_t)lay.k_bytes; a.o_hsf = (uint32_t)lay.o_hsf; a.o_ssqf = (uint32_t)lay.o_ssqf;
+  a.flag_wg = pb.flag_wg;
+  a.flag_pair = pb.flag_pair;
+  a.cnt = pb.cnt;
+  a.ctl = pb.ctl;
+  a.part = pb.part;
+  a.attn_ws = pb.attn_ws;
+  a.epoch0 = epoch0;
+  a.hpx = d.Hq / 8;
+  attn_split(d, a.hpx, a.S, a.bps);
+  if (a.S > 32) return hipErrorInvalidValue;
+  void* args[] = {&a};
+  const int MT = (d.M + 15) / 16;
+  const void* fn = nullptr;
+  if (d.dh == 256) fn = reinterpret_cast<const void*>(&k_loop_persistent<256, 4, 8, 2, 4>);
+  else if (MT == 1) fn = reinterpret_cast<const void*>(&k_loop_persistent<128, 1, 2, 1, 1>);
+  else if (MT == 2) fn = reinterpret_cast<const void*>(&k_loop_persistent<128, 2, 2, 1, 1>);
+  else if (MT == 3) fn = reinterpret_cast<const void*>(&k_loop_persistent<128, 3, 2, 1, 1>);
+  else fn = reinterpret_cast<const void*>(&k_loop_persistent<128, 4, 2, 1, 1>);
+  return hipLaunchCooperativeKernel(fn, dim3(kPersistWGs), dim3(256), args, 0, st);
+}
+
+uint64_t persistent_phases(const Dims& d) { return 1 + (uint64_t)d.N * (6 * (uint64_t)d.L + 1); }
+
+}  // namespace phyai
+
+#ifdef PHYAI_PHASE_TRACE
+// Trace build only: copy the persistent loop's phase timestamps out (host dst of
+// 256 * 4096 * 6 uint64: per workgroup and phase, wait begin, wait end, publish, products done,
+// cross-wave sum done, epilogue issued), then clear.
+extern "C" int phyai_persist_trace(void* host_dst) {
+  static uint64_t zeros[256 * phyai::kTracePhases * 6];
+  if (hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(phyai::g_ptrace), sizeof(zeros), 0, hipMemcpyDeviceToHost) !=
+          hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(phyai::g_ptrace), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) != hipSuccess)
+    return 4;
+  return 0;
+}
+#endif

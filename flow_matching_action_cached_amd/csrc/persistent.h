@@ -1,0 +1,58 @@
+// Internal interface of the persistent Euler loop (loop_persistent.hip) for the host runtime.
+#pragma once
+
+#include "kernels.h"
+
+namespace phyai {
+
+constexpr int kPersistWGs = 256;  // one workgroup per compute unit (8 XCDs x 32)
+
+// Byte offsets of the per-(step, layer) activation block and of the per-step final block.
+struct PersistLayout {
+  size_t o_hsa, o_ssqa, o_q, o_o, o_hsm, o_ssqm, o_act, kl_bytes;  // per (step, layer)
+  size_t o_hsf, o_ssqf, k_bytes;                                     // per step (final norm input)
+};
+
+// Device buffers of the persistent loop (owned by the context, allocated with the tables).
+struct PersistBufs {
+  char* act;            // N * L activation blocks
+  char* fin;            // N final blocks
+  uint64_t* flag_wg;    // [kPersistWGs] last finished phase (epoch) of each workgroup
+  uint64_t* flag_pair;  // [D/32] last residual epilogue (epoch) of each tile pair
+  unsigned* cnt;        // [D/32] arrival counters of the residual split sums
+  unsigned* ctl;        // [0] abort word (sticky until the host resets it), [1] failing epoch, [2] placement
+  float* part;          // residual split partials
+  float* attn_ws;       // attention split partials
+};
+
+// Kernel arguments.
+struct PArgs {
+  Dims d;
+  Bufs b;
+  char* act;
+  uint32_t kl_bytes, o_hsa, o_ssqa, o_q, o_o, o_hsm, o_ssqm, o_act;
+  char* fin;
+  uint32_t k_bytes, o_hsf, o_ssqf;
+  uint64_t* flag_wg;
+  uint64_t* flag_pair;
+  unsigned* cnt;
+  unsigned* ctl;
+  float* part;
+  float* attn_ws;
+  uint64_t epoch0;  // epoch of this launch's first phase (monotonic across launches)
+  int hpx;          // query heads per XCD
+  int S, bps;       // attention key splits per (sample, head), 32-key blocks per split
+};
+
+// Shapes the persistent loop implements (bf16, <= 64 token rows, heads a multiple of 8, ...).
+bool persistent_supported(const Dims& d, WDtype wt);
+PersistLayout persistent_layout(const Dims& d);
+size_t persistent_part_floats(const Dims& d);
+size_t persistent_attn_floats(const Dims& d);
+// Phases of one launch (the host advances epoch0 by this much plus one per launch).
+uint64_t persistent_phases(const Dims& d);
+// One cooperative launch of the whole loop on `stream`; x must hold the noise.
+hipError_t enqueue_denoise_persistent(const Dims& d, const Bufs& b, const PersistBufs& pb, uint64_t epoch0,
+                                      hipStream_t stream);
+
+}  // namespace phyai

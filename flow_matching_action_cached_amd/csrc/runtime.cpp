@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "persistent.h"
 
 using namespace phyai;
 
@@ -54,6 +55,14 @@ struct phyai_ctx {
   };
   std::map<std::tuple<int, int, int>, GraphEntry> graphs;
   uint64_t graph_clock = 0;
+  // persistent loop (<= 64 token rows, bf16; off until enabled): its buffers are sized with
+  // the tables
+  int persist_enabled = 0;
+  void* pmem = nullptr;
+  PersistBufs pb{};
+  int p_steps = 0;                   // steps the buffers hold
+  uint64_t p_epoch = 1;              // first epoch of the next launch (monotonic)
+  bool p_pending = false;            // a launch ran since the last abort check
   // single-kernel repeat graphs for measurement: (which, layer, reps, batch, prefix, steps)
   std::map<std::tuple<int, int, int, int, int, int>, hipGraphExec_t> kgraphs;
 };
@@ -157,6 +166,85 @@ int graph_bucket(const phyai_ctx* c, int batch) {
   const int H = c->base.H;
   if (batch * H <= 64) return batch;
   return std::min(c->base.B, (batch + 7) / 8 * 8);
+}
+
+// Dims of a persistent launch at `batch` (nullopt-like: ok = false when unsupported).
+bool persistent_dims(const phyai_ctx* c, int batch, Dims& d) {
+  if (c->joint || !c->persist_enabled || !c->pmem || batch * c->base.H > 64) return false;
+  d = launch_dims(c, batch, c->prefix_len, c->n_steps);
+  return d.N <= c->p_steps && persistent_supported(d, c->wt);
+}
+
+void free_persistent(phyai_ctx* c) {
+  if (c->pmem) hipFree(c->pmem);
+  c->pmem = nullptr;
+  c->pb = PersistBufs{};
+  c->p_steps = 0;
+}
+
+// Buffers of the persistent loop for n_steps (kept when large enough).  Silently absent when
+// the shape is not one the persistent kernel implements or the allocation fails: the graph
+// path then runs.
+void alloc_persistent(phyai_ctx* c, int n_steps) {
+  if (!c->persist_enabled || c->joint || c->wt != W_BF16 || c->base.H > 64) return;
+  Dims d = launch_dims(c, 1, c->cfg.max_prefix_len, n_steps);
+  if (!persistent_supported(d, c->wt)) return;
+  if (c->pmem && c->p_steps >= n_steps) return;
+  free_persistent(c);
+  const PersistLayout lay = persistent_layout(d);
+  size_t attn_f = 0;
+  for (int b = 1; b <= c->base.B && b * d.H <= 64; ++b) {  // every batch the path may run
+    Dims db = launch_dims(c, b, c->cfg.max_prefix_len, n_steps);
+    attn_f = std::max(attn_f, persistent_attn_floats(db));
+  }
+  Layout pl;
+  const size_t o_act = pl.take(lay.kl_bytes * (size_t)n_steps * d.L);
+  const size_t o_fin = pl.take(lay.k_bytes * (size_t)n_steps);
+  const size_t o_fw = pl.take(kPersistWGs * 8), o_fp = pl.take((size_t)(d.D / 32) * 8);
+  const size_t o_cnt = pl.take((size_t)(d.D / 32) * 4), o_ctl = pl.take(16);
+  const size_t o_part = pl.take(persistent_part_floats(d) * 4), o_attn = pl.take(attn_f * 4);
+  if (hipMalloc(&c->pmem, pl.off) != hipSuccess) {
+    c->pmem = nullptr;
+    return;
+  }
+  // zero: padding rows of the activation blocks stay zero; flags start below every epoch
+  if (hipMemsetAsync(c->pmem, 0, pl.off, c->stream) != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess) {
+    free_persistent(c);
+    return;
+  }
+  char* base = static_cast<char*>(c->pmem);
+  c->pb.act = base + o_act;
+  c->pb.fin = base + o_fin;
+  c->pb.flag_wg = reinterpret_cast<uint64_t*>(base + o_fw);
+  c->pb.flag_pair = reinterpret_cast<uint64_t*>(base + o_fp);
+  c->pb.cnt = reinterpret_cast<unsigned*>(base + o_cnt);
+  c->pb.ctl = reinterpret_cast<unsigned*>(base + o_ctl);
+  c->pb.part = reinterpret_cast<float*>(base + o_part);
+  c->pb.attn_ws = reinterpret_cast<float*>(base + o_attn);
+  c->p_steps = n_steps;
+  c->p_epoch = 1;
+}
+
+// After the stream has drained: a persistent launch that gave up on a wait left the abort
+// word set (and every later launch returned at once).  Report it and reset the flags.
+phyai_status check_persistent(phyai_ctx* c) {
+  if (!c->pmem || !c->p_pending) return PHYAI_OK;
+  c->p_pending = false;
+  unsigned ctl[3] = {0, 0, 0};
+  HIPCHK(c, hipMemcpy(ctl, c->pb.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  if (ctl[0] == 0) return PHYAI_OK;
+  const Dims d = launch_dims(c, 1, c->cfg.max_prefix_len, c->p_steps);
+  HIPCHK(c, hipMemset(c->pb.flag_wg, 0, kPersistWGs * 8));
+  HIPCHK(c, hipMemset(c->pb.flag_pair, 0, (size_t)(d.D / 32) * 8));
+  HIPCHK(c, hipMemset(c->pb.cnt, 0, (size_t)(d.D / 32) * 4));
+  HIPCHK(c, hipMemset(c->pb.ctl, 0, 16));
+  c->p_epoch = 1;
+  char msg[160];
+  std::snprintf(msg, sizeof(msg),
+                "persistent loop aborted: a hand-off wait exceeded its bound (phase %u of the launch); "
+                "its output is invalid",
+                ctl[1]);
+  return fail(c, PHYAI_ERR_DEVICE, msg);
 }
 
 // ---------------------------------------------------------------- UniPC step weights
@@ -602,6 +690,11 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* c, const float* t_host, int n_
   HIPCHK(c, enqueue_tables(d, c->b, c->wt, c->t_dev, c->e_dev, mod, cvec, gate, c->stream));
   // host buffers above must outlive the async copies
   HIPCHK(c, hipStreamSynchronize(c->stream));
+  {
+    const phyai_status ps = check_persistent(c);  // (buffers are replaced only when the stream is idle)
+    if (ps != PHYAI_OK) return ps;
+  }
+  alloc_persistent(c, n_steps);
   c->n_steps = n_steps;
   c->have_tables = true;
   return PHYAI_OK;
@@ -633,6 +726,19 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
   const size_t xbytes = (size_t)batch * d.H * d.A * 4, xbucket = (size_t)d.M * d.A * 4;
   HIPCHK(c, hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream));
   if (xbucket > xbytes) HIPCHK(c, enqueue_zero_f32(c->b.x + xbytes / 4, (xbucket - xbytes) / 4, c->stream));
+  Dims dp;
+  if (persistent_dims(c, bucket, dp)) {  // the whole loop as one persistent kernel
+    const hipError_t e = enqueue_denoise_persistent(dp, c->b, c->pb, c->p_epoch, c->stream);
+    if (e == hipSuccess) {
+      c->p_epoch += persistent_phases(dp) + 1;
+      c->p_pending = true;
+      HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
+      return PHYAI_OK;
+    }
+    // a cooperative launch that the device cannot hold: use the graph path from now on
+    (void)hipGetLastError();
+    c->persist_enabled = 0;
+  }
   const phyai_status st = run_loop(c, d, plan, "denoise");
   if (st != PHYAI_OK) return st;
   HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
@@ -811,7 +917,25 @@ phyai_status phyai_sync(phyai_ctx* c) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   HIPCHK(c, hipStreamSynchronize(c->stream));
   HIPCHK(c, hipGetLastError());
+  return check_persistent(c);
+}
+
+phyai_status phyai_set_persistent(phyai_ctx* c, int enable) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  c->persist_enabled = enable ? 1 : 0;
+  if (c->persist_enabled && c->have_tables && !c->pmem) {
+    // buffers for the installed tables; replaced only once the stream is idle
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    alloc_persistent(c, c->n_steps);
+  }
   return PHYAI_OK;
+}
+
+int phyai_loop_form(const phyai_ctx* c, int batch) {
+  if (!c || c->joint || !c->have_prefix || !c->have_tables || batch < 1 || batch > c->batch) return -1;
+  Dims d;
+  return persistent_dims(c, graph_bucket(c, batch), d) ? 1 : 0;
 }
 
 phyai_status phyai_get_modulation(phyai_ctx* c, float* dst) {
@@ -828,6 +952,7 @@ void phyai_destroy(phyai_ctx* c) {
   if (!c) return;
   hipStreamSynchronize(c->stream);
   drop_graphs(c);
+  free_persistent(c);
   if (c->tab) hipFree(c->tab);
   if (c->arena) hipFree(c->arena);
   if (c->cap_stream) hipStreamDestroy(c->cap_stream);

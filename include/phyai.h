@@ -222,6 +222,25 @@ phyai_status phyai_denoise(phyai_ctx* ctx, const float* noise, int batch, int n_
  * Both run the same kernels in the same order and give bitwise identical results. */
 phyai_status phyai_set_graph_mode(phyai_ctx* ctx, int use_graph);
 
+/* Persistent loop (page "FlashRT-PAI speeds physical AI inference up to 12.66x": deep kernel
+ * fusion with launch overlap).  For batches of at most 64 token rows with bf16 weights and a
+ * supported shape (n_q_heads a multiple of 8, (n_q_heads/8)*head_dim a multiple of 128, width
+ * a multiple of 256, mlp_dim of 1024, no rotary positions or residual gates; implemented for
+ * the pi0.5-shaped expert and head_dim 128 / width 256 / mlp_dim 1024 test shapes), the whole
+ * N-step loop runs as one cooperative launch of 256 co-resident workgroups that hand each
+ * phase's results to the next through flags in device memory; every other call runs the
+ * graph of per-layer launches.  enable = 1 uses it where supported, 0 (default) never.  The
+ * persistent launch cannot be captured into a caller's graph: leave it disabled for capture.
+ * Its buffers (about 1.3 MB per step and layer for the pi0.5 shape) are allocated with the
+ * timestep tables, or by this call when the tables are already set (the call then waits for
+ * the context stream); without them the graph path runs.  A wait that exceeds its bound
+ * aborts the launch; phyai_sync then reports PHYAI_ERR_DEVICE and resets the loop's flags. */
+phyai_status phyai_set_persistent(phyai_ctx* ctx, int enable);
+
+/* Which form a phyai_denoise of `batch` samples would run now: 1 the persistent kernel, 0 the
+ * graph (or eager) launches, -1 not runnable (prefix or tables missing, bad batch, NULL). */
+int phyai_loop_form(const phyai_ctx* ctx, int batch);
+
 /* Wait for the context stream; reports asynchronous device errors (DEVICE, with the
  * HIP message in phyai_last_error).  The reading of the pages' request life cycle
  * (PhyAI reading Sec. 5.4: a request ends when its action chunk is ready) is this call:
