@@ -21,8 +21,9 @@
 // Hand-offs.  A workgroup publishes a monotonic epoch flag when it has finished a phase (all
 // its stores performed); a consumer polls exactly the flags of what it reads: its XCD's 32
 // workgroups, the tile pairs of a residual sum, or the token rows of the out-projection.  The
-// last of the 8 partial sums of a residual tile pair to arrive adds them in XCD order and
-// writes the residual, the next norm's input and its statistics.  Every wait is bounded: on
+// 8 partial sums of a residual tile pair travel as (value, epoch tag) words to the pair's
+// reducer, which adds them in XCD order and writes the residual, the next norm's input and
+// its statistics.  Every wait is bounded: on
 // overrun a sticky abort word is set, every workgroup leaves at its next wait, and the host
 // reports a device error.
 //
@@ -106,12 +107,14 @@ __device__ __forceinline__ bf16x8 bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t 
 // Lanes of wave 0 poll flags base[i * stride] (i < n) until each reaches epoch e; every wave
 // then meets at the workgroup barrier.  False once the loop is aborted (by this wait's
 // overrun or by another workgroup): the caller leaves the kernel.
-__device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int n, uint64_t e, int* lds_ok) {
+__device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int n, uint64_t e, int* lds_ok,
+                           int skip = -1) {
   const int tid = threadIdx.x;
   PTRACE((int)(e - a.epoch0) + 1, 0);
   if (tid < 64) {
     int ok = 1;
     for (int i = tid; i < n && ok; i += 64) {
+      if (i == skip) continue;
       const uint64_t* f = base + (size_t)i * stride;
       unsigned spins = 0;
       while ((int64_t)(ld_flag(f) - e) < 0) {
@@ -400,42 +403,75 @@ __device__ void attn_unit(const PArgs& a, const char* blk_kl, int k, int l, int 
   }
 }
 
-// Merge of the key splits, one wave per (sample, head, query tile, 16-byte slot u): weights
-// 2^(m_s - M) l_s in split order, output columns 32 u + 16 t + 4 grp + i of the head.
+// Merge of the key splits, one workgroup per (sample, head, query tile, 16-byte slot u):
+// wave w merges splits [8 w, 8 w + 8) with weights 2^(m_s - M_w) l_s (few values in flight
+// per lane, so every load of a wave is issued before the first is used), then wave 0
+// combines the four partial merges with weights 2^(M_w - M).  Output columns
+// 32 u + 16 t + 4 grp + i of the head.
 template <int DH>
-__device__ void merge_wave(const PArgs& a, const char* blk_kl, int b, int head, int jt, int u) {
+__device__ void merge_wg(const PArgs& a, const char* blk_kl, int b, int head, int jt, int u, char* lds) {
   const Dims& d = a.d;
-  constexpr int PAY = DH / 32, SM = 32;
+  constexpr int PAY = DH / 32, SW = 8;
   constexpr uint32_t STRIDE = PAY * 1024 + 128;
-  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int QTh = (d.H + 15) / 16, S = a.S, qd = d.Hq * DH;
   const int tok = jt * 16 + r16;
   const size_t item = ((size_t)b * d.Hq + head) * QTh + jt;
   const __amdgpu_buffer_rsrc_t ws = rsrc(a.attn_ws + item * S * (STRIDE / 4), STRIDE * S);
-  float ms[SM], ls[SM];
-  u32x4 pv[SM];
+  float ms[SW], ls[SW];
+  u32x4 pv[SW];
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2) {  // every split's statistics and payload in one round trip
-    const uint32_t sp = (uint32_t)min(s2, S - 1) * STRIDE;
-    ms[s2] = ld_f32_sc1(ws, sp + PAY * 1024 + r16 * 4);
-    ls[s2] = ld_f32_sc1(ws, sp + PAY * 1024 + 64 + r16 * 4);
-    pv[s2] = ld_16_sc1(ws, sp + (u * 64 + lane) * 16);
+  for (int i = 0; i < SW; ++i) {
+    const uint32_t sp = (uint32_t)min(w * SW + i, S - 1) * STRIDE;
+    ms[i] = ld_f32_sc1(ws, sp + PAY * 1024 + r16 * 4);
+    ls[i] = ld_f32_sc1(ws, sp + PAY * 1024 + 64 + r16 * 4);
+    pv[i] = ld_16_sc1(ws, sp + (u * 64 + lane) * 16);
   }
-  float M = -INFINITY;
+  float Mw = -INFINITY;
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2)
-    if (s2 < S) M = fmaxf(M, ms[s2]);
+  for (int i = 0; i < SW; ++i)
+    if (w * SW + i < S) Mw = fmaxf(Mw, ms[i]);
   float den = 0.f;
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2) {
-    const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+  for (int i = 0; i < SW; ++i) {
+    const float wgt = w * SW + i < S ? exp2f(ms[i] - Mw) * ls[i] : 0.f;
     den += wgt;
-    const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2]);
+    const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[i]);
     acc[0] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
     acc[1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
   }
-  if (tok >= d.H) return;
+  // partial merges of waves 1..3 to LDS: [wave][10][64] floats (M_w, den_w, 8 sums)
+  float* pm = reinterpret_cast<float*>(lds);
+  if (w > 0) {
+    float* q = pm + (size_t)(w - 1) * 10 * 64 + lane;
+    q[0] = Mw;
+    q[64] = den;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[(2 + 4 * t + i) * 64] = acc[t][i];
+  }
+  __syncthreads();
+  if (w != 0 || tok >= d.H) return;
+  float M = Mw;
+#pragma unroll
+  for (int v = 1; v < 4; ++v) M = fmaxf(M, pm[(v - 1) * 640 + lane]);
+  const float c0 = exp2f(Mw - M);
+  den *= c0;
+  acc[0] *= c0;
+  acc[1] *= c0;
+#pragma unroll
+  for (int v = 1; v < 4; ++v) {
+    const float* q = pm + (v - 1) * 640 + lane;
+    const float cv = q[0] == -INFINITY ? 0.f : exp2f(q[0] - M);
+    den += cv * q[64];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] += cv * q[(2 + 4 * t + i) * 64];
+  }
   const int m = b * d.H + tok;
   const float inv = 1.0f / den;
   const __amdgpu_buffer_rsrc_t ro = rsrc(blk_kl + a.o_o, (uint32_t)(64 * qd * 2));
@@ -613,9 +649,13 @@ __device__ bool resid_sum(const PArgs& a, int pair, int x, const f32x4 (&tot)[2]
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, tot[nt][i]), tag}, rl,
+        for (int i = 0; i < 4; ++i) {
+          // (the element is copied out first: a bit cast of a vector element lvalue read
+          // element 0 for every i in this compiler)
+          const float tv = tot[nt][i];
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(tv), tag}, rl,
                                                 (uint32_t)(ll_index(pair, x, nt, w, i, lane) * 8), 0, kSC1);
+        }
     return true;
   }
   int ok = 1;
@@ -623,20 +663,29 @@ __device__ bool resid_sum(const PArgs& a, int pair, int x, const f32x4 (&tot)[2]
     float v[8][2][4];
     unsigned spins = 0;
     while (true) {
-      bool got = true;
+      // all 64 words in flight at once (this XCD's own slot too, ignored), then one test
+      u32x2 wd[8][2][4];
+#pragma unroll
+      for (int x2 = 0; x2 < 8; ++x2)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            wd[x2][nt][i] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)(ll_index(pair, x2, nt, w, i, lane) * 8), 0, kSC1));
+      unsigned stale = 0;
 #pragma unroll
       for (int x2 = 0; x2 < 8; ++x2)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if (x2 == rx) continue;
-            const u32x2 wd = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)(ll_index(pair, x2, nt, w, i, lane) * 8), 0, kSC1));
-            got = got && wd[1] == tag;
-            v[x2][nt][i] = __builtin_bit_cast(float, wd[0]);
+            const u32x2 wv = wd[x2][nt][i];
+            const unsigned lo = wv[0], hi = wv[1];
+            stale |= x2 == rx ? 0u : hi ^ tag;
+            v[x2][nt][i] = __uint_as_float(lo);
           }
-      if (__all(got)) break;
+      if (!__any(stale != 0)) break;
       ++spins;
       if ((spins & 63) == 0 && ld_u32_agent(a.ctl) != 0) {
         ok = 0;
@@ -683,31 +732,43 @@ __device__ bool resid_sum(const PArgs& a, int pair, int x, const f32x4 (&tot)[2]
   return true;
 }
 
+// Flagged form: each contributor stores its partial, waits for the stores to be performed
+// and raises its (pair, XCD) flag; the reducer polls the seven flags with a few lanes, then
+// loads the seven partials in one round trip.  Partial layout: [pair][x][nt][w][64] f32x4.
 template <int MT>
-__device__ void resid_split(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], char* hs_next, char* ssq_next,
-                            uint64_t e, unsigned* lds_flag, const ResidPre& rp) {
+__device__ bool resid_flagged(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp,
+                              char* hs_next, char* ssq_next, uint64_t e, int* lds_ok) {
   const Dims& d = a.d;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t part_bytes = 2 * MT * 1024;
+  constexpr uint32_t part_bytes = 2 * MT * 1024;
   const __amdgpu_buffer_rsrc_t ws = rsrc(a.part + (size_t)pair * 8 * (part_bytes / 4), part_bytes * 8);
-  if (w < MT)
+  uint64_t* pflag = a.flag_pair + d.D / 32 + pair * 8;
+  const int rx = pair & 7;
+  if (x != rx) {
+    if (w < MT)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      st_16_sc1(ws, x * part_bytes + ((nt * MT + w) * 64 + lane) * 16, __builtin_bit_cast(u32x4, tot[nt]));
-  if (!split_arrive_wg(a.cnt + pair, 8u, lds_flag)) return;
+      for (int nt = 0; nt < 2; ++nt)
+        st_16_sc1(ws, x * part_bytes + ((nt * MT + w) * 64 + lane) * 16, __builtin_bit_cast(u32x4, tot[nt]));
+    publish(pflag + x, e);
+    return true;
+  }
+  // the seven other partials of this pair
+  if (!wait_flags(a, pflag, 1, 8, e, lds_ok, rx)) return false;
   if (w < MT) {
     const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
     const __amdgpu_buffer_rsrc_t rhs = rsrc(hs_next, (uint32_t)(64 * d.D * 2));
     const __amdgpu_buffer_rsrc_t rss = rsrc(ssq_next, (uint32_t)(64 * (d.D / 16) * 4));
+    u32x4 pv[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int x2 = 0; x2 < 8; ++x2) pv[nt][x2] = ld_16_sc1(ws, x2 * part_bytes + ((nt * MT + w) * 64 + lane) * 16);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      u32x4 pv[8];
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) pv[s2] = ld_16_sc1(ws, s2 * part_bytes + ((nt * MT + w) * 64 + lane) * 16);
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) sum += __builtin_bit_cast(f32x4, pv[s2]);
+      for (int x2 = 0; x2 < 8; ++x2) sum += x2 == rx ? tot[nt] : __builtin_bit_cast(f32x4, pv[nt][x2]);
       const int tile = 2 * pair + nt, col = tile * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -724,6 +785,7 @@ __device__ void resid_split(const PArgs& a, int pair, int x, const f32x4 (&tot)[
     }
   }
   publish(a.flag_pair + pair, e);
+  return true;
 }
 
 // ------------------------------------------------------------------ the loop
@@ -733,7 +795,6 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
   const Bufs& bf = a.b;
   __shared__ __attribute__((aligned(16))) char lds[40960];
   __shared__ int lds_ok;
-  __shared__ unsigned lds_flag;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, x = wg & 7, c = wg >> 3;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -752,7 +813,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
   const int gu_units = d.F / 128;                                  // gate/up tiles per XCD
   const int QTh = (d.H + 15) / 16;
   const int att_units = d.B * hpx * a.S;
-  const int mrg_waves = d.B * hpx * QTh * (DH / 32);
+  const int mrg_items = d.B * hpx * QTh * (DH / 32);
   const uint64_t e0 = a.epoch0;
   const uint64_t per_step = 6 * (uint64_t)L + 1;
   auto E = [&](int k, int l, int ph) { return e0 + 1 + (uint64_t)k * per_step + 6 * (uint64_t)l + ph; };
@@ -816,28 +877,45 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           const float* rinv_s = reinterpret_cast<const float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
           if (w < MT) {
             const int lane = tid & 63, grp = lane >> 4;
-            const __amdgpu_buffer_rsrc_t rq = rsrc(blk + a.o_q, (uint32_t)(64 * qd * 2));
-            const uint32_t cache_bytes = (uint32_t)((size_t)d.B * d.Lc * d.Hkv * d.KS * DH * 2);
-            const __amdgpu_buffer_rsrc_t rkc = rsrc(bf.kc, cache_bytes), rvt = rsrc(bf.vt, cache_bytes);
             const int kd = d.Hkv * DH;
+            // row m0 + i of this lane: sample b, chunk token t (32-bit offsets: the cache
+            // resources are below 4 GB)
+            const int m0 = w * 16 + grp * 4;
+            int b0 = m0 / d.H;
+            const int t0 = m0 - b0 * d.H;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               if (rt[nt] < 0) continue;
-              const int col = rt[nt] * 16 + r16;
+              const int c0 = rt[nt] * 16;  // the tile lies in one of q, k, v (uniform)
+              const int col = c0 + r16;
+              __amdgpu_buffer_rsrc_t rdst;
+              uint32_t base, rstride, bstride;  // byte offset of (b, t): base + b bstride + t rstride
+              if (c0 < qd) {
+                rdst = rsrc(blk + a.o_q, (uint32_t)(64 * qd * 2));
+                base = (uint32_t)col * 2;
+                rstride = (uint32_t)qd * 2;
+                bstride = (uint32_t)(d.H * qd * 2);
+              } else {
+                const uint32_t cache_bytes = (uint32_t)((size_t)d.B * d.Lc * d.Hkv * d.KS * DH * 2);
+                const bool isk = c0 < qd + kd;
+                const int cc = col - qd - (isk ? 0 : kd), r = cc / DH, dd = cc % DH;
+                rdst = rsrc(isk ? bf.kc : bf.vt, cache_bytes);
+                const uint32_t head_off = (uint32_t)(((l * d.Hkv + r) * d.KS) * DH) * 2;
+                base = head_off + (uint32_t)(isk ? (d.P * DH + dd) : (dd * d.KS + d.P)) * 2;
+                rstride = (uint32_t)(isk ? DH : 1) * 2;
+                bstride = (uint32_t)(d.Lc * d.Hkv * d.KS * DH) * 2;
+              }
+              int b = b0, t = t0;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int m = w * 16 + grp * 4 + i;
-                if (m >= d.M) continue;
-                const float y = rinv_s[m] * tot[nt][i] + cq[nt];
-                const int b = m / d.H, t = m - b * d.H;
-                if (col < qd) {
-                  st_bf16(rq, (uint32_t)(((size_t)m * qd + col) * 2), y);
-                } else if (col < qd + kd) {
-                  const int r = (col - qd) / DH, dd = (col - qd) % DH;
-                  st_bf16(rkc, (uint32_t)((((((size_t)b * d.Lc + l) * d.Hkv + r) * d.KS + d.P + t) * DH + dd) * 2), y);
-                } else {
-                  const int r = (col - qd - kd) / DH, dd = (col - qd - kd) % DH;
-                  st_bf16(rvt, (uint32_t)((((((size_t)b * d.Lc + l) * d.Hkv + r) * DH + dd) * d.KS + d.P + t) * 2), y);
+                const int m = m0 + i;
+                if (m < d.M) {
+                  const float y = rinv_s[m] * tot[nt][i] + cq[nt];
+                  st_bf16(rdst, base + (uint32_t)b * bstride + (uint32_t)t * rstride, y);
+                }
+                if (++t == d.H) {
+                  t = 0;
+                  ++b;
                 }
               }
             }
@@ -872,7 +950,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
         if (c < npair) {
           load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * c, 2 * c + 1,
                      x * hpx * DH / 32);
-          resid_pre_static(ro, bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D, c);
+          if ((c & 7) == x) resid_pre_static(ro, bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D, c);
         }
       }
       // ---------------- merge of the key splits
@@ -880,10 +958,11 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
         const uint64_t e = E(k, l, 2);
         if (!wait_flags(a, local_flags, 8, 32, E(k, l, 1), &lds_ok)) return;
         if (a.S > 1)
-          for (int iw = c * 4 + w; iw < mrg_waves; iw += 128) {
-            const int u = iw % (DH / 32), jt = (iw / (DH / 32)) % QTh, hl = iw / (DH / 32) / QTh % hpx;
-            const int b = iw / (DH / 32) / QTh / hpx;
-            merge_wave<DH>(a, blk, b, x * hpx + hl, jt, u);
+          for (int it = c; it < mrg_items; it += 32) {
+            const int u = it % (DH / 32), jt = (it / (DH / 32)) % QTh, hl = it / (DH / 32) / QTh % hpx;
+            const int b = it / (DH / 32) / QTh / hpx;
+            merge_wg<DH>(a, blk, b, x * hpx + hl, jt, u, lds);
+            __syncthreads();  // LDS reused by the next item
           }
         PTRACE((int)(e - e0), 5);
         publish_wg(a, myflag, e);
@@ -898,13 +977,13 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           if (pp != c) {
             load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * pp, 2 * pp + 1,
                        x * hpx * DH / 32);
-            resid_pre_static(ro, scale_next, pp);
+            if (red) resid_pre_static(ro, scale_next, pp);
           }
-          resid_pre_h<MT>(a, ro, pp);
+          if (red) resid_pre_h<MT>(a, ro, pp);
           f32x4 tot[2];
           gemm_unit<MT, KO, false>(d, wo, reinterpret_cast<const bf16*>(blk + a.o_o), qd, x * hpx * DH / 32, nullptr,
                                    tot, lds, (int)(e - e0));
-          resid_split<MT>(a, pp, x, tot, blk + a.o_hsm, blk + a.o_ssqm, e, &lds_flag, ro);
+          if (!resid_flagged<MT>(a, pp, x, tot, ro, blk + a.o_hsm, blk + a.o_ssqm, e, &lds_ok)) return;
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
@@ -954,7 +1033,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * c, 2 * c + 1,
                      x * (d.F / 256));
           const int jn = (l + 1 < L) ? 2 * (l + 1) : 2 * L;
-          resid_pre_static(rd, bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D, c);
+          if ((c & 7) == x) resid_pre_static(rd, bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D, c);
         }
       }
       // ---------------- down projection (this XCD's MLP columns) + residual across XCDs
@@ -972,13 +1051,13 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           if (pp != c) {
             load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * pp, 2 * pp + 1,
                        x * (d.F / 256));
-            resid_pre_static(rd, scale_next, pp);
+            if (red) resid_pre_static(rd, scale_next, pp);
           }
-          resid_pre_h<MT>(a, rd, pp);
+          if (red) resid_pre_h<MT>(a, rd, pp);
           f32x4 tot[2];
           gemm_unit<MT, KD, false>(d, wd, reinterpret_cast<const bf16*>(blk + a.o_act), d.F, x * (d.F / 256), nullptr,
                                    tot, lds, (int)(e - e0));
-          resid_split<MT>(a, pp, x, tot, hs_next, ssq_next, e, &lds_flag, rd);
+          if (!resid_flagged<MT>(a, pp, x, tot, rd, hs_next, ssq_next, e, &lds_ok)) return;
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
@@ -1067,7 +1146,6 @@ hipError_t enqueue_denoise_persistent(const Dims& d, const Bufs& b, const Persis
   a.k_bytes = (uint32_t)lay.k_bytes; a.o_hsf = (uint32_t)lay.o_hsf; a.o_ssqf = (uint32_t)lay.o_ssqf;
   a.flag_wg = pb.flag_wg;
   a.flag_pair = pb.flag_pair;
-  a.cnt = pb.cnt;
   a.ctl = pb.ctl;
   a.part = pb.part;
   a.attn_ws = pb.attn_ws;

@@ -18,10 +18,10 @@ struct PersistBufs {
   char* act;            // N * L activation blocks
   char* fin;            // N final blocks
   uint64_t* flag_wg;    // [kPersistWGs] last finished phase (epoch) of each workgroup
-  uint64_t* flag_pair;  // [D/32] last residual epilogue (epoch) of each tile pair
-  unsigned* cnt;        // [D/32] arrival counters of the residual split sums
+  uint64_t* flag_pair;  // [D/32] last residual epilogue (epoch) of each tile pair, then
+                        // [D/32][8] last partial (epoch) of each (tile pair, XCD)
   unsigned* ctl;        // [0] abort word (sticky until the host resets it), [1] failing epoch, [2] placement
-  float* part;          // residual split partials
+  float* part;          // residual split partials: (value, epoch tag) words
   float* attn_ws;       // attention split partials
 };
 
@@ -35,7 +35,6 @@ struct PArgs {
   uint32_t k_bytes, o_hsf, o_ssqf;
   uint64_t* flag_wg;
   uint64_t* flag_pair;
-  unsigned* cnt;
   unsigned* ctl;
   float* part;
   float* attn_ws;
