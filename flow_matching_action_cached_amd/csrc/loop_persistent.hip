@@ -596,19 +596,14 @@ __device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds
 
 // ------------------------------------------------------------------ residual sums across XCDs
 // Tile pair p of a residual linear has one partial per XCD (its split of the input columns).
-// The partials travel as 8-byte words (value, epoch tag): every XCD but one stores its partial
-// and moves on; the reducer (XCD p mod 8) polls the seven others' words until each carries
-// this phase's tag, adds the eight partials in XCD order, and writes the residual
-// h += sum, the next norm's input hs = h (1 + scale_next) and its statistics, then the pair's
-// epoch flag.  No counter and no wait for store acknowledgements on the contributors' side.
+// Every XCD but one stores its partial and raises its (pair, XCD) flag; the reducer (XCD
+// p mod 8) waits for the seven flags, adds the eight partials in XCD order, and writes the
+// residual h += sum, the next norm's input hs = h (1 + scale_next) and its statistics, then
+// the pair's epoch flag.
 struct ResidPre {
   float sc1[2];   // 1 + scale of the norm that consumes h, at this lane's column of tile nt
   float h[2][4];  // residual rows of this wave's m-tile (reducer only)
 };
-
-__device__ __forceinline__ size_t ll_index(int pair, int x, int nt, int w, int i, int lane) {
-  return (((((size_t)pair * 8 + x) * 2 + nt) * 4 + w) * 4 + i) * 64 + lane;
-}
 
 // Loads ahead of the phase's wait: the static scale of both tiles' columns.
 __device__ __forceinline__ void resid_pre_static(ResidPre& rp, const float* scale_next, int pair) {
@@ -632,109 +627,9 @@ __device__ __forceinline__ void resid_pre_h(const PArgs& a, ResidPre& rp, int pa
     }
 }
 
-// Returns false if the loop was aborted while polling.
-template <int MT>
-__device__ bool resid_sum(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp, char* hs_next,
-                          char* ssq_next, uint64_t e, int* lds_ok) {
-  const Dims& d = a.d;
-  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Each word is built as (value bits, tag) lanes of a u32x2 and moved with one 8-byte buffer
-  // access (single-copy atomic for an aligned 8-byte location).
-  const __amdgpu_buffer_rsrc_t rl = rsrc(a.part, (uint32_t)((size_t)(d.D / 32) * 8 * 2 * 4 * 4 * 64 * 8));
-  const uint32_t tag = (uint32_t)e;
-  const int rx = pair & 7;
-  if (x != rx) {
-    if (w < MT)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // (the element is copied out first: a bit cast of a vector element lvalue read
-          // element 0 for every i in this compiler)
-          const float tv = tot[nt][i];
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(tv), tag}, rl,
-                                                (uint32_t)(ll_index(pair, x, nt, w, i, lane) * 8), 0, kSC1);
-        }
-    return true;
-  }
-  int ok = 1;
-  if (w < MT) {
-    float v[8][2][4];
-    unsigned spins = 0;
-    while (true) {
-      // all 64 words in flight at once (this XCD's own slot too, ignored), then one test
-      u32x2 wd[8][2][4];
-#pragma unroll
-      for (int x2 = 0; x2 < 8; ++x2)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            wd[x2][nt][i] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rl, (uint32_t)(ll_index(pair, x2, nt, w, i, lane) * 8), 0, kSC1));
-      unsigned stale = 0;
-#pragma unroll
-      for (int x2 = 0; x2 < 8; ++x2)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x2 wv = wd[x2][nt][i];
-            const unsigned lo = wv[0], hi = wv[1];
-            stale |= x2 == rx ? 0u : hi ^ tag;
-            v[x2][nt][i] = __uint_as_float(lo);
-          }
-      if (!__any(stale != 0)) break;
-      ++spins;
-      if ((spins & 63) == 0 && ld_u32_agent(a.ctl) != 0) {
-        ok = 0;
-        break;
-      }
-      if (spins > kSpinMax / 64) {
-        st_u32_agent(a.ctl, 1u);
-        st_u32_agent(a.ctl + 1, (unsigned)(e - a.epoch0));
-        ok = 0;
-        break;
-      }
-    }
-    if (ok) {
-      const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
-      const __amdgpu_buffer_rsrc_t rhs = rsrc(hs_next, (uint32_t)(64 * d.D * 2));
-      const __amdgpu_buffer_rsrc_t rss = rsrc(ssq_next, (uint32_t)(64 * (d.D / 16) * 4));
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int tile = 2 * pair + nt, col = tile * 16 + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sum = 0.f;
-#pragma unroll
-          for (int x2 = 0; x2 < 8; ++x2) sum += x2 == rx ? tot[nt][i] : v[x2][nt][i];
-          const int m = w * 16 + grp * 4 + i;
-          float hn = 0.f;
-          if (m < d.M) {
-            hn = rp.h[nt][i] + sum;
-            st_f32(rh, (uint32_t)(((size_t)m * d.D + col) * 4), hn);
-            st_bf16(rhs, (uint32_t)(sw_idx(m, col, d.D) * 2), hn * rp.sc1[nt]);
-          }
-          const float sq = sum16(hn * hn);
-          if (r16 == 0 && m < d.M) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + tile) * 4), sq);
-        }
-      }
-    }
-  }
-  if (tid == 0) *lds_ok = 1;
-  __syncthreads();
-  if (w < MT && lane == 0 && !ok) *lds_ok = 0;
-  __syncthreads();
-  if (*lds_ok == 0) return false;
-  publish(a.flag_pair + pair, e);
-  return true;
-}
-
-// Flagged form: each contributor stores its partial, waits for the stores to be performed
-// and raises its (pair, XCD) flag; the reducer polls the seven flags with a few lanes, then
-// loads the seven partials in one round trip.  Partial layout: [pair][x][nt][w][64] f32x4.
+// The contributor waits for its partial's stores to be performed before raising its flag;
+// the reducer polls the seven flags with a few lanes, then loads the seven partials in one
+// round trip.  Partial layout: [pair][x][nt][w][64] f32x4.  False if the loop was aborted.
 template <int MT>
 __device__ bool resid_flagged(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp,
                               char* hs_next, char* ssq_next, uint64_t e, int* lds_ok) {
@@ -1122,7 +1017,8 @@ static void attn_split(const Dims& d, int hpx, int& S, int& bps) {
   S = (nblk + bps - 1) / bps;
 }
 
-size_t persistent_part_floats(const Dims& d) { return (size_t)(d.D / 32) * 8 * 2 * 4 * 4 * 64 * 2; }
+// [pair][x][nt][m-tile (<= 4)][64 lanes] f32x4
+size_t persistent_part_floats(const Dims& d) { return (size_t)(d.D / 32) * 8 * 2 * 4 * 64 * 4; }
 
 size_t persistent_attn_floats(const Dims& d) {
   int S, bps;
