@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -58,6 +59,9 @@ struct phyai_ctx {
   // persistent loop (<= 64 token rows, bf16; off until enabled): its buffers are sized with
   // the tables
   int persist_enabled = 0;
+  // this device's allocation-free scratch (null if its address lookup failed: lookup_err)
+  void* noalloc_scratch = nullptr;
+  hipError_t noalloc_lookup_err = hipSuccess;
   void* pmem = nullptr;
   PersistBufs pb{};
   int p_steps = 0;                   // steps the buffers hold
@@ -336,6 +340,47 @@ std::vector<float> unipc_weights(const float* t_host, int n, int order) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free scratch
+// Split-reduction scratch of phyai_denoise_noalloc (callers that cannot allocate device
+// memory): one copy per device, held until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory: the host uses only the address that
+// hipGetSymbolAddress returns for a device, looked up once per device with that device
+// current and kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[device] = p;
+  }
+  *out = g_scratch[device];
+  return hipSuccess;
+}
+
+// Argument and state checks shared by the two denoise entry points.
+phyai_status check_denoise(phyai_ctx* c, const float* noise, int batch, int n_steps, const float* out,
+                           const char* who) {
+  const std::string w(who);
+  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, w + ": joint denoiser context (use phyai_wam_denoise)");
+  if (!noise || !out) return fail(c, PHYAI_ERR_INVALID_ARG, w + ": null pointer");
+  if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, w + ": weights not set");
+  if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, w + ": prefix KV not set");
+  if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, w + ": timestep tables not set");
+  if (n_steps != c->n_steps) return fail(c, PHYAI_ERR_INVALID_ARG, w + ": n_steps differs from the tables");
+  if (batch < 1 || batch > c->batch)
+    return fail(c, PHYAI_ERR_INVALID_ARG, w + ": batch outside [1, batch of the installed prefix]");
+  return PHYAI_OK;
+}
+
 extern "C" {
 
 const char* phyai_version(void) { return "phyai-mi355x 0.1 (gfx950)"; }
@@ -407,6 +452,8 @@ phyai_status phyai_create(const phyai_config* cfg, void* hip_stream, phyai_ctx**
     delete c;
     return PHYAI_ERR_DEVICE;
   }
+  // set-up of the allocation-free path: this device's scratch address (the device is current)
+  c->noalloc_lookup_err = scratch_address(c->device, &c->noalloc_scratch);
 
   Dims& d = c->base;
   d.L = g.n_layers; d.D = g.width; d.Hq = g.n_q_heads; d.Hkv = g.n_kv_heads; d.dh = g.head_dim;
@@ -709,14 +756,10 @@ phyai_status phyai_set_graph_mode(phyai_ctx* c, int use_graph) {
 phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_steps, float* out) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();
-  if (c->joint) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: joint denoiser context (use phyai_wam_denoise)");
-  if (!noise || !out) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: null pointer");
-  if (!c->have_weights) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: weights not set");
-  if (!c->have_prefix) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: prefix KV not set");
-  if (!c->have_tables) return fail(c, PHYAI_ERR_BAD_STATE, "denoise: timestep tables not set");
-  if (n_steps != c->n_steps) return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: n_steps differs from the tables");
-  if (batch < 1 || batch > c->batch)
-    return fail(c, PHYAI_ERR_INVALID_ARG, "denoise: batch outside [1, batch of the installed prefix]");
+  {
+    const phyai_status st = check_denoise(c, noise, batch, n_steps, out, "denoise");
+    if (st != PHYAI_OK) return st;
+  }
   // the loop runs at the bucket's batch; pad slots start from x = 0 on their (stale but
   // finite) cache rows, and samples never interact, so the real rows are those of the
   // bucket's run
@@ -741,6 +784,49 @@ phyai_status phyai_denoise(phyai_ctx* c, const float* noise, int batch, int n_st
   }
   const phyai_status st = run_loop(c, d, plan, "denoise");
   if (st != PHYAI_OK) return st;
+  HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  return PHYAI_OK;
+}
+
+phyai_status phyai_denoise_noalloc(phyai_ctx* c, const float* noise, int batch, int n_steps, float* out) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  {
+    const phyai_status st = check_denoise(c, noise, batch, n_steps, out, "denoise_noalloc");
+    if (st != PHYAI_OK) return st;
+  }
+  if (!c->noalloc_scratch)
+    return fail(c, PHYAI_ERR_DEVICE, std::string("denoise_noalloc: no scratch address for this device: ") +
+                                         hipGetErrorString(c->noalloc_lookup_err));
+  const int bucket = graph_bucket(c, batch);
+  const Dims d = launch_dims(c, bucket, c->prefix_len, n_steps);
+  const Plan plan = make_plan(d, c->wt);
+  // the scratch: arrival counters first (cleared by every call), then the split partials
+  Layout sl;
+  const size_t o_acnt = sl.take(attn_counters(d) * 4), o_gcnt = sl.take(gemm_counters(d) * 4);
+  const size_t cnt_bytes = sl.off;
+  const size_t o_aws = sl.take(std::max<size_t>(attn_ws_floats(d, plan), 1) * 4);
+  const size_t o_gws = sl.take(std::max<size_t>(gemm_ws_floats(d, plan), 1) * 4);
+  if (sl.off > kNoAllocScratchBytes) {
+    char msg[200];
+    std::snprintf(msg, sizeof(msg),
+                  "denoise_noalloc: this batch and prefix need %zu bytes of split scratch; the allocation-free "
+                  "path holds at most %zu (use phyai_denoise)",
+                  sl.off, kNoAllocScratchBytes);
+    return fail(c, PHYAI_ERR_INVALID_ARG, msg);
+  }
+  char* sp = static_cast<char*>(c->noalloc_scratch);
+  Bufs b = c->b;
+  b.attn_cnt = reinterpret_cast<unsigned*>(sp + o_acnt);
+  b.gemm_cnt = reinterpret_cast<unsigned*>(sp + o_gcnt);
+  b.attn_ws = reinterpret_cast<float*>(sp + o_aws);
+  b.gemm_ws = reinterpret_cast<float*>(sp + o_gws);
+  const size_t xbytes = (size_t)batch * d.H * d.A * 4, xbucket = (size_t)d.M * d.A * 4;
+  HIPCHK(c, hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream));
+  if (xbucket > xbytes) HIPCHK(c, enqueue_zero_f32(c->b.x + xbytes / 4, (xbucket - xbytes) / 4, c->stream));
+  // a fill kernel, not a memset: the counters start at zero whatever the last call left
+  HIPCHK(c, enqueue_zero_f32(reinterpret_cast<float*>(sp), cnt_bytes / 4, c->stream));
+  HIPCHK(c, enqueue_denoise(d, b, plan, c->wt, c->stream));
   HIPCHK(c, hipMemcpyAsync(out, c->b.x, xbytes, hipMemcpyDeviceToDevice, c->stream));
   return PHYAI_OK;
 }

@@ -218,6 +218,22 @@ phyai_status phyai_set_timestep_tables(phyai_ctx* ctx, const float* t_host, int 
 phyai_status phyai_denoise(phyai_ctx* ctx, const float* noise, int batch, int n_steps,
                            float* actions_out);
 
+/* Allocation-free denoise, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid hipMalloc).  Same arguments, checks,
+ * bucketing and result as phyai_denoise (bitwise: the same kernels in the same order), but
+ * the loop is launched eagerly (no graph is captured, the persistent loop is not used) and
+ * its split-reduction scratch (partial sums and arrival counters) lives in the library's
+ * static device array of 16 MiB per device, held until the process ends, instead of the
+ * context's arena.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Every call on one device shares that array: the counters are cleared
+ * at the start of each call, and calls that overlap on one device (other streams or
+ * contexts) race and give wrong results.  INVALID_ARG, with the sizes in phyai_last_error,
+ * when the batch and prefix need more than 16 MiB of scratch (e.g. pi0.5 at batch 1 and
+ * prefix 816 needs about 12.0 MiB); DEVICE if the array's address could not be obtained
+ * when the context was created. */
+phyai_status phyai_denoise_noalloc(phyai_ctx* ctx, const float* noise, int batch, int n_steps,
+                                   float* actions_out);
+
 /* Choose graph replay (1, default) or eager kernel launches (0) for phyai_denoise.
  * Both run the same kernels in the same order and give bitwise identical results. */
 phyai_status phyai_set_graph_mode(phyai_ctx* ctx, int use_graph);
