@@ -61,6 +61,13 @@ def profiled_traffic(kernel):
     return PROFILED_TRAFFIC["bytes"].get(kernel)
 
 
+def stage_traffic(stage):
+    """Counted bytes per launch of a loop stage (the attention stage: attention + merge)."""
+    parts = ["attention", "attn_merge"] if stage == "attention" else [stage]
+    vals = [profiled_traffic(k) for k in parts]
+    return None if any(v is None for v in vals) else int(sum(vals))
+
+
 KERNEL_IDS = {"qkv": 0, "attention": 1, "attn_merge": 7, "o_proj": 2, "gate_up": 3, "down": 4, "out_euler": 5}
 KERNELS = ["qkv", "attention", "o_proj", "gate_up", "down", "out_euler"]
 
@@ -180,22 +187,75 @@ def device_inputs(d, inputs, torch):
 
 
 def cpu_baseline(d, inputs):
-    """The CPU oracle (float64 NumPy) on one whole chunk of the same workload."""
+    """The CPU oracle (float64 NumPy) on one whole chunk of the same workload, all cores;
+    beside it, labelled extrapolations: one Euler step on one thread (x N steps), the batch-32
+    chunk (the oracle evaluates samples one by one), and the joint denoiser's guided pair from
+    one layer of one step at full width (x layers x steps)."""
     from oracle import expert as ox
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
+    t = schedule(d.n_steps)
     ts = []
     for _ in range(4):  # one warm-up, three timed
         t0 = time.perf_counter()
-        ox.denoise(inputs, d, t=schedule(d.n_steps))
+        ox.denoise(inputs, d, t=t)
         ts.append(time.perf_counter() - t0)
     sec = statistics.median(ts[1:])
-    return {"value": round(sec * 1000.0, 1), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
-            "sample": "1 chunk (10 Euler steps) of the pi0.5-shaped workload at batch 1, float64 NumPy; "
-                      "median of 3 timed runs after 1 warm-up"}
+    out = {"value": round(sec * 1000.0, 1), "unit": "ms/chunk", "cores": int(threads), "kind": "oracle",
+           "sample": "1 chunk (10 Euler steps) of the pi0.5-shaped workload at batch 1, float64 NumPy; "
+                     "median of 3 timed runs after 1 warm-up"}
+    # one Euler step (velocity of step 0 and the update) of sample 0 on one thread, x N
+    p = ox.as_f64_params(inputs)
+    tables = ox.modulation_tables(t, inputs["w_mod"], inputs["b_mod"])
+    kp = inputs["k_pre"][0].astype("float64")
+    vp = inputs["v_pre"][0].astype("float64")
+    x0 = inputs["noise"][0].astype("float64")
+
+    def one_step():
+        t0 = time.perf_counter()
+        x0 + ox.step_sizes(t)[0] * ox.velocity(x0, tables[0], p, kp, vp, d)
+        return time.perf_counter() - t0
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one_step()
+            st = one_step()
+        out["single_thread"] = {
+            "value": round(st * d.n_steps * 1000.0, 1), "unit": "ms/chunk", "cores": 1, "kind": "oracle",
+            "extrapolated": True,
+            "sample": f"one Euler step of the batch-1 chunk on one thread ({st * 1000.0:.1f} ms), x {d.n_steps} steps"}
+    out["batch32_extrapolated"] = {
+        "value": round(32 * sec * 1000.0, 1), "unit": "ms per batch-32 chunk",
+        "chunks_per_s": round(32 / (32 * sec), 3), "cores": int(threads), "kind": "oracle", "extrapolated": True,
+        "sample": "the timed batch-1 chunk x 32 samples (samples never interact; the oracle runs them one by one)"}
+    # joint denoiser: both guidance branches through one layer of one step at full width
+    import dataclasses as dc
+    import synth
+    from oracle import wam as ow
+    dw = synth.WAM_CONFIGS["wam"]
+    d1 = dc.replace(dw, n_layers=1)
+    iw = synth.make_wam_inputs(d1, 0)
+    keys = ("w_in_lat", "b_in_lat", "w_in_act", "b_in_act", "w_out_lat", "b_out_lat", "w_out_act", "b_out_act",
+            "w_qkv", "w_o", "w_gu", "w_d")
+    pw = {k: iw[k].astype("float64") for k in keys}
+    tw = schedule(dw.n_steps)
+    zl, za = iw["z_lat"].astype("float64"), iw["z_act"].astype("float64")
+    t0 = time.perf_counter()
+    for cond in (iw["c_cond"], iw["c_uncond"]):
+        ow.velocity(zl, za, ow.modulation(tw[0], cond, iw["w_mod"], iw["b_mod"]), pw, d1)
+    lw = time.perf_counter() - t0
+    del pw, iw
+    out["joint_extrapolated"] = {
+        "value": round(lw * dw.n_layers * dw.n_steps * 1000.0, 1), "unit": "ms/chunk", "cores": int(threads),
+        "kind": "oracle", "extrapolated": True,
+        "sample": f"one layer of one step of both guidance branches at full width ({dw.latent_tokens + dw.action_tokens}"
+                  f" tokens, width {dw.width}; {lw * 1000.0:.0f} ms incl. in/out projections), x {dw.n_layers} layers "
+                  f"x {dw.n_steps} steps"}
+    return out
 
 
 def main():
@@ -269,14 +329,31 @@ def main():
     lat.sort()
     p99 = lat[min(len(lat) - 1, int(round(0.99 * (len(lat) - 1))))]
 
-    # isolated kernel durations: one graph replay of back-to-back launches each
-    per_launch_us = kernel_times(ex, args.kernel_reps, torch, KERNELS + ["attn_merge"])
-    launches = {"qkv": d.n_layers, "attention": d.n_layers, "o_proj": d.n_layers, "gate_up": d.n_layers,
-                "down": d.n_layers, "out_euler": 1}
-    share = {k: per_launch_us[k] * launches[k] for k in KERNELS}
+    # in-loop kernel durations: the same loop with an event after every launch on the context
+    # stream, queued behind a short wait so that it runs back to back; the attention stage is the
+    # attention launch plus the merge of its key splits
+    # Each event costs the queue a few microseconds, which the intervals include: the loop with
+    # marks runs longer than the graph replay by n_events x that cost, so every interval is
+    # corrected by the mean cost per event (the graph's kernels run back to back: the sum of
+    # their durations is its chunk time).
+    stage_reps = max(5, args.steps // 5)
+    st_us, loop_ms = ex.time_loop_stages(noise, reps=stage_reps)
+    n_marks = 1 + d.n_steps * (6 * d.n_layers + 1)  # launches, each followed by an event
+    ev_us = max(0.0, (loop_ms - ms_per_chunk) * 1000.0 / n_marks)
+    raw_us = {"qkv": st_us[0], "attention": st_us[1] + st_us[7], "o_proj": st_us[2], "gate_up": st_us[3],
+              "down": st_us[4], "out_euler": st_us[5]}
+    inloop_us = {k: v - ev_us * (2 if k == "attention" else 1) for k, v in raw_us.items()}
+    per_chunk = {k: d.n_steps * d.n_layers for k in KERNELS}
+    per_chunk["out_euler"] = d.n_steps
+    share = {k: inloop_us[k] * per_chunk[k] for k in KERNELS}
     dominant = max(share, key=share.get)
     abytes = algorithmic_bytes(d)
-    ach = abytes[dominant] / (per_launch_us[dominant] * 1e-6) / 1e9
+    ach = abytes[dominant] / (inloop_us[dominant] * 1e-6) / 1e9
+    print(f"[bench] in-loop stages (us/launch): {inloop_us}, loop with marks {loop_ms:.4f} ms", file=sys.stderr,
+          flush=True)
+    # cache-warm figures: one graph replay of back-to-back launches of layer 0 (the same operands
+    # can stay in L2 / the memory-side cache between launches)
+    per_launch_us = kernel_times(ex, args.kernel_reps, torch, KERNELS + ["attn_merge"])
     print(f"[bench] isolated kernels (us/launch): {per_launch_us}", file=sys.stderr, flush=True)
 
     ex.denoise(noise, out)
@@ -592,11 +669,22 @@ def main():
                        "p99": round(p99, 4)},
         "chunk_hbm": {"algorithmic_bytes": cb, "achieved_GBs": round(cb / (ms_per_chunk * 1e-3) / 1e9, 1),
                       "frac": round(cb / (ms_per_chunk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "kernel_us": {k: round(v, 3) for k, v in per_launch_us.items()},
+        "kernel_us": {k: round(v, 3) for k, v in inloop_us.items()},
+        "kernel_us_share_of_chunk": {k: round(share[k] / 1000.0 / ms_per_chunk, 4) for k in KERNELS},
+        "kernel_us_inloop_raw": {k: round(v, 3) for k, v in raw_us.items()},
+        "loop_with_marks_ms": round(loop_ms, 4),
+        "event_cost_us": round(ev_us, 3),
+        "kernel_us_cache_warm": {k: round(v, 3) for k, v in per_launch_us.items()},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(dominant),
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": stage_traffic(dominant),
                      "algorithmic_bytes_per_launch": abytes[dominant],
-                     "avg_launch_us": round(per_launch_us[dominant], 3)},
+                     "avg_launch_us": round(inloop_us[dominant], 3),
+                     "timing": "in-loop: HIP events between the launches of the loop on its stream, less the mean "
+                               "cost of an event (marked loop time - graph loop time) / events, mean over "
+                               f"{stage_reps} runs x {per_chunk[dominant]} launches"
+                               + (" (attention launch + split merge)" if dominant == "attention" else ""),
+                     "avg_launch_us_cache_warm": round(per_launch_us[dominant] + (per_launch_us["attn_merge"]
+                                                       if dominant == "attention" else 0.0), 3)},
         "output_finite": finite,
         "variants": variants,
         "cpu_baseline": cpu,

@@ -24,7 +24,7 @@ EXPORTED = (
     "phyai_capsule_bytes", "phyai_capsule_save", "phyai_capsule_restore", "phyai_capsule_fork",
     "phyai_unipc_weights",
     "phyai_set_timestep_tables",
-    "phyai_denoise", "phyai_denoise_noalloc", "phyai_set_graph_mode", "phyai_set_persistent", "phyai_loop_form", "phyai_sync", "phyai_last_error", "phyai_status_string",
+    "phyai_denoise", "phyai_denoise_noalloc", "phyai_time_loop_stages", "phyai_set_graph_mode", "phyai_set_persistent", "phyai_loop_form", "phyai_sync", "phyai_last_error", "phyai_status_string",
     "phyai_destroy", "phyai_quantize_int4_g128", "phyai_get_modulation", "phyai_version",
     "phyai_enqueue_kernel_repeat", "phyai_wam_create", "phyai_wam_set_weights", "phyai_wam_set_conditions",
     "phyai_wam_denoise",
@@ -98,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.phyai_set_timestep_tables.argtypes = [vp, ctypes.POINTER(cf), ci]
     lib.phyai_denoise.argtypes = [vp, vp, ci, ci, vp]
     lib.phyai_denoise_noalloc.argtypes = [vp, vp, ci, ci, vp]
+    lib.phyai_time_loop_stages.argtypes = [vp, vp, ci, ci, vp, vp]
     lib.phyai_set_graph_mode.argtypes = [vp, ci]
     lib.phyai_set_persistent.argtypes = [vp, ci]
     lib.phyai_loop_form.argtypes = [vp, ci]
@@ -273,6 +274,17 @@ class ActionExpert(_Context):
             out = torch.empty_like(noise)
         self._check(self._lib.phyai_denoise(self._h, _ptr(noise), int(noise.shape[0]), self.n_steps, _ptr(out)))
         return out
+
+    def time_loop_stages(self, noise, reps=10):
+        """In-loop mean duration (us) of each kernel id of the denoise loop and the mean chunk time
+        (ms), from events between the launches of the loop (see phyai_time_loop_stages)."""
+        import torch
+        assert noise.dtype == torch.float32 and noise.is_contiguous()
+        us = (ctypes.c_float * 8)()
+        ms = ctypes.c_float()
+        self._check(self._lib.phyai_time_loop_stages(self._h, _ptr(noise), int(noise.shape[0]), int(reps),
+                                                     ctypes.addressof(us), ctypes.addressof(ms)))
+        return list(us), ms.value
 
     def denoise_noalloc(self, noise, out=None):
         """As denoise, through the allocation-free entry point (static scratch, eager launches)."""

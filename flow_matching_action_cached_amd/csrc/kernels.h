@@ -70,8 +70,18 @@ size_t tiled_split_ws_floats(const Dims& d);  // split scratch of the tiled resi
 size_t tiled_split_counters(const Dims& d);
 Plan make_plan(const Dims& d, WDtype wt);
 
+// Measurement marks: with them, enqueue_denoise records ev[0] before the first launch and
+// ev[i] after launch i (kind[i] = its kernel id as in enqueue_one, kind[0] = -1); cap is the
+// number of events available (1 + N (6 L + 1) + 1 are needed).
+struct LaunchMarks {
+  hipEvent_t* ev;
+  int* kind;
+  int n, cap;
+};
+
 // Enqueue the whole Euler loop (N steps) on `stream`.  x must already hold the noise.
-hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t stream);
+hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t stream,
+                           LaunchMarks* marks = nullptr);
 
 // Enqueue one launch of loop kernel `which` (0 QKV, 1 attention, 2 O, 3 gate/up, 4 down,
 // 5 out/Euler/in-projection, 6 first in-projection) with the arguments of step k, layer l.
@@ -101,6 +111,8 @@ hipError_t enqueue_wam_one(const Dims& d, const Bufs& b, const Plan& p, int whic
 
 // Zero n floats at p (stream-ordered kernel; no memset node when a caller captures it).
 hipError_t enqueue_zero_f32(float* p, size_t n, hipStream_t stream);
+// A one-wave kernel that returns after `us` microseconds (bounded wait for measurements).
+hipError_t enqueue_delay_us(unsigned us, hipStream_t stream);
 
 // One-off kernels.  With Dims::tmlp, e_scratch holds 3 N D doubles (embedding, hidden, MLP output).
 hipError_t enqueue_tables(const Dims& d, const Bufs& b, WDtype wt, const float* t_dev, double* e_scratch,

@@ -1527,12 +1527,24 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
 }
 
 template <class AT, class WT, class IOT>
-static hipError_t denoise_impl(const Dims& d, const Bufs& b, const Plan& p, hipStream_t st) {
-  hipError_t e = launch_one<AT, WT, IOT>(d, b, p, 6, 0, 0, st);
+static hipError_t denoise_impl(const Dims& d, const Bufs& b, const Plan& p, hipStream_t st, LaunchMarks* mk) {
+  // with marks: an event before the first launch and after every launch, and its kind
+  auto mark = [&](int which) -> hipError_t {
+    if (!mk) return hipSuccess;
+    if (mk->n >= mk->cap) return hipErrorInvalidValue;
+    mk->kind[mk->n] = which;
+    return hipEventRecord(mk->ev[mk->n++], st);
+  };
+  hipError_t e = mark(-1);
+  auto one = [&](int which, int k, int l) {
+    if (e == hipSuccess) e = launch_one<AT, WT, IOT>(d, b, p, which, k, l, st);
+    if (e == hipSuccess) e = mark(which);
+  };
+  one(6, 0, 0);
   for (int k = 0; k < d.N && e == hipSuccess; ++k) {
     for (int l = 0; l < d.L && e == hipSuccess; ++l)
-      for (int i = 0; i < 6 && e == hipSuccess; ++i) e = launch_one<AT, WT, IOT>(d, b, p, kLayerOrder[i], k, l, st);
-    if (e == hipSuccess) e = launch_one<AT, WT, IOT>(d, b, p, 5, k, 0, st);
+      for (int i = 0; i < 6 && e == hipSuccess; ++i) one(kLayerOrder[i], k, l);
+    one(5, k, 0);
   }
   return e;
 }
@@ -1657,11 +1669,12 @@ hipError_t enqueue_wam_denoise(const Dims& d, const Bufs& b, const Plan& p, hipS
   return e;
 }
 
-hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t st) {
+hipError_t enqueue_denoise(const Dims& d, const Bufs& b, const Plan& p, WDtype wt, hipStream_t st,
+                           LaunchMarks* marks) {
   switch (wt) {
-    case W_F32: return denoise_impl<float, float, float>(d, b, p, st);
-    case W_BF16: return denoise_impl<bf16, bf16, bf16>(d, b, p, st);
-    case W_INT4: return denoise_impl<bf16, i4, bf16>(d, b, p, st);
+    case W_F32: return denoise_impl<float, float, float>(d, b, p, st, marks);
+    case W_BF16: return denoise_impl<bf16, bf16, bf16>(d, b, p, st, marks);
+    case W_INT4: return denoise_impl<bf16, i4, bf16>(d, b, p, st, marks);
   }
   return hipErrorInvalidValue;
 }

@@ -870,6 +870,65 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
   return PHYAI_OK;
 }
 
+phyai_status phyai_time_loop_stages(phyai_ctx* c, const float* noise, int batch, int reps, float* stage_us,
+                                    float* chunk_ms) {
+  if (!c) return PHYAI_ERR_INVALID_ARG;
+  c->err.clear();
+  {
+    const phyai_status st = check_denoise(c, noise, batch, c->n_steps, stage_us, "time_loop_stages");
+    if (st != PHYAI_OK) return st;
+  }
+  if (!chunk_ms || reps < 1 || reps > 1000)
+    return fail(c, PHYAI_ERR_INVALID_ARG, "time_loop_stages: null output or reps outside [1, 1000]");
+  const int bucket = graph_bucket(c, batch);
+  const Dims d = launch_dims(c, bucket, c->prefix_len, c->n_steps);
+  const Plan plan = make_plan(d, c->wt);
+  const int n_ev = 2 + d.N * (6 * d.L + 1);
+  std::vector<hipEvent_t> ev(n_ev, nullptr);
+  std::vector<int> kind(n_ev, -1);
+  auto release = [&]() {
+    for (hipEvent_t e : ev)
+      if (e) hipEventDestroy(e);
+  };
+  auto bail = [&](const char* what, hipError_t e) {
+    release();
+    return fail(c, PHYAI_ERR_DEVICE, std::string("time_loop_stages: ") + what + ": " + hipGetErrorString(e));
+  };
+  for (int i = 0; i < n_ev; ++i) {
+    const hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) return bail("event", e);
+  }
+  double sum[8] = {0}, total = 0.0;
+  long cnt[8] = {0};
+  const size_t xbytes = (size_t)batch * d.H * d.A * 4, xbucket = (size_t)d.M * d.A * 4;
+  hipError_t e = hipSuccess;
+  for (int r = 0; r < reps; ++r) {
+    // the loop of phyai_denoise with an event after every launch, queued behind a short
+    // wait so that it runs back to back (graph capture cannot record timing events here)
+    LaunchMarks mk{ev.data(), kind.data(), 0, n_ev};
+    if ((e = hipMemcpyAsync(c->b.x, noise, xbytes, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess ||
+        (xbucket > xbytes && (e = enqueue_zero_f32(c->b.x + xbytes / 4, (xbucket - xbytes) / 4, c->stream)) != hipSuccess) ||
+        (e = enqueue_delay_us(20000, c->stream)) != hipSuccess ||
+        (e = enqueue_denoise(d, c->b, plan, c->wt, c->stream, &mk)) != hipSuccess ||
+        (e = hipStreamSynchronize(c->stream)) != hipSuccess)
+      return bail("replay", e);
+    float ms = 0.f;
+    for (int i = 1; i < mk.n; ++i) {
+      if ((e = hipEventElapsedTime(&ms, ev[i - 1], ev[i])) != hipSuccess) return bail("elapsed time", e);
+      if (kind[i] >= 0 && kind[i] < 8) {
+        sum[kind[i]] += ms;
+        ++cnt[kind[i]];
+      }
+    }
+    if ((e = hipEventElapsedTime(&ms, ev[0], ev[mk.n - 1])) != hipSuccess) return bail("elapsed time", e);
+    total += ms;
+  }
+  release();
+  for (int k = 0; k < 8; ++k) stage_us[k] = cnt[k] ? (float)(sum[k] / cnt[k] * 1000.0) : 0.f;
+  *chunk_ms = (float)(total / reps);
+  return PHYAI_OK;
+}
+
 phyai_status phyai_set_prefill_weights(phyai_ctx* c, const phyai_prefill_weights* w) {
   if (!c) return PHYAI_ERR_INVALID_ARG;
   c->err.clear();

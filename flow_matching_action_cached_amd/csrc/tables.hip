@@ -237,6 +237,18 @@ hipError_t enqueue_zero_f32(float* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// One wave that returns after `ticks` of the 100 MHz real-time counter (a bounded wait:
+// measurement code queues work behind it so that the queue runs back to back).
+__global__ void k_delay(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(10);
+}
+
+hipError_t enqueue_delay_us(unsigned us, hipStream_t st) {
+  hipLaunchKernelGGL(k_delay, dim3(1), dim3(64), 0, st, (uint64_t)us * 100u);
+  return hipGetLastError();
+}
+
 hipError_t enqueue_capsule_copy(const Dims& d, void* kc, void* vt, void* payload, int batch, int prefix_len,
                                 size_t es, bool save, hipStream_t st) {
   const size_t heads = (size_t)batch * d.L * d.Hkv;

@@ -300,6 +300,20 @@ phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
  * overwrites the context's activations, state and chunk K/V rows (re-run phyai_denoise after). */
 phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* ctx, int which, int layer, int reps);
 
+/* Measurement aid: the in-loop duration of each kernel of phyai_denoise.  Queues the same
+ * loop as phyai_denoise for `batch` (same bucket, launches and order) on the context stream
+ * with an event recorded before the first launch and after every launch, behind a 20 ms
+ * one-wave wait so that the queued launches run back to back; `reps` times (1..1000) from
+ * x = noise, each run synchronised.  Returns in host
+ * stage_us[8] the mean time in microseconds between the events around each launch of a
+ * kernel id (0 QKV, 1 attention, 2 O + residual, 3 gate/up, 4 down + residual,
+ * 5 out-projection/Euler/in-projection, 6 first in-projection, 7 merge of the attention
+ * splits; 0 for an id with no launch), and in host *chunk_ms the mean first-to-last event
+ * interval of a run.  Synchronous; the events are released before return.  Arguments and
+ * state are checked as for phyai_denoise. */
+phyai_status phyai_time_loop_stages(phyai_ctx* ctx, const float* noise, int batch, int reps, float* stage_us,
+                                    float* chunk_ms);
+
 /* ---------------------------------------------------------------- joint video/action denoiser
  * (PhyAI reading, Figure 4 and Sec. 5.5 third item; Sec. 5.4): latent video tokens and action
  * tokens evolve together in one sequence under full self-attention (no cached prefix, no
