@@ -840,6 +840,10 @@ phyai_status phyai_enqueue_kernel_repeat(phyai_ctx* c, int which, int layer, int
     return fail(c, PHYAI_ERR_BAD_STATE, "enqueue_kernel_repeat: weights, prefix and tables must be set");
   const Dims d = launch_dims(c, c->batch, c->prefix_len, c->n_steps);
   const Plan plan = make_plan(d, c->wt);
+  if (which == 7 && !c->joint) {  // the split merge has a launch of its own only on one path
+    const int nblk = (d.P + d.H + 31) / 32;
+    if (plan.attn_wide || (nblk + plan.attn_bps - 1) / plan.attn_bps == 1) return PHYAI_OK;
+  }
   auto key = std::make_tuple(which, layer, reps, c->batch, c->prefix_len, c->n_steps);
   auto it = c->kgraphs.find(key);
   if (it == c->kgraphs.end()) {

@@ -293,8 +293,8 @@ phyai_status phyai_get_modulation(phyai_ctx* ctx, float* dst);
 /* Measurement aid: enqueue on the context stream one graph replay of `reps` back-to-back
  * launches of a single kernel of the loop, with the arguments it has at step 0 and layer
  * `layer`.  which: 0 norm-folded QKV (+ chunk K/V into the cache), 1 attention, 7 merge of
- * the attention's key splits (an empty replay where attention merges in-kernel or runs
- * unsplit), 2 O-projection + residual, 3 gate/up + GeGLU, 4 down-projection + residual,
+ * the attention's key splits (nothing is enqueued where attention merges in-kernel or
+ * runs unsplit), 2 O-projection + residual, 3 gate/up + GeGLU, 4 down-projection + residual,
  * 5 out-projection + Euler + in-projection, 6 first in-projection.  Requires weights, prefix and tables.  The caller
  * brackets the call with events on the same stream to time one kernel in isolation.  It
  * overwrites the context's activations, state and chunk K/V rows (re-run phyai_denoise after). */

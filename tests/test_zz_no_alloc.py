@@ -76,13 +76,14 @@ def test_noalloc_pi05_batch1_matches_denoise():
 
 
 def test_noalloc_rejects_beyond_its_scratch():
-    """pi0.5 widths, one layer, 2 samples x 32 tokens over a 990-token prefix (32 key blocks):
-    32 query tiles, each split into 32 one-block splits, need 32 x 32 x 16512 B = 16.9 MB of
-    attention partials, above the 16 MiB array.  phyai_denoise still runs it, and one sample
-    (16 query tiles, 8.5 MB) fits."""
+    """pi0.5 widths in fp32 (whose attention leaves one partial per 32-key block for a merge
+    launch), one layer, 2 samples x 32 tokens over a 990-token prefix (32 key blocks): 32 query
+    tiles, each split into 32 one-block splits, need 32 x 32 x 16512 B = 16.9 MB of attention
+    partials, above the 16 MiB array.  phyai_denoise still runs it, and one sample (16 query
+    tiles, 8.5 MB) fits."""
     import flow_matching_action_cached_amd as fm
-    d = dataclasses.replace(PI05, n_layers=1, chunk_len=32, prefix_len=990, batch=2, n_steps=2)
-    _say("case: noalloc limit, pi05 widths, 1 layer, batch 2 x 32, prefix 990")
+    d = dataclasses.replace(PI05, n_layers=1, chunk_len=32, prefix_len=990, batch=2, n_steps=2, weight_dtype="f32")
+    _say("case: noalloc limit, pi05 widths fp32, 1 layer, batch 2 x 32, prefix 990")
     inp = synth.make_expert_inputs(d, 5)
     dev = device_inputs(d, inp)
     e = make_expert(d, dev, ex.schedule(d.n_steps))
