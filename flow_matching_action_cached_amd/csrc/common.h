@@ -126,10 +126,19 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-// Sum over the 16 lanes that share a lane group (xor 1..8).
+// Value of another lane of the same 16-lane row (DPP, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row (lanes 16 g .. 16 g + 15): lane ^ 1 and lane ^ 2 within
+// each quad, then the row rotated by 4 and by 8.  Every lane ends with the row's total (the
+// association may differ between lanes in the last bit; callers take one lane's value).
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x124>(v);  // row_ror 4
+  v += dpp_mov<0x128>(v);  // row_ror 8
   return v;
 }
 

@@ -10,8 +10,8 @@
 //   k_gemm<RESID>  output projection + residual;
 //   k_gemm<GEGLU>  adaptive-RMSNorm folded in, gate/up projection, gelu(g)*u;
 //   k_gemm<RESID>  down projection + residual;
-// and once per step k_out_euler (final norm, out-projection, x += dt v, and the
-// next step's in-projection).
+// and once per step k_out_rows (final norm, out-projection, x += dt v, and the
+// next step's in-projection, 16 token rows per workgroup).
 //
 // Norm folding.  adaRMS(h) W^T = rinv * ((h * (1 + scale)) W^T) + W shift, with
 // rinv = 1/sqrt(mean(h^2) + eps) per token row.  The producer of h (residual
@@ -1060,107 +1060,179 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
 }
 
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
-// One workgroup per token row.  k_prev >= 0: final adaptive norm of step k_prev,
-// v = rinv (hs W_out^T) + W_out shift + b_out, x += dt v.  k_next >= 0: in-projection
-// h = x W_in^T + b_in for step k_next, writing h, hs = h * (1 + scale) of that step's
-// first norm, and the row's sum-of-squares partials.  Loads are 16-byte vectors at
-// clamped addresses, issued before any of them is consumed.
+// k_prev >= 0: final adaptive norm of step k_prev, v = rinv (hs W_out^T) + W_out shift +
+// b_out, x += dt v.  k_next >= 0: in-projection h = x W_in^T + b_in for step k_next,
+// writing h, hs = h * (1 + scale) of that step's first norm, and the rows' sum-of-squares
+// partials.  One 16-row tile (the row tile of the swizzled activations) per workgroup, so
+// that the io weights are read once per 16 rows.  Out-projection
+// on MFMA (the bf16 or fp32 activations and weights, fp32 accumulation): the four waves
+// take the k-blocks round robin and their products are added in wave order; the update
+// and the in-projection (fp32, x from LDS, one output column per thread and pass) follow.
+// With few row tiles the in-projection's columns are split over `cs` workgroups per tile
+// (workgroup = tile * cs + c); each recomputes the tile's update (the out-projection is
+// small).  The state may be overwritten only once every workgroup of the tile has read it:
+// each arrives on the tile's counter after its reads, and the last to arrive writes it.
 template <class AT, class IOT>
-__global__ __launch_bounds__(256) void k_out_euler(Dims d, Bufs bf, int k_prev, int k_next) {
-  typedef typename FragOf<AT>::type AF;    // 8 activations
-  typedef typename FragOf<IOT>::type WF;   // 8 weights
-  __shared__ float xs[256];
-  __shared__ float vres[256];
-  __shared__ float wred[4];
-  const int tid = threadIdx.x, lane = tid & 63;
+__global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, int k_next, int cs) {
+  typedef typename FragOf<AT>::type AF;
+  typedef typename FragOf<IOT>::type WF;
+  __shared__ float xs[16][257];
+  __shared__ f32x4 red[4][16][64];
+  __shared__ float rinv_s[16];
+  __shared__ unsigned last_s;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = blockIdx.x;
+  const int rt = blockIdx.x / cs, cpart = blockIdx.x - rt * cs, m0 = rt * 16;
+  const int nta = (d.A + 15) / 16;  // 16-column output tiles of the out-projection (A <= 256)
+  PHASE_MARK(0);
   if (k_prev >= 0) {
-    const int n16 = d.D / 16;
-    float ss = 0.f;
-    if (w == 0) {
-      const float a0 = bf.ssq[(size_t)m * n16 + min(lane, n16 - 1)];
-      const float a1 = bf.ssq[(size_t)m * n16 + min(lane + 64, n16 - 1)];
-      ss = (lane < n16 ? a0 : 0.f) + (lane + 64 < n16 ? a1 : 0.f);
+    {  // final-norm statistics of the tile's rows: 16 threads per row
+      const int r = tid >> 4, j0 = tid & 15, m = min(m0 + r, d.M - 1), n16 = d.D / 16;
+      float ss = 0.f;
+      for (int j = j0; j < n16; j += 16) ss += bf.ssq[(size_t)m * n16 + j];
+      ss = sum16(ss);
+      if (j0 == 0) rinv_s[r] = 1.0f / sqrtf(ss / (float)d.D + d.eps);
     }
-    // hs chunks of this lane: k = lane*8 + 512*j (8 consecutive k are contiguous when swizzled)
-    const AT* hsr = static_cast<const AT*>(bf.hs);
+    PHASE_MARK(1);
+    const AT* hs = static_cast<const AT*>(bf.hs);
     const IOT* wo = static_cast<const IOT*>(bf.w_out);
-    AF hv[4];
-    float hmask[4];
+    const int kbn = d.D / 32;
+    for (int nt0 = 0; nt0 < nta; nt0 += 2) {  // two output tiles at a time
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int kb0 = w; kb0 < kbn; kb0 += 32) {  // this wave's k-blocks kb0 + 4 i, all loads in flight
+        AF af[8];
+        WF wf[2][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = lane * 8 + 512 * j;
-      hmask[j] = k < d.D ? 1.f : 0.f;
-      hv[j] = load_frag(hsr + sw_idx(m, min(k, d.D - 8), d.D));
-    }
-    for (int a0 = w; a0 < d.A; a0 += 32) {  // 8 outputs (a0, a0+4, ...) per pass
-      WF wv[8][4];
+        for (int i = 0; i < 8; ++i) {
+          const int kb = min(kb0 + 4 * i, kbn - 1);
+          af[i] = load_frag(hs + sw_frag(rt, kb, d.D, lane));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int a = min(a0 + 4 * u, d.A - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wv[u][j] = load_frag(wo + (size_t)a * d.D + min(lane * 8 + 512 * j, d.D - 8));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float part = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part += to_f32(hv[j][e]) * to_f32(wv[u][j][e]);
-          acc += hmask[j] * part;
+          for (int j = 0; j < 2; ++j)
+            wf[j][i] = load_frag(wo + (size_t)min((nt0 + j) * 16 + r16, d.A - 1) * d.D + kb * 32 + grp * 8);
         }
-        acc = wave_sum(acc);
-        if (lane == 0 && a0 + 4 * u < d.A) vres[a0 + 4 * u] = acc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (kb0 + 4 * i < kbn) acc[j] = mma(af[i], (nt0 + j) * 16 + r16 < d.A ? wf[j][i] : zero_frag<IOT>(), acc[j]);
       }
+      red[w][nt0][lane] = acc[0];
+      if (nt0 + 1 < nta) red[w][nt0 + 1][lane] = acc[1];
     }
-    if (w == 0) {
-      ss = wave_sum(ss);
-      if (lane == 0) wred[0] = ss;
-    }
+    PHASE_MARK(2);
     __syncthreads();
-    const float rinv = 1.0f / sqrtf(wred[0] / (float)d.D + d.eps);
-    for (int a = tid; a < d.A; a += 256) {
-      const IOT* bo = static_cast<const IOT*>(bf.b_out);
-      const float* cv = bf.cvec + (size_t)k_prev * bf.cv_stride + bf.cv_out_off;
-      const float v = rinv * vres[a] + cv[a] + to_f32(bo[a]);
-      const float xn = bf.x[(size_t)m * d.A + a] + bf.dt[k_prev] * v;
-      bf.x[(size_t)m * d.A + a] = xn;
-      xs[a] = xn;
+    const IOT* bo = static_cast<const IOT*>(bf.b_out);
+    const float* cv = bf.cvec + (size_t)k_prev * bf.cv_stride + bf.cv_out_off;
+    const float dt = bf.dt[k_prev];
+    for (int e = tid; e < 16 * 256; e += 256) xs[e >> 8][e & 255] = 0.f;  // columns past A stay zero
+    __syncthreads();
+    for (int e = tid; e < nta * 64; e += 256) {
+      const int nt = e >> 6, l = e & 63, a = nt * 16 + (l & 15);
+      const f32x4 s = ((red[0][nt][l] + red[1][nt][l]) + red[2][nt][l]) + red[3][nt][l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * (l >> 4) + i, m = m0 + r;
+        if (m < d.M && a < d.A) {
+          const float v = rinv_s[r] * s[i] + cv[a] + to_f32(bo[a]);
+          const float xn = bf.x[(size_t)m * d.A + a] + dt * v;
+          xs[r][a] = xn;
+          if (cs == 1) bf.x[(size_t)m * d.A + a] = xn;
+        }
+      }
     }
     __syncthreads();
   } else {
-    for (int a = tid; a < d.A; a += 256) xs[a] = bf.x[(size_t)m * d.A + a];
+    for (int e = tid; e < 16 * 256; e += 256) {
+      const int r = e >> 8, a = e & 255, m = m0 + r;
+      xs[r][a] = (m < d.M && a < d.A) ? bf.x[(size_t)m * d.A + a] : 0.f;
+    }
     __syncthreads();
   }
-  if (k_next < 0) return;
+  PHASE_MARK(3);
+  const bool split_x = k_prev >= 0 && cs > 1;
+  unsigned arrived = 0;
+  if (split_x && tid == 0)  // every thread's reads of the state are done (barrier above)
+    arrived = __hip_atomic_fetch_add(bf.gemm_cnt + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto write_state = [&]() {
+    if (!split_x) return;
+    if (tid == 0) {
+      last_s = arrived == (unsigned)cs - 1 ? 1u : 0u;
+      if (last_s) __hip_atomic_store(bf.gemm_cnt + rt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_s) return;
+    for (int e = tid; e < 16 * d.A; e += 256) {
+      const int r = e / d.A, a = e - r * d.A, m = m0 + r;
+      if (m < d.M) bf.x[(size_t)m * d.A + a] = xs[r][a];
+    }
+  };
+  if (k_next < 0) {
+    write_state();
+    return;
+  }
+  // in-projection on fp32 MFMA (exact products of the fp32 state and the weights):
+  // H = X W_in^T + b_in, one 16 x 16 output tile per MFMA chain, K = A in 32-wide chunks
+  // (columns past A are zero in xs and in the weight fragments)
   const IOT* wi = static_cast<const IOT*>(bf.w_in);
   const IOT* bi = static_cast<const IOT*>(bf.b_in);
   const float* scl = bf.mod + (size_t)k_next * d.nmod * 2 * d.D;  // norm 0, scale row
-  AT* hs = static_cast<AT*>(bf.hs);
-  const int na = d.A / 8;
-  for (int n0 = 0; n0 < d.D; n0 += 256) {
-    const int n = n0 + tid;  // D % 256 == 0: every thread has a column
-    const IOT* wr = wi + (size_t)n * d.A;
-    float hn = to_f32(bi[n]);
-    const float sc1 = 1.0f + scl[n];
-    for (int c0 = 0; c0 < na; c0 += 8) {
-      WF wv[8];
+  AT* hsw = static_cast<AT*>(bf.hs);
+  const int kc_n = (d.A + 31) / 32, ntn = d.D / 16;
+  // this workgroup's column tiles: [ntb, nte), four of a wave's (nt0 + 4 j) at a time
+  const int ntb = cpart * (ntn / cs), nte = ntb + ntn / cs;
+  for (int nt0 = ntb + w; nt0 < nte; nt0 += 16) {
+    f32x4 acc[4];
+    float b0[4], sc1[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) wv[c] = load_frag(wr + 8 * min(c0 + c, na - 1));
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < kc_n; ++kc) {
+      const int a0 = kc * 32 + grp * 8;
+      WF wv[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (c0 + c < na)
+      for (int j = 0; j < 4; ++j) {
+        const int n = min(nt0 + 4 * j, nte - 1) * 16 + r16;
+        wv[j] = load_frag(wi + (size_t)n * d.A + min(a0, d.A - 8));
+        if (kc == 0) {  // the epilogue's bias and scale, with the first weights
+          b0[j] = to_f32(bi[n]);
+          sc1[j] = 1.0f + scl[n];
+        }
+      }
+      f32x8 xa;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) hn += xs[8 * (c0 + c) + e] * to_f32(wv[c][e]);
+      for (int e = 0; e < 8; ++e) xa[e] = xs[r16][a0 + e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x8 wb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wb[e] = a0 < d.A ? to_f32(wv[j][e]) : 0.f;
+        acc[j] = mma(xa, wb, acc[j]);
+      }
     }
-    bf.h[(size_t)m * d.D + n] = hn;
-    hs[sw_idx(m, n, d.D)] = to_elem<AT>(hn * sc1);
-    const float sq = sum16(hn * hn);
-    if ((tid & 15) == 0) bf.ssq[(size_t)m * (d.D / 16) + n / 16] = sq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nt = nt0 + 4 * j;
+      if (nt >= nte) break;
+      const int n = nt * 16 + r16;
+      // acc[j][i]: row 4 grp + i, column n
+      float hn[4], sq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hn[i] = acc[j][i] + b0[j];
+        sq[i] = sum16(hn[i] * hn[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * grp + i;
+        if (m < d.M) {
+          bf.h[(size_t)m * d.D + n] = hn[i];
+          hsw[sw_idx(m, n, d.D)] = to_elem<AT>(hn[i] * sc1[j]);
+          if (r16 == 0) bf.ssq[(size_t)m * (d.D / 16) + nt] = sq[i];
+        }
+      }
+    }
   }
+  write_state();
+  PHASE_MARK(7);
 }
 
 // ------------------------------------------------------------------ joint denoiser: guidance + Euler
@@ -1517,11 +1589,19 @@ static hipError_t launch_one(const Dims& d, const Bufs& b, const Plan& p, int wh
       return launch_gemm<AT, WT, EPI_RESID, 1>(d, b, g, d.D / 16, st);
     }
     case 5:
-      hipLaunchKernelGGL((k_out_euler<AT, IOT>), dim3(d.M), dim3(256), 0, st, d, b, k, k + 1 < d.N ? k + 1 : -1);
+    case 6: {
+      // column splits of the in-projection: about 128 workgroups, at least 4 column tiles each
+      const int tiles = (d.M + 15) / 16;
+      int cs = 1;
+      if (b.gemm_cnt && (size_t)tiles <= gemm_counters(d))  // the tiles' arrival counters
+        while (tiles * cs * 2 <= 128 && (d.D / 16) % (cs * 2) == 0 && d.D / 16 / (cs * 2) >= 4) cs *= 2;
+      if (which == 5)
+        hipLaunchKernelGGL((k_out_rows<AT, IOT>), dim3(tiles * cs), dim3(256), 0, st, d, b, k, k + 1 < d.N ? k + 1 : -1,
+                           cs);
+      else
+        hipLaunchKernelGGL((k_out_rows<AT, IOT>), dim3(tiles * cs), dim3(256), 0, st, d, b, -1, 0, cs);
       return hipGetLastError();
-    case 6:
-      hipLaunchKernelGGL((k_out_euler<AT, IOT>), dim3(d.M), dim3(256), 0, st, d, b, -1, 0);
-      return hipGetLastError();
+    }
   }
   return hipErrorInvalidValue;
 }
