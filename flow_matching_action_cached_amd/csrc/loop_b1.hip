@@ -1241,111 +1241,186 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
 // state).  Rows [0, H) of every activation hold the conditional branch (modulation
 // table 0), rows [H, 2H) the unconditional one (table 1); token t < Tl is a latent
 // token (Cl channels, latent projections), the rest action tokens (A dims).
-// One workgroup per token t.  k_prev >= 0: both branches' final norm and out-projection,
-// v = v_u + gamma (v_c - v_u), z += dt v.  k_next >= 0: in-projection of z (identical for
-// both branches), hs of each branch with its own first-norm scale, row statistics.
+// k_prev >= 0: both branches' final norm and out-projection, v = v_u + gamma (v_c - v_u),
+// z += dt v (or the UniPC update).  k_next >= 0: in-projection of z (identical for both
+// branches), hs of each branch with its own first-norm scale, row statistics.  One 16-token
+// tile per workgroup (tokens of one kind: latent tiles first, then action tiles; the last
+// tile of a kind may be ragged), so that the io projections are read once per 16 tokens:
+// the out-projection of both branches on MFMA (the four waves take the k-blocks round
+// robin, products added in wave order), the guided update per element, and the
+// in-projection on fp32 MFMA.  Token dims up to 256, four 16-column output tiles per pass
+// of the out-projection.
 template <class AT, class IOT>
-__global__ __launch_bounds__(256) void k_wam_out(Dims d, Bufs bf, int k_prev, int k_next) {
+__global__ __launch_bounds__(256) void k_wam_rows(Dims d, Bufs bf, int k_prev, int k_next) {
   typedef typename FragOf<AT>::type AF;
   typedef typename FragOf<IOT>::type WF;
-  __shared__ float xs[256];
-  __shared__ float vres[2][256];
-  __shared__ float wred[2];
-  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int NTC = 4;  // 16-column output tiles per pass (both branches: 8 products)
+  __shared__ float xs[16][257];
+  __shared__ f32x4 red[4][2 * NTC][64];
+  __shared__ float rinv_s[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = blockIdx.x;
-  const bool lat = t < d.Tl;
+  const int ntl = (d.Tl + 15) / 16;
+  const bool lat = (int)blockIdx.x < ntl;
+  const int t0 = lat ? blockIdx.x * 16 : d.Tl + ((int)blockIdx.x - ntl) * 16;
+  const int tend = lat ? d.Tl : d.H;  // end of this kind's tokens
   const int dim = lat ? d.Cl : d.A;
+  const int ntd = (dim + 15) / 16;
   const IOT* wo = static_cast<const IOT*>(lat ? bf.w_out : bf.w_out2);
   const IOT* bo = static_cast<const IOT*>(lat ? bf.b_out : bf.b_out2);
   const IOT* wi = static_cast<const IOT*>(lat ? bf.w_in : bf.w_in2);
   const IOT* bi = static_cast<const IOT*>(lat ? bf.b_in : bf.b_in2);
-  float* z = lat ? bf.x + (size_t)t * d.Cl : bf.x2 + (size_t)(t - d.Tl) * d.A;
-  const int rows[2] = {t, d.H + t};
+  // state of token t, channel a
+  auto zptr = [&](int t) { return lat ? bf.x + (size_t)t * d.Cl : bf.x2 + (size_t)(t - d.Tl) * d.A; };
+  for (int e = tid; e < 16 * 256; e += 256) xs[e >> 8][e & 255] = 0.f;  // channels past dim stay zero
+  __syncthreads();
   if (k_prev >= 0) {
-    const int n16 = d.D / 16;
-    if (w < 2) {  // wave b: row statistics of branch b
-      const int m = rows[w];
-      float ss = 0.f;
-      for (int j = lane; j < n16; j += 64) ss += bf.ssq[(size_t)m * n16 + j];
-      ss = wave_sum(ss);
-      if (lane == 0) wred[w] = ss;
-    }
-    const AT* hsb = static_cast<const AT*>(bf.hs);
-    for (int o0 = w; o0 < 2 * dim; o0 += 4) {  // output o: branch o / dim, channel o % dim
-      const int br = o0 / dim, a = o0 % dim;
-      const int m = rows[br];
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = lane * 8 + 512 * j;
-        const int kc = min(k, d.D - 8);
-        const AF hv = load_frag(hsb + sw_idx(m, kc, d.D));
-        const WF wv = load_frag(wo + (size_t)a * d.D + kc);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part += to_f32(hv[e]) * to_f32(wv[e]);
-        acc += k < d.D ? part : 0.f;
+    {  // final-norm statistics of the 32 rows (2 branches x 16 tokens), 16 threads per row
+      const int n16 = d.D / 16;
+      for (int rr = tid >> 4; rr < 32; rr += 16) {
+        const int br = rr >> 4, t = min(t0 + (rr & 15), tend - 1), m = br * d.H + t;
+        float ss = 0.f;
+        for (int j = tid & 15; j < n16; j += 16) ss += bf.ssq[(size_t)m * n16 + j];
+        ss = sum16(ss);
+        if ((tid & 15) == 0) rinv_s[br][rr & 15] = 1.0f / sqrtf(ss / (float)d.D + d.eps);
       }
-      acc = wave_sum(acc);
-      if (lane == 0) vres[br][a] = acc;
     }
-    __syncthreads();
-    for (int a = tid; a < dim; a += 256) {
-      const int ooff = bf.cv_out_off + (lat ? 0 : d.Cl) + a;
-      float v[2];
+    const AT* hs = static_cast<const AT*>(bf.hs);
+    const int kbn = d.D / 32;
+    const int trow = min(t0 + r16, tend - 1);
+    for (int nc = 0; nc < ntd; nc += NTC) {  // output tiles [nc, nc + nn) of both branches
+      const int nn = min(NTC, ntd - nc);
+      for (int bt = 0; bt < 2 * nn; ++bt) {
+        const int br = bt / nn, nt = nc + bt - br * nn;
+        const int m = br * d.H + trow;
+        const int a = min(nt * 16 + r16, dim - 1);
+        const bool av = nt * 16 + r16 < dim;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb0 = w; kb0 < kbn; kb0 += 32) {
+          AF af[8];
+          WF wf[8];
 #pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        const float rinv = 1.0f / sqrtf(wred[br] / (float)d.D + d.eps);
-        const float* cv = bf.cvec + ((size_t)k_prev * d.ntab + br) * bf.cv_stride;
-        v[br] = rinv * vres[br][a] + cv[ooff] + to_f32(bo[a]);
-      }
-      const float vg = v[1] + d.gamma * (v[0] - v[1]);
-      float zn;
-      if (d.solver) {  // UniPC: corrector of the step into k_prev, then the predictor out of it
-        const float* cf = bf.uni + (size_t)k_prev * 8;
-        const size_t ne = (size_t)d.Tl * d.Cl + (size_t)(d.H - d.Tl) * d.A;
-        const size_t e = lat ? (size_t)t * d.Cl + a : (size_t)d.Tl * d.Cl + (size_t)(t - d.Tl) * d.A + a;
-        float* xp = bf.ust;                                          // corrected z_{k-1} -> z_k
-        float* m_new = bf.ust + ne * (1 + (k_prev & 1));             // holds m_{k-2}, takes m_k
-        const float* m_km1 = bf.ust + ne * (1 + ((k_prev + 1) & 1));  // m_{k-1}
-        const float zk = z[a];
-        const float m = zk - cf[0] * vg;
-        float xc = zk, m1 = 0.f;
-        if (k_prev >= 1) {
-          m1 = m_km1[e];
-          const float m2 = k_prev >= 2 ? m_new[e] : 0.f;
-          xc = cf[1] * xp[e] + cf[2] * m + cf[3] * m1 + cf[4] * m2;
+          for (int i = 0; i < 8; ++i) {
+            const int kb = min(kb0 + 4 * i, kbn - 1);
+            af[i] = load_frag(hs + sw_idx(m, kb * 32 + grp * 8, d.D));
+            wf[i] = load_frag(wo + (size_t)a * d.D + kb * 32 + grp * 8);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (kb0 + 4 * i < kbn) acc = mma(af[i], av ? wf[i] : zero_frag<IOT>(), acc);
         }
-        zn = cf[5] * xc + cf[6] * m + cf[7] * m1;
-        xp[e] = xc;
-        m_new[e] = m;
-      } else {
-        zn = z[a] + bf.dt[k_prev] * vg;
+        red[w][bt][lane] = acc;
       }
-      z[a] = zn;
-      xs[a] = zn;
+      __syncthreads();
+      const int ca = min(dim - nc * 16, NTC * 16);  // channels of this pass
+      for (int e = tid; e < 16 * ca; e += 256) {
+        const int r = e / ca, a = nc * 16 + (e - r * ca), t = t0 + r;
+        if (t >= tend) continue;
+        const int nt = (a >> 4) - nc, l = (r >> 2) * 16 + (a & 15), i = r & 3;
+        const int ooff = bf.cv_out_off + (lat ? 0 : d.Cl) + a;
+        float v[2];
+#pragma unroll
+        for (int br = 0; br < 2; ++br) {
+          const int bt = br * nn + nt;
+          const float sum = ((red[0][bt][l][i] + red[1][bt][l][i]) + red[2][bt][l][i]) + red[3][bt][l][i];
+          const float* cv = bf.cvec + ((size_t)k_prev * d.ntab + br) * bf.cv_stride;
+          v[br] = rinv_s[br][r] * sum + cv[ooff] + to_f32(bo[a]);
+        }
+        const float vg = v[1] + d.gamma * (v[0] - v[1]);
+        float* z = zptr(t);
+        float zn;
+        if (d.solver) {  // UniPC: corrector of the step into k_prev, then the predictor out of it
+          const float* cf = bf.uni + (size_t)k_prev * 8;
+          const size_t ne = (size_t)d.Tl * d.Cl + (size_t)(d.H - d.Tl) * d.A;
+          const size_t el = lat ? (size_t)t * d.Cl + a : (size_t)d.Tl * d.Cl + (size_t)(t - d.Tl) * d.A + a;
+          float* xp = bf.ust;                                          // corrected z_{k-1} -> z_k
+          float* m_new = bf.ust + ne * (1 + (k_prev & 1));             // holds m_{k-2}, takes m_k
+          const float* m_km1 = bf.ust + ne * (1 + ((k_prev + 1) & 1));  // m_{k-1}
+          const float zk = z[a];
+          const float mm = zk - cf[0] * vg;
+          float xc = zk, m1 = 0.f;
+          if (k_prev >= 1) {
+            m1 = m_km1[el];
+            const float m2 = k_prev >= 2 ? m_new[el] : 0.f;
+            xc = cf[1] * xp[el] + cf[2] * mm + cf[3] * m1 + cf[4] * m2;
+          }
+          zn = cf[5] * xc + cf[6] * mm + cf[7] * m1;
+          xp[el] = xc;
+          m_new[el] = mm;
+        } else {
+          zn = z[a] + bf.dt[k_prev] * vg;
+        }
+        z[a] = zn;
+        xs[r][a] = zn;
+      }
+      __syncthreads();  // red is reused by the next pass; xs complete for the in-projection
     }
-    __syncthreads();
   } else {
-    for (int a = tid; a < dim; a += 256) xs[a] = z[a];
+    for (int e = tid; e < 16 * dim; e += 256) {
+      const int r = e / dim, a = e - r * dim, t = t0 + r;
+      if (t < tend) xs[r][a] = zptr(t)[a];
+    }
     __syncthreads();
   }
   if (k_next < 0) return;
-  AT* hs = static_cast<AT*>(bf.hs);
+  // in-projection (identical for both branches) on fp32 MFMA; hs of each branch with its
+  // own first-norm scale; the same row statistics for both rows
+  AT* hsw = static_cast<AT*>(bf.hs);
   const size_t stab = (size_t)d.nmod * 2 * d.D;
   const float* scl = bf.mod + (size_t)k_next * d.ntab * stab;  // table 0, norm 0, scale row
-  for (int n0 = 0; n0 < d.D; n0 += 256) {
-    const int n = n0 + tid;
-    float hn = to_f32(bi[n]);
-    for (int a = 0; a < dim; ++a) hn += xs[a] * to_f32(wi[(size_t)n * dim + a]);
-    const float sq = sum16(hn * hn);
+  const int kc_n = (dim + 31) / 32, ntn = d.D / 16;
+  for (int nt0 = w; nt0 < ntn; nt0 += 16) {
+    f32x4 acc[4];
+    float b0[4], s0[4], s1[4];
 #pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      const int m = rows[br];
-      bf.h[(size_t)m * d.D + n] = hn;
-      hs[sw_idx(m, n, d.D)] = to_elem<AT>(hn * (1.0f + scl[br * stab + n]));
-      if ((tid & 15) == 0) bf.ssq[(size_t)m * (d.D / 16) + n / 16] = sq;
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < kc_n; ++kc) {
+      const int a0 = kc * 32 + grp * 8;
+      WF wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = min(nt0 + 4 * j, ntn - 1) * 16 + r16;
+        wv[j] = load_frag(wi + (size_t)n * dim + min(a0, dim - 8));
+        if (kc == 0) {
+          b0[j] = to_f32(bi[n]);
+          s0[j] = 1.0f + scl[n];
+          s1[j] = 1.0f + scl[stab + n];
+        }
+      }
+      f32x8 xa;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xa[e] = xs[r16][min(a0 + e, 255)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x8 wb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wb[e] = a0 < dim ? to_f32(wv[j][e]) : 0.f;
+        acc[j] = mma(xa, wb, acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nt = nt0 + 4 * j;
+      if (nt >= ntn) break;
+      const int n = nt * 16 + r16;
+      float hn[4], sq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hn[i] = acc[j][i] + b0[j];
+        sq[i] = sum16(hn[i] * hn[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * grp + i;
+        if (t >= tend) continue;
+#pragma unroll
+        for (int br = 0; br < 2; ++br) {
+          const int m = br * d.H + t;
+          bf.h[(size_t)m * d.D + n] = hn[i];
+          hsw[sw_idx(m, n, d.D)] = to_elem<AT>(hn[i] * (br ? s1[j] : s0[j]));
+          if (r16 == 0) bf.ssq[(size_t)m * (d.D / 16) + nt] = sq[i];
+        }
+      }
     }
   }
 }
@@ -1726,10 +1801,12 @@ static hipError_t launch_one_wam(const Dims& d, const Bufs& b, const Plan& p, in
       return launch_gemm_tiled(d, b, g, EPI_RESID, d.D, st);
     }
     case 5:
-      hipLaunchKernelGGL((k_wam_out<bf16, bf16>), dim3(d.H), dim3(256), 0, st, d, b, k, k + 1 < d.N ? k + 1 : -1);
+      hipLaunchKernelGGL((k_wam_rows<bf16, bf16>), dim3((d.Tl + 15) / 16 + (d.H - d.Tl + 15) / 16), dim3(256), 0, st, d,
+                         b, k, k + 1 < d.N ? k + 1 : -1);
       return hipGetLastError();
     case 6:
-      hipLaunchKernelGGL((k_wam_out<bf16, bf16>), dim3(d.H), dim3(256), 0, st, d, b, -1, 0);
+      hipLaunchKernelGGL((k_wam_rows<bf16, bf16>), dim3((d.Tl + 15) / 16 + (d.H - d.Tl + 15) / 16), dim3(256), 0, st, d,
+                         b, -1, 0);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;
