@@ -16,8 +16,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libphyai.so")
 
 SOURCES = [os.path.join(CSRC, n)
-           for n in ("loop_b1.hip", "loop_persistent.hip", "gemm_tiled.hip", "tables.hip", "runtime.cpp")]
-HEADERS = [os.path.join(CSRC, n) for n in ("common.h", "kernels.h", "epilogue.h", "persistent.h")] + \
+           for n in ("loop.hip", "gemv.hip", "attention.hip", "update.hip", "loop_persistent.hip", "gemm_tiled.hip",
+                     "tables.hip", "runtime.cpp")]
+HEADERS = [os.path.join(CSRC, n) for n in ("common.h", "kernels.h", "epilogue.h", "launch.h", "persistent.h")] + \
     [os.path.join(INCLUDE, "phyai.h")]
 
 # Packed-fp32 VALU forms are kept out of every code object (they are not needed here and
@@ -39,7 +40,8 @@ def build(verbose: bool = False, phase_trace: bool = False) -> str:
     """Compile every source for gfx950 and link libphyai.so next to this file.
 
     phase_trace=True builds libphyai_trace.so instead: the same library with per-wave phase
-    timestamps recorded by the kernels (exported reader: phyai_phase_trace)."""
+    timestamps recorded by the kernels (exported readers phyai_phase_trace_gemv, _attn and
+    _update, and phyai_persist_trace for the persistent loop)."""
     cc = hipcc()
     objs = []
     objdir = os.path.join(PKG, "_build_trace" if phase_trace else "_build")

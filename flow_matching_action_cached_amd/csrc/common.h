@@ -19,16 +19,28 @@
 namespace phyai {
 
 // Optional per-phase timestamps (a build with -DPHYAI_PHASE_TRACE only): each wave's lane 0
-// stores the 100 MHz real-time counter at numbered points of a kernel into
-// g_phase_trace[(workgroup * 8 + wave) * 8 + slot] (workgroups < 2048, waves < 8); phyai_phase_trace() copies it out.
+// stores the 100 MHz real-time counter at numbered points of a kernel into this file's
+// g_phase_trace[(workgroup * 8 + wave) * 8 + slot] (workgroups < 2048, waves < 8); each
+// kernel file exports a reader (PHYAI_PHASE_TRACE_READER) that copies its array out.
 #ifdef PHYAI_PHASE_TRACE
-extern __device__ uint64_t g_phase_trace[4096 * 4 * 8];
+static __device__ uint64_t g_phase_trace[4096 * 4 * 8];
 #define PHASE_MARK(slot)                                                                          \
   do {                                                                                            \
     if ((threadIdx.x & 63) == 0 && blockIdx.x < 2048 && (threadIdx.x >> 6) < 8)                   \
       g_phase_trace[((size_t)blockIdx.x * 8 + (threadIdx.x >> 6)) * 8 + (slot)] =                 \
           __builtin_amdgcn_s_memrealtime();                                                       \
   } while (0)
+// Copy this file's timestamps out (host dst of 4096*4*8 uint64), then clear them.
+#define PHYAI_PHASE_TRACE_READER(fn)                                                                   \
+  extern "C" int fn(void* host_dst) {                                                                 \
+    static uint64_t zeros[4096 * 4 * 8];                                                               \
+    if (hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_phase_trace), sizeof(zeros), 0, hipMemcpyDeviceToHost) != \
+            hipSuccess ||                                                                              \
+        hipMemcpyToSymbol(HIP_SYMBOL(g_phase_trace), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) !=     \
+            hipSuccess)                                                                                \
+      return 4;                                                                                        \
+    return 0;                                                                                          \
+  }
 #else
 #define PHASE_MARK(slot) ((void)0)
 #endif

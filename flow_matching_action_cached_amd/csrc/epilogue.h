@@ -71,6 +71,13 @@ __device__ __forceinline__ float resid_store(const Dims& d, const Bufs& bf, int 
   return hn;
 }
 
+// GeGLU output of token row m, feature f from the gate and up pre-activations (norm folded
+// in): act = gelu_tanh(gate) * up, swizzled [Mpad][F] in the GEMM input type.
+template <class AT>
+__device__ __forceinline__ void geglu_store(const Dims& d, const Bufs& bf, int m, int f, float yg, float yu) {
+  static_cast<AT*>(bf.act)[sw_idx(m, f, d.F)] = to_elem<AT>(gelu_tanh(yg) * yu);
+}
+
 // LDS-tiled GEMM family (gemm_tiled.hip) for more than 64 token rows, bf16 only.
 // n_cols: output columns (gate/up: 2F); epi: Epi.
 hipError_t launch_gemm_tiled(const Dims& d, const Bufs& b, const GemmLaunch& g, int epi, int n_cols,

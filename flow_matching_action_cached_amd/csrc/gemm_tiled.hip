@@ -236,9 +236,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
           const float* cv = g.cvec + (size_t)(m / d.rows_per_tab) * bf.cv_stride;
           const float cg = cv[f], cu = cv[g.n_second + f];
           const float ri = rinv_s[m - tm * BM];
-          const float yg = ri * acc[i][j][e] + cg;
-          const float yu = ri * acc[i][j + 1][e] + cu;
-          static_cast<AT*>(bf.act)[sw_idx(m, f, d.F)] = to_elem<AT>(gelu_tanh(yg) * yu);
+          geglu_store<AT>(d, bf, m, f, ri * acc[i][j][e] + cg, ri * acc[i][j + 1][e] + cu);
         }
       }
     }

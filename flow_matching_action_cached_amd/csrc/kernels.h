@@ -1,5 +1,6 @@
 // Internal interface between the host runtime (runtime.cpp) and the HIP kernels
-// (loop_b1.hip, gemm_tiled.hip, tables.hip).  Not part of the public C ABI.
+// (loop.hip, gemv.hip, attention.hip, update.hip, gemm_tiled.hip, tables.hip).  Not part of
+// the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
