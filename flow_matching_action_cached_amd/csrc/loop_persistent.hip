@@ -16,21 +16,27 @@
 // and split merge, and their slice of the output projection's inputs; it owns the MLP columns
 // [x F/8, (x+1) F/8) of gate/up and the same slice of the down projection's inputs.  The two
 // residual sums (output projection over the 8 head groups, down projection over the 8 column
-// groups) are the only hand-offs between XCDs; the others stay inside one XCD's L2.
+// groups) and the out-projection rows are the only hand-offs between XCDs; the others stay
+// inside one XCD's L2.  Each residual sum is an all-reduce: every XCD adds the 8 partials of
+// its tile pairs itself (in XCD order, so all copies agree bit for bit), keeps the residual
+// of its tile pair in registers and writes its own copy of the next norm's input and its
+// statistics.
 //
 // Hand-offs.  A workgroup publishes a monotonic epoch flag when it has finished a phase (all
 // its stores performed); a consumer polls exactly the flags of what it reads: its XCD's 32
-// workgroups, the tile pairs of a residual sum, or the token rows of the out-projection.  The
-// 8 partial sums of a residual tile pair travel as (value, epoch tag) words to the pair's
-// reducer, which adds them in XCD order and writes the residual, the next norm's input and
-// its statistics.  Every wait is bounded: on
-// overrun a sticky abort word is set, every workgroup leaves at its next wait, and the host
-// reports a device error.
+// workgroups, the (tile pair, XCD) partials of a residual sum, or the token rows of the
+// out-projection.  An XCD's 32 flags are contiguous; flags that only that XCD reads are
+// stored plainly into its L2 and polled with scalar loads (which do not wait behind the
+// weight loads in flight), the others are stored and polled at agent scope.  Every wait is
+// bounded: on overrun a sticky abort word is set, every workgroup leaves at its next wait,
+// and the host reports a device error.
 //
-// Visibility.  Data that many workgroups read (norm inputs, statistics, q, o, act) is written
-// with agent-scope stores into per-(step, layer) buffers that nothing has read before in this
-// launch, so plain loads (served by L1 and L2) cannot meet stale lines; data read once (split
-// partials, the residual, the state, the chunk's own K/V rows) is read with agent-scope loads.
+// Visibility.  Data read across XCDs (the out-projection's outputs, residual partials, the
+// state, the chunk's own K/V rows) is written with agent-scope stores.  Data that many
+// workgroups read (norm inputs, statistics, q, o, act) lives in per-(step, layer) buffers
+// that nothing has read before in this launch, so plain loads (served by L1 and L2) cannot
+// meet stale lines; data read once (split partials, the out-projection's residual rows, the
+// state, the K/V rows) is read with agent-scope loads.
 #include "epilogue.h"
 #include "persistent.h"
 
@@ -42,14 +48,16 @@ namespace phyai {
 
 #ifdef PHYAI_PHASE_TRACE
 // Trace build only: per workgroup and phase, the real-time counter (100 MHz) when the wait
-// for the phase begins, when it ends, and when the phase's flag is published.
+// for the phase begins, when it ends, and when the phase's flag is published, then stamps
+// inside the phase (kTraceSlots per phase).
 constexpr int kTracePhases = 4096;
-__device__ uint64_t g_ptrace[256 * kTracePhases * 6];
+constexpr int kTraceSlots = 8;
+__device__ uint64_t g_ptrace[256 * kTracePhases * kTraceSlots];
 __device__ int g_ptrace_phase;  // not used for indexing; the phase index travels in a register
 #define PTRACE(phase, slot)                                                                        \
   do {                                                                                             \
     if (threadIdx.x == 0 && (phase) < kTracePhases)                                                \
-      g_ptrace[((size_t)blockIdx.x * kTracePhases + (phase)) * 6 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+      g_ptrace[((size_t)blockIdx.x * kTracePhases + (phase)) * kTraceSlots + (slot)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #else
 #define PTRACE(phase, slot) ((void)0)
@@ -75,11 +83,15 @@ __device__ __forceinline__ void st_u32_agent(unsigned* p, unsigned v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Stores: agent scope by default; AUX 0 (plain, into this XCD's L2) for data that only this
+// XCD's workgroups read.
+template <int AUX = kSC1>
 __device__ __forceinline__ void st_bf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, byte_off, 0, kSC1);
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, byte_off, 0, AUX);
 }
+template <int AUX = kSC1>
 __device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, byte_off, 0, kSC1);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, byte_off, 0, AUX);
 }
 __device__ __forceinline__ float ld_f32_sc1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSC1));
@@ -105,8 +117,10 @@ __device__ __forceinline__ bf16x8 bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t 
 
 // ------------------------------------------------------------------ hand-off waits
 // Lanes of wave 0 poll flags base[i * stride] (i < n) until each reaches epoch e; every wave
-// then meets at the workgroup barrier.  False once the loop is aborted (by this wait's
-// overrun or by another workgroup): the caller leaves the kernel.
+// then meets at the workgroup barrier.  With stride 0 the flags are those of workgroups
+// 0 .. n-1 in the XCD-major flag array (workgroup i at (i mod 8) 32 + i / 8).  False once the
+// loop is aborted (by this wait's overrun or by another workgroup): the caller leaves the
+// kernel.
 __device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int n, uint64_t e, int* lds_ok,
                            int skip = -1) {
   const int tid = threadIdx.x;
@@ -115,7 +129,7 @@ __device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int
     int ok = 1;
     for (int i = tid; i < n && ok; i += 64) {
       if (i == skip) continue;
-      const uint64_t* f = base + (size_t)i * stride;
+      const uint64_t* f = base + (stride ? (size_t)i * stride : (size_t)((i & 7) * 32 + (i >> 3)));
       unsigned spins = 0;
       while ((int64_t)(ld_flag(f) - e) < 0) {
         ++spins;
@@ -139,14 +153,86 @@ __device__ bool wait_flags(const PArgs& a, const uint64_t* base, int stride, int
   return *lds_ok != 0;
 }
 
+// 32 contiguous flags (256 B) all at epoch e or later, read with four scalar loads that miss
+// the scalar cache (glc) and read this XCD's L2, issued together and waited for once.  Scalar
+// loads wait only for scalar and LDS operations, not behind the vector loads in flight (the
+// next phase's weights, issued before the wait), which would hold a vector poll's result
+// until they have all returned.
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ bool flags32_reached(const uint64_t* f, uint64_t e) {
+  u32x16 v0, v1, v2, v3;
+  asm volatile(
+      "s_load_dwordx16 %0, %4, 0x0 glc\n\t"
+      "s_load_dwordx16 %1, %4, 0x40 glc\n\t"
+      "s_load_dwordx16 %2, %4, 0x80 glc\n\t"
+      "s_load_dwordx16 %3, %4, 0xc0 glc\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3)
+      : "s"(f)
+      : "memory");
+  bool ok = true;
+  auto chk = [&](const u32x16& v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t fv = ((uint64_t)v[2 * i + 1] << 32) | v[2 * i];
+      ok &= (int64_t)(fv - e) >= 0;
+    }
+  };
+  chk(v0);
+  chk(v1);
+  chk(v2);
+  chk(v3);
+  return ok;
+}
+
+// wait_flags for the 32 flags of this XCD's workgroups (contiguous, written by workgroups
+// that share this XCD's L2): wave 0 polls them with scalar loads.
+__device__ bool wait_local(const PArgs& a, const uint64_t* flags32, uint64_t e, int* lds_ok) {
+  PTRACE((int)(e - a.epoch0) + 1, 0);
+  if (threadIdx.x < 64) {
+    int ok = 1;
+    unsigned spins = 0;
+    for (;;) {
+      if (flags32_reached(flags32, e)) break;
+      ++spins;
+      if ((spins & 255) == 0 && ld_u32_agent(a.ctl) != 0) {
+        ok = 0;
+        break;
+      }
+      if (spins > kSpinMax) {
+        if (threadIdx.x == 0) {
+          st_u32_agent(a.ctl, 1u);
+          st_u32_agent(a.ctl + 1, (unsigned)(e - a.epoch0));
+        }
+        ok = 0;
+        break;
+      }
+    }
+    if (threadIdx.x == 0) *lds_ok = ok;
+  }
+  __syncthreads();
+  PTRACE((int)(e - a.epoch0) + 1, 1);
+  return *lds_ok != 0;
+}
+
 // All of this workgroup's stores are performed; then its flag takes epoch e.
 __device__ __forceinline__ void publish(uint64_t* flag, uint64_t e) {
   wait_all_mem();
   __syncthreads();
   if (threadIdx.x == 0) st_flag(flag, e);
 }
-__device__ __forceinline__ void publish_wg(const PArgs& a, uint64_t* flag, uint64_t e) {
-  publish(flag, e);
+// The end of a phase.  A flag that only this XCD's workgroups poll (scalar loads of this
+// XCD's L2) takes a plain store, which lands in that L2; one that other XCDs poll (agent-scope
+// loads) an agent-scope store.
+__device__ __forceinline__ void publish_wg(const PArgs& a, uint64_t* flag, uint64_t e, bool cross) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (cross)
+      st_flag(flag, e);
+    else
+      __hip_atomic_store(flag, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   PTRACE((int)(e - a.epoch0), 2);
 }
 
@@ -485,10 +571,11 @@ __device__ void merge_wg(const PArgs& a, const char* blk_kl, int b, int head, in
 }
 
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
-// One workgroup per token row m (as the launch-per-kernel form).  k_prev >= 0: final norm of
-// step k_prev (its input and statistics from that step's final buffers), v, x += dt v.
-// k_next >= 0: h = x W_in^T + b_in, and the first norm's input and statistics of step k_next.
-__device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds) {
+// One workgroup per token row m (as the launch-per-kernel form), on XCD x.  k_prev >= 0:
+// final norm of step k_prev (its input and statistics from XCD x's copy of that step's final
+// buffers), v, x += dt v.  k_next >= 0: h = x W_in^T + b_in, and the first norm's input and
+// statistics of step k_next, into every XCD's copy.
+__device__ void out_row(const PArgs& a, int m, int x, int k_prev, int k_next, char* lds) {
   const Dims& d = a.d;
   const Bufs& bf = a.b;
   float* xs = reinterpret_cast<float*>(lds);
@@ -499,8 +586,8 @@ __device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds
   const __amdgpu_buffer_rsrc_t rx = rsrc(bf.x, (uint32_t)(d.M * d.A * 4));
   if (k_prev >= 0) {
     const char* fin = a.fin + (size_t)k_prev * a.k_bytes;
-    const float* ssq = reinterpret_cast<const float*>(fin + a.o_ssqf);
-    const bf16* hsr = reinterpret_cast<const bf16*>(fin + a.o_hsf);
+    const float* ssq = reinterpret_cast<const float*>(fin + a.o_ssqf + (size_t)x * a.ssq_cb);
+    const bf16* hsr = reinterpret_cast<const bf16*>(fin + a.o_hsf + (size_t)x * a.hs_cb);
     const bf16* wo = static_cast<const bf16*>(bf.w_out);
     const int n16 = d.D / 16;
     float ss = 0.f;
@@ -567,9 +654,9 @@ __device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds
   const bf16* bi = static_cast<const bf16*>(bf.b_in);
   const float* scl = bf.mod + (size_t)k_next * d.nmod * 2 * d.D;  // norm 0, scale row
   char* blk = a.act + (size_t)k_next * d.L * a.kl_bytes;            // (k_next, layer 0)
-  const __amdgpu_buffer_rsrc_t rh = rsrc(bf.h, (uint32_t)(64 * d.D * 4));
-  const __amdgpu_buffer_rsrc_t rhs = rsrc(blk + a.o_hsa, (uint32_t)(64 * d.D * 2));
-  const __amdgpu_buffer_rsrc_t rss = rsrc(blk + a.o_ssqa, (uint32_t)(64 * (d.D / 16) * 4));
+  const __amdgpu_buffer_rsrc_t rh = rsrc(a.hx, (uint32_t)(64 * d.D * 4));
+  const __amdgpu_buffer_rsrc_t rhs = rsrc(blk + a.o_hsa, 8 * a.hs_cb);
+  const __amdgpu_buffer_rsrc_t rss = rsrc(blk + a.o_ssqa, 8 * a.ssq_cb);
   const int na = d.A / 8;
   const __amdgpu_buffer_rsrc_t rwi = rsrc(wi, (uint32_t)(d.D * d.A * 2));
   for (int n0 = 0; n0 < d.D; n0 += 256) {
@@ -587,22 +674,29 @@ __device__ void out_row(const PArgs& a, int m, int k_prev, int k_next, char* lds
 #pragma unroll
           for (int e = 0; e < 8; ++e) hn += xs[8 * (c0 + c) + e] * (float)wv[c][e];
     }
-    st_f32(rh, (uint32_t)(((size_t)m * d.D + n) * 4), hn);
-    st_bf16(rhs, (uint32_t)(sw_idx(m, n, d.D) * 2), hn * sc1);
+    const uint32_t oh = (uint32_t)(((size_t)m * d.D + n) * 4), ohs = (uint32_t)(sw_idx(m, n, d.D) * 2);
     const float sq = sum16(hn * hn);
-    if ((tid & 15) == 0) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + n / 16) * 4), sq);
+    const uint32_t oss = (uint32_t)(((size_t)m * (d.D / 16) + n / 16) * 4);
+    st_f32(rh, oh, hn);
+#pragma unroll
+    for (int xc = 0; xc < 8; ++xc) {
+      st_bf16(rhs, xc * a.hs_cb + ohs, hn * sc1);
+      if ((tid & 15) == 0) st_f32(rss, xc * a.ssq_cb + oss, sq);
+    }
   }
 }
 
 // ------------------------------------------------------------------ residual sums across XCDs
 // Tile pair p of a residual linear has one partial per XCD (its split of the input columns).
-// Every XCD but one stores its partial and raises its (pair, XCD) flag; the reducer (XCD
-// p mod 8) waits for the seven flags, adds the eight partials in XCD order, and writes the
-// residual h += sum, the next norm's input hs = h (1 + scale_next) and its statistics, then
-// the pair's epoch flag.
+// Workgroup p of every XCD stores its partial in the sum's slot (output projection 0, down
+// projection 1) and raises its (pair, XCD) flag, waits for the seven others, and adds the
+// eight partials in XCD order: every XCD gets the same sums bit for bit, keeps the residual
+// h += sum of its pair in registers and writes its own copy of the next norm's input
+// hs = h (1 + scale_next) and of its statistics.  A slot is written again two sums later,
+// after its writer has seen every other XCD's flag of the sum in between, raised after that
+// XCD's loads of the slot had returned.
 struct ResidPre {
-  float sc1[2];   // 1 + scale of the norm that consumes h, at this lane's column of tile nt
-  float h[2][4];  // residual rows of this wave's m-tile (reducer only)
+  float sc1[2];  // 1 + scale of the norm that consumes h, at this lane's column of tile nt
 };
 
 // Loads ahead of the phase's wait: the static scale of both tiles' columns.
@@ -611,75 +705,74 @@ __device__ __forceinline__ void resid_pre_static(ResidPre& rp, const float* scal
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) rp.sc1[nt] = 1.0f + scale_next[(2 * pair + nt) * 16 + r16];
 }
-// After the wait (the residual is written by the previous residual sum of the pair).
+// The residual rows of the pair (this wave's m-tile) as the out-projection rows wrote them at
+// the start of the step; the residual sums then keep them in registers.
 template <int MT>
-__device__ __forceinline__ void resid_pre_h(const PArgs& a, ResidPre& rp, int pair) {
+__device__ __forceinline__ void load_h0(const PArgs& a, float (&h)[2][4], int pair) {
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
+  const __amdgpu_buffer_rsrc_t rh = rsrc(a.hx, (uint32_t)(64 * d.D * 4));
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(w * 16 + grp * 4 + i, d.M - 1);
-      rp.h[nt][i] = w < MT ? ld_f32_sc1(rh, (uint32_t)(((size_t)m * d.D + (2 * pair + nt) * 16 + r16) * 4)) : 0.f;
+      h[nt][i] = w < MT ? ld_f32_sc1(rh, (uint32_t)(((size_t)m * d.D + (2 * pair + nt) * 16 + r16) * 4)) : 0.f;
     }
 }
 
-// The contributor waits for its partial's stores to be performed before raising its flag;
-// the reducer polls the seven flags with a few lanes, then loads the seven partials in one
-// round trip.  Partial layout: [pair][x][nt][w][64] f32x4.  False if the loop was aborted.
+// Partial layout: [slot][pair][x][nt][w][64] f32x4.  The partial's stores are performed before
+// the flag; a few lanes poll the seven other flags, then the seven partials are loaded in one
+// round trip.  hs_next / ssq_next: XCD x's copies.  False if the loop was aborted.
 template <int MT>
-__device__ bool resid_flagged(const PArgs& a, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp,
-                              char* hs_next, char* ssq_next, uint64_t e, int* lds_ok) {
+__device__ bool resid_allreduce(const PArgs& a, int slot, int pair, int x, const f32x4 (&tot)[2], const ResidPre& rp,
+                                float (&h)[2][4], char* hs_next, char* ssq_next, uint64_t e, int* lds_ok) {
   const Dims& d = a.d;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr uint32_t part_bytes = 2 * MT * 1024;
-  const __amdgpu_buffer_rsrc_t ws = rsrc(a.part + (size_t)pair * 8 * (part_bytes / 4), part_bytes * 8);
-  uint64_t* pflag = a.flag_pair + d.D / 32 + pair * 8;
-  const int rx = pair & 7;
-  if (x != rx) {
-    if (w < MT)
+  const size_t pair_floats = (size_t)8 * (part_bytes / 4);
+  const __amdgpu_buffer_rsrc_t ws = rsrc(a.part + ((size_t)slot * (d.D / 32) + pair) * pair_floats, part_bytes * 8);
+  uint64_t* pflag = a.flag_part + pair * 8;
+  if (w < MT)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        st_16_sc1(ws, x * part_bytes + ((nt * MT + w) * 64 + lane) * 16, __builtin_bit_cast(u32x4, tot[nt]));
-    publish(pflag + x, e);
-    return true;
-  }
-  // the seven other partials of this pair
-  if (!wait_flags(a, pflag, 1, 8, e, lds_ok, rx)) return false;
+    for (int nt = 0; nt < 2; ++nt)
+      st_16_sc1(ws, x * part_bytes + ((nt * MT + w) * 64 + lane) * 16, __builtin_bit_cast(u32x4, tot[nt]));
+  publish(pflag + x, e);
+  PTRACE((int)(e - a.epoch0), 6);
+  if (!wait_flags(a, pflag, 1, 8, e, lds_ok, x)) return false;
+  PTRACE((int)(e - a.epoch0), 7);
   if (w < MT) {
-    const __amdgpu_buffer_rsrc_t rh = rsrc(a.b.h, (uint32_t)(64 * d.D * 4));
     const __amdgpu_buffer_rsrc_t rhs = rsrc(hs_next, (uint32_t)(64 * d.D * 2));
     const __amdgpu_buffer_rsrc_t rss = rsrc(ssq_next, (uint32_t)(64 * (d.D / 16) * 4));
     u32x4 pv[2][8];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int x2 = 0; x2 < 8; ++x2) pv[nt][x2] = ld_16_sc1(ws, x2 * part_bytes + ((nt * MT + w) * 64 + lane) * 16);
+      for (int x2 = 0; x2 < 8; ++x2)
+        pv[nt][x2] = x2 == x ? __builtin_bit_cast(u32x4, tot[nt])
+                             : ld_16_sc1(ws, x2 * part_bytes + ((nt * MT + w) * 64 + lane) * 16);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x2 = 0; x2 < 8; ++x2) sum += x2 == rx ? tot[nt] : __builtin_bit_cast(f32x4, pv[nt][x2]);
+      for (int x2 = 0; x2 < 8; ++x2) sum += __builtin_bit_cast(f32x4, pv[nt][x2]);
       const int tile = 2 * pair + nt, col = tile * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = w * 16 + grp * 4 + i;
         float hn = 0.f;
         if (m < d.M) {
-          hn = rp.h[nt][i] + sum[i];
-          st_f32(rh, (uint32_t)(((size_t)m * d.D + col) * 4), hn);
-          st_bf16(rhs, (uint32_t)(sw_idx(m, col, d.D) * 2), hn * rp.sc1[nt]);
+          hn = h[nt][i] + sum[i];
+          h[nt][i] = hn;
+          st_bf16<0>(rhs, (uint32_t)(sw_idx(m, col, d.D) * 2), hn * rp.sc1[nt]);
         }
         const float sq = sum16(hn * hn);
-        if (r16 == 0 && m < d.M) st_f32(rss, (uint32_t)(((size_t)m * (d.D / 16) + tile) * 4), sq);
+        if (r16 == 0 && m < d.M) st_f32<0>(rss, (uint32_t)(((size_t)m * (d.D / 16) + tile) * 4), sq);
       }
     }
   }
-  publish(a.flag_pair + pair, e);
   return true;
 }
 
@@ -713,8 +806,9 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
   const uint64_t per_step = 6 * (uint64_t)L + 1;
   auto E = [&](int k, int l, int ph) { return e0 + 1 + (uint64_t)k * per_step + 6 * (uint64_t)l + ph; };
   auto E_out = [&](int k) { return e0 + 1 + (uint64_t)k * per_step + 6 * (uint64_t)L; };
-  uint64_t* myflag = a.flag_wg + wg;
-  const uint64_t* local_flags = a.flag_wg + x;                     // stride 8: this XCD's workgroups
+  // XCD-major flags: an XCD's 32 flags share two cache lines that no other XCD writes
+  uint64_t* myflag = a.flag_wg + x * 32 + c;
+  const uint64_t* local_flags = a.flag_wg + x * 32;
 
   // QKV tile pair pp of this XCD -> global column tiles
   auto qkv_tile = [&](int t) { return t < nq_t ? x * nq_t + t : qd / 16 + (t - nq_t); };
@@ -729,6 +823,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
   bool kvp_valid = false;
   float cq[2];  // norm-folded bias of the QKV unit's two tiles at this lane's column (or gate, up)
   ResidPre ro, rd;
+  float hreg[2][4] = {};  // residual rows of tile pair c (this wave's m-tile), kept across the step
   const int r16 = tid & 15;
   // weights and the static epilogue operands of this workgroup's first QKV unit of (k, l)
   auto pre_qkv = [&](int k, int l) {
@@ -743,8 +838,8 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
   };
 
   // ---- in-projection of step 0
-  if (wg < d.M) out_row(a, wg, -1, 0, lds);
-  publish_wg(a, myflag, e0);
+  if (wg < d.M) out_row(a, wg, x, -1, 0, lds);
+  publish_wg(a, myflag, e0, true);
   pre_qkv(0, 0);
 
   for (int k = 0; k < d.N; ++k) {
@@ -753,8 +848,8 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
       // ---------------- QKV (+ the chunk's K/V into the cache)
       {
         const uint64_t e = E(k, l, 0);
-        bool ok = l == 0 ? wait_flags(a, a.flag_wg, 1, d.M, k == 0 ? e0 : E_out(k - 1), &lds_ok)
-                         : wait_flags(a, a.flag_pair, 1, npair, E(k, l - 1, 5), &lds_ok);
+        bool ok = l == 0 ? wait_flags(a, a.flag_wg, 0, d.M, k == 0 ? e0 : E_out(k - 1), &lds_ok)
+                         : wait_local(a, local_flags, E(k, l - 1, 5), &lds_ok);
         if (!ok) return;
         const float* cv = bf.cvec + (size_t)k * bf.cv_stride + (size_t)l * d.qkv;
         const bf16* W = static_cast<const bf16*>(bf.w_qkv) + (size_t)l * d.qkv * d.D;
@@ -767,8 +862,9 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
             cq[1] = cv[(rt[1] < 0 ? rt[0] : rt[1]) * 16 + r16];
           }
           f32x4 tot[2];
-          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsa), d.D, 0,
-                                  reinterpret_cast<const float*>(blk + a.o_ssqa), tot, lds, (int)(e - e0));
+          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsa + (size_t)x * a.hs_cb), d.D, 0,
+                                  reinterpret_cast<const float*>(blk + a.o_ssqa + (size_t)x * a.ssq_cb), tot, lds,
+                                  (int)(e - e0));
           const float* rinv_s = reinterpret_cast<const float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
           if (w < MT) {
             const int lane = tid & 63, grp = lane >> 4;
@@ -818,7 +914,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           __syncthreads();  // LDS (partials, rinv) reused by the next unit
         }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, false);
         // the first block of this workgroup's attention unit, when it holds prefix rows only
         kvp_valid = false;
         if (c < att_units) {
@@ -833,25 +929,25 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
       // ---------------- attention over the cached prefix and the chunk
       {
         const uint64_t e = E(k, l, 1);
-        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 0), &lds_ok)) return;
+        if (!wait_local(a, local_flags, E(k, l, 0), &lds_ok)) return;
         for (int u = c; u < att_units; u += 32) {
           const int s = u % a.S, hl = (u / a.S) % hpx, b = u / a.S / hpx;
           attn_unit<DH>(a, blk, k, l, b, x * hpx + hl, s, kvp, kvp_valid && u == c, lds);
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, false);
         // output projection: weights of tile pair c over this XCD's heads, the next norm's scale
         if (c < npair) {
           load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * c, 2 * c + 1,
                      x * hpx * DH / 32);
-          if ((c & 7) == x) resid_pre_static(ro, bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D, c);
+          resid_pre_static(ro, bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D, c);
         }
       }
       // ---------------- merge of the key splits
       {
         const uint64_t e = E(k, l, 2);
-        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 1), &lds_ok)) return;
+        if (!wait_local(a, local_flags, E(k, l, 1), &lds_ok)) return;
         if (a.S > 1)
           for (int it = c; it < mrg_items; it += 32) {
             const int u = it % (DH / 32), jt = (it / (DH / 32)) % QTh, hl = it / (DH / 32) / QTh % hpx;
@@ -860,29 +956,24 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
             __syncthreads();  // LDS reused by the next item
           }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, false);
       }
       // ---------------- output projection (this XCD's heads) + residual across XCDs
       {
         const uint64_t e = E(k, l, 3);
-        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 2), &lds_ok)) return;
-        const float* scale_next = bf.mod + (((size_t)k * d.nmod + 2 * l + 1) * 2) * d.D;
-        for (int pp = c; pp < npair; pp += 32) {
-          const bool red = (pp & 7) == x;
-          if (pp != c) {
-            load_w<KO>(wo, static_cast<const bf16*>(bf.w_o) + (size_t)l * d.D * qd, d.D, qd, 2 * pp, 2 * pp + 1,
-                       x * hpx * DH / 32);
-            if (red) resid_pre_static(ro, scale_next, pp);
-          }
-          if (red) resid_pre_h<MT>(a, ro, pp);
+        if (!wait_local(a, local_flags, E(k, l, 2), &lds_ok)) return;
+        if (c < npair) {  // at most 32 pairs: one per workgroup
+          if (l == 0) load_h0<MT>(a, hreg, c);
           f32x4 tot[2];
           gemm_unit<MT, KO, false>(d, wo, reinterpret_cast<const bf16*>(blk + a.o_o), qd, x * hpx * DH / 32, nullptr,
                                    tot, lds, (int)(e - e0));
-          if (!resid_flagged<MT>(a, pp, x, tot, ro, blk + a.o_hsm, blk + a.o_ssqm, e, &lds_ok)) return;
+          if (!resid_allreduce<MT>(a, 0, c, x, tot, ro, hreg, blk + a.o_hsm + (size_t)x * a.hs_cb,
+                                   blk + a.o_ssqm + (size_t)x * a.ssq_cb, e, &lds_ok))
+            return;
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, false);
         if (c < gu_units) {
           const int j = x * gu_units + c;  // gate tile j, up tile F/16 + j
           load_w<KQ>(wq, static_cast<const bf16*>(bf.w_gu) + (size_t)l * 2 * d.F * d.D, 2 * d.F, d.D, j, d.F / 16 + j, 0);
@@ -894,7 +985,7 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
       // ---------------- gate/up + GeGLU (this XCD's MLP columns)
       {
         const uint64_t e = E(k, l, 4);
-        if (!wait_flags(a, a.flag_pair, 1, npair, E(k, l, 3), &lds_ok)) return;
+        if (!wait_local(a, local_flags, E(k, l, 3), &lds_ok)) return;
         const float* cv = bf.cvec + (size_t)k * bf.cv_stride + bf.cv_gu_off + (size_t)l * 2 * d.F;
         const __amdgpu_buffer_rsrc_t ract = rsrc(blk + a.o_act, (uint32_t)(64 * d.F * 2));
         for (int u = c; u < gu_units; u += 32) {
@@ -906,8 +997,9 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
             cq[1] = cv[d.F + j * 16 + r16];
           }
           f32x4 tot[2];
-          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsm), d.D, 0,
-                                  reinterpret_cast<const float*>(blk + a.o_ssqm), tot, lds, (int)(e - e0));
+          gemm_unit<MT, KQ, true>(d, wq, reinterpret_cast<const bf16*>(blk + a.o_hsm + (size_t)x * a.hs_cb), d.D, 0,
+                                  reinterpret_cast<const float*>(blk + a.o_ssqm + (size_t)x * a.ssq_cb), tot, lds,
+                                  (int)(e - e0));
           const float* rinv_s = reinterpret_cast<const float*>(lds + sizeof(f32x4) * 4 * 2 * MT * 64);
           if (w < MT) {
             const int grp = (tid & 63) >> 4;
@@ -923,50 +1015,45 @@ __global__ __launch_bounds__(256) void k_loop_persistent(PArgs a) {
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, false);
         if (c < npair) {
           load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * c, 2 * c + 1,
                      x * (d.F / 256));
           const int jn = (l + 1 < L) ? 2 * (l + 1) : 2 * L;
-          if ((c & 7) == x) resid_pre_static(rd, bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D, c);
+          resid_pre_static(rd, bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D, c);
         }
       }
       // ---------------- down projection (this XCD's MLP columns) + residual across XCDs
       {
         const uint64_t e = E(k, l, 5);
-        if (!wait_flags(a, local_flags, 8, 32, E(k, l, 4), &lds_ok)) return;
-        const int jn = (l + 1 < L) ? 2 * (l + 1) : 2 * L;
-        const float* scale_next = bf.mod + (((size_t)k * d.nmod + jn) * 2) * d.D;
+        if (!wait_local(a, local_flags, E(k, l, 4), &lds_ok)) return;
         char* nblk = l + 1 < L ? a.act + ((size_t)k * L + l + 1) * a.kl_bytes : nullptr;
         char* fin = a.fin + (size_t)k * a.k_bytes;
-        char* hs_next = nblk ? nblk + a.o_hsa : fin + a.o_hsf;
-        char* ssq_next = nblk ? nblk + a.o_ssqa : fin + a.o_ssqf;
-        for (int pp = c; pp < npair; pp += 32) {
-          const bool red = (pp & 7) == x;
-          if (pp != c) {
-            load_w<KD>(wd, static_cast<const bf16*>(bf.w_d) + (size_t)l * d.D * d.F, d.D, d.F, 2 * pp, 2 * pp + 1,
-                       x * (d.F / 256));
-            if (red) resid_pre_static(rd, scale_next, pp);
-          }
-          if (red) resid_pre_h<MT>(a, rd, pp);
+        char* hs_next = (nblk ? nblk + a.o_hsa : fin + a.o_hsf) + (size_t)x * a.hs_cb;
+        char* ssq_next = (nblk ? nblk + a.o_ssqa : fin + a.o_ssqf) + (size_t)x * a.ssq_cb;
+        if (c < npair) {
           f32x4 tot[2];
           gemm_unit<MT, KD, false>(d, wd, reinterpret_cast<const bf16*>(blk + a.o_act), d.F, x * (d.F / 256), nullptr,
                                    tot, lds, (int)(e - e0));
-          if (!resid_flagged<MT>(a, pp, x, tot, rd, hs_next, ssq_next, e, &lds_ok)) return;
+          if (!resid_allreduce<MT>(a, 1, c, x, tot, rd, hreg, hs_next, ssq_next, e, &lds_ok)) return;
           __syncthreads();
         }
         PTRACE((int)(e - e0), 5);
-        publish_wg(a, myflag, e);
+        publish_wg(a, myflag, e, l + 1 == L);
         if (l + 1 < L) pre_qkv(k, l + 1);
       }
     }
     // ---------------- final norm, out-projection, Euler update, next in-projection
     {
       const uint64_t e = E_out(k);
-      if (!wait_flags(a, a.flag_pair, 1, npair, E(k, L - 1, 5), &lds_ok)) return;
-      if (wg < d.M) out_row(a, wg, k, k + 1 < d.N ? k + 1 : -1, lds);
+      // a row's workgroup overwrites every XCD's copy of h: it waits for every workgroup's
+      // last residual sum (the others only for their own XCD's)
+      const bool ok = wg < d.M ? wait_flags(a, a.flag_wg, 1, kPersistWGs, E(k, L - 1, 5), &lds_ok)
+                               : wait_local(a, local_flags, E(k, L - 1, 5), &lds_ok);
+      if (!ok) return;
+      if (wg < d.M) out_row(a, wg, x, k, k + 1 < d.N ? k + 1 : -1, lds);
       PTRACE((int)(e - e0), 5);
-      publish_wg(a, myflag, e);
+      publish_wg(a, myflag, e, true);
       if (k + 1 < d.N) pre_qkv(k + 1, 0);
     }
   }
@@ -979,7 +1066,8 @@ bool persistent_supported(const Dims& d, WDtype wt) {
   if (wt != W_BF16 || d.joint || d.M > 64 || d.rope_theta > 0.f || d.gated) return false;
   if (d.Hq % 8 || d.Hq % d.Hkv) return false;
   const int hpx = d.Hq / 8;
-  if ((hpx * d.dh) % 128 || d.D % 256 || d.F % 1024 || d.A > 256) return false;
+  // D <= 1024: at most 32 residual tile pairs, one per workgroup of an XCD
+  if ((hpx * d.dh) % 128 || d.D % 256 || d.D > 1024 || d.F % 1024 || d.A > 256) return false;
   const int MT = (d.M + 15) / 16;
   const int KQ = d.D / 128, KO = hpx * d.dh / 128, KD = d.F / 1024;
   if (d.dh == 256 && MT == 4 && KQ == 8 && KO == 2 && KD == 4) return true;   // pi0.5-shaped expert
@@ -991,18 +1079,20 @@ PersistLayout persistent_layout(const Dims& d) {
   PersistLayout p{};
   auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
   const size_t qd = (size_t)d.Hq * d.dh;
+  p.hs_cb = a256(64 * d.D * 2);
+  p.ssq_cb = a256(64 * (d.D / 16) * 4);
   size_t off = 0;
-  p.o_hsa = off; off = a256(off + 64 * d.D * 2);
-  p.o_ssqa = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.o_hsa = off; off += 8 * p.hs_cb;
+  p.o_ssqa = off; off += 8 * p.ssq_cb;
   p.o_q = off; off = a256(off + 64 * qd * 2);
   p.o_o = off; off = a256(off + 64 * qd * 2);
-  p.o_hsm = off; off = a256(off + 64 * d.D * 2);
-  p.o_ssqm = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.o_hsm = off; off += 8 * p.hs_cb;
+  p.o_ssqm = off; off += 8 * p.ssq_cb;
   p.o_act = off; off = a256(off + 64 * (size_t)d.F * 2);
   p.kl_bytes = off;
   off = 0;
-  p.o_hsf = off; off = a256(off + 64 * d.D * 2);
-  p.o_ssqf = off; off = a256(off + 64 * (d.D / 16) * 4);
+  p.o_hsf = off; off += 8 * p.hs_cb;
+  p.o_ssqf = off; off += 8 * p.ssq_cb;
   p.k_bytes = off;
   return p;
 }
@@ -1017,8 +1107,9 @@ static void attn_split(const Dims& d, int hpx, int& S, int& bps) {
   S = (nblk + bps - 1) / bps;
 }
 
-// [pair][x][nt][m-tile (<= 4)][64 lanes] f32x4
-size_t persistent_part_floats(const Dims& d) { return (size_t)(d.D / 32) * 8 * 2 * 4 * 64 * 4; }
+// [slot][pair][x][nt][m-tile (<= 4)][64 lanes] f32x4
+size_t persistent_part_floats(const Dims& d) { return (size_t)2 * (d.D / 32) * 8 * 2 * 4 * 64 * 4; }
+size_t persistent_hx_floats(const Dims& d) { return (size_t)64 * d.D; }
 
 size_t persistent_attn_floats(const Dims& d) {
   int S, bps;
@@ -1040,8 +1131,10 @@ hipError_t enqueue_denoise_persistent(const Dims& d, const Bufs& b, const Persis
   a.o_hsm = (uint32_t)lay.o_hsm; a.o_ssqm = (uint32_t)lay.o_ssqm; a.o_act = (uint32_t)lay.o_act;
   a.fin = pb.fin;
   a.k_bytes = (uint32_t)lay.k_bytes; a.o_hsf = (uint32_t)lay.o_hsf; a.o_ssqf = (uint32_t)lay.o_ssqf;
+  a.hs_cb = (uint32_t)lay.hs_cb; a.ssq_cb = (uint32_t)lay.ssq_cb;
   a.flag_wg = pb.flag_wg;
-  a.flag_pair = pb.flag_pair;
+  a.flag_part = pb.flag_part;
+  a.hx = pb.hx;
   a.ctl = pb.ctl;
   a.part = pb.part;
   a.attn_ws = pb.attn_ws;
@@ -1066,10 +1159,11 @@ uint64_t persistent_phases(const Dims& d) { return 1 + (uint64_t)d.N * (6 * (uin
 
 #ifdef PHYAI_PHASE_TRACE
 // Trace build only: copy the persistent loop's phase timestamps out (host dst of
-// 256 * 4096 * 6 uint64: per workgroup and phase, wait begin, wait end, publish, products done,
-// cross-wave sum done, epilogue issued), then clear.
+// 256 * 4096 * 8 uint64: per workgroup and phase, wait begin, wait end, publish, products done,
+// cross-wave sum done, epilogue issued, residual partial's flag raised, other partials'
+// wait ended), then clear.
 extern "C" int phyai_persist_trace(void* host_dst) {
-  static uint64_t zeros[256 * phyai::kTracePhases * 6];
+  static uint64_t zeros[256 * phyai::kTracePhases * phyai::kTraceSlots];
   if (hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(phyai::g_ptrace), sizeof(zeros), 0, hipMemcpyDeviceToHost) !=
           hipSuccess ||
       hipMemcpyToSymbol(HIP_SYMBOL(phyai::g_ptrace), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) != hipSuccess)

@@ -204,9 +204,10 @@ void alloc_persistent(phyai_ctx* c, int n_steps) {
   Layout pl;
   const size_t o_act = pl.take(lay.kl_bytes * (size_t)n_steps * d.L);
   const size_t o_fin = pl.take(lay.k_bytes * (size_t)n_steps);
-  const size_t o_fw = pl.take(kPersistWGs * 8), o_fp = pl.take((size_t)(d.D / 32) * 9 * 8);
+  const size_t o_fw = pl.take(kPersistWGs * 8), o_fp = pl.take((size_t)(d.D / 32) * 8 * 8);
   const size_t o_ctl = pl.take(16);
   const size_t o_part = pl.take(persistent_part_floats(d) * 4), o_attn = pl.take(attn_f * 4);
+  const size_t o_hx = pl.take(persistent_hx_floats(d) * 4);
   if (hipMalloc(&c->pmem, pl.off) != hipSuccess) {
     c->pmem = nullptr;
     return;
@@ -220,9 +221,10 @@ void alloc_persistent(phyai_ctx* c, int n_steps) {
   c->pb.act = base + o_act;
   c->pb.fin = base + o_fin;
   c->pb.flag_wg = reinterpret_cast<uint64_t*>(base + o_fw);
-  c->pb.flag_pair = reinterpret_cast<uint64_t*>(base + o_fp);
+  c->pb.flag_part = reinterpret_cast<uint64_t*>(base + o_fp);
   c->pb.ctl = reinterpret_cast<unsigned*>(base + o_ctl);
   c->pb.part = reinterpret_cast<float*>(base + o_part);
+  c->pb.hx = reinterpret_cast<float*>(base + o_hx);
   c->pb.attn_ws = reinterpret_cast<float*>(base + o_attn);
   c->p_steps = n_steps;
   c->p_epoch = 1;
@@ -238,9 +240,7 @@ phyai_status check_persistent(phyai_ctx* c) {
   if (ctl[0] == 0) return PHYAI_OK;
   const Dims d = launch_dims(c, 1, c->cfg.max_prefix_len, c->p_steps);
   HIPCHK(c, hipMemset(c->pb.flag_wg, 0, kPersistWGs * 8));
-  HIPCHK(c, hipMemset(c->pb.flag_pair, 0, (size_t)(d.D / 32) * 9 * 8));
-  // the residual words carry epoch tags: none may match an epoch of the restarted count
-  HIPCHK(c, hipMemset(c->pb.part, 0, persistent_part_floats(d) * 4));
+  HIPCHK(c, hipMemset(c->pb.flag_part, 0, (size_t)(d.D / 32) * 8 * 8));
   HIPCHK(c, hipMemset(c->pb.ctl, 0, 16));
   c->p_epoch = 1;
   char msg[160];
