@@ -35,15 +35,15 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 # loop kernels and their ids for phyai_enqueue_kernel_repeat; "attn_merge" combines the
 # key splits of the few-row attention (its own launch), and has no algorithmic bytes of its own
-# HBM bytes per launch of the batch-1 loop kernels (single-kernel repeats of layer 0) from the
+# HBM bytes per launch of the batch-1 loop kernels (dispatches inside the loop) from the
 # rocprofv3 FETCH_SIZE and WRITE_SIZE passes summarised in profiles/pi05_b1_loop_kernels.md:
 # raw KiB scaled by what the same counters read for a 256 MiB device-to-device copy (fetch x2.0,
 # write x1.0).  They describe the kernel sources they were taken on: the hash covers every
 # source file of the library, and any change makes the bench report traffic null.
 PROFILED_TRAFFIC = {
-    "sources_sha256": "2e6e039a7e74814fc03c6085f4428e596e95592e6993fb04233e04637a3a317d",
-    "bytes": {"qkv": 6889747, "attention": 8964253, "attn_merge": 6811925, "o_proj": 7570932,
-              "gate_up": 18529280, "down": 13640429, "out_euler": 2533650},
+    "sources_sha256": "e62bb12475ed10164d58f56f165a1faa6fd34051ae5eed41e9a80395859e7691",
+    "bytes": {"qkv": 6890497, "attention": 8951298, "attn_merge": 6812672, "o_proj": 7587964,
+              "gate_up": 18531329, "down": 13653985, "out_euler": 2142132},
 }
 
 
@@ -258,6 +258,62 @@ def cpu_baseline(d, inputs):
     return out
 
 
+PHASE_NAMES = ["QKV", "attention", "merge", "O + residual sum", "gate/up", "down + residual sum"]
+
+
+def persistent_trace(d, ex, noise, out, np, torch):
+    """Per-phase breakdown of the persistent loop (phase-trace build: per workgroup and phase,
+    real-time stamps at 100 MHz of the wait's begin and end and of the flag's publication).
+    A phase's span on an XCD runs from that XCD's last flag of the previous phase to its last
+    flag of this one; the hand-off lag from that previous flag to a workgroup's wait end."""
+    lib = ex._lib
+    lib.phyai_persist_trace.argtypes = [ctypes.c_void_p]
+    slots, max_phases = 8, 4096
+    buf = np.zeros(256 * max_phases * slots, np.uint64)
+    ex.set_persistent(True)
+    if ex.loop_form(1) != 1:
+        raise RuntimeError("the persistent loop form is not available for this workload")
+    for _ in range(3):
+        ex.denoise(noise, out)
+    ex.sync()
+    lib.phyai_persist_trace(buf.ctypes.data)  # clear
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    ex.denoise(noise, out)
+    b.record()
+    ex.sync()
+    if lib.phyai_persist_trace(buf.ctypes.data) != 0:
+        raise RuntimeError("phyai_persist_trace failed")
+    L = d.n_layers
+    n_ph = 1 + d.n_steps * (6 * L + 1)
+    t = buf.reshape(256, max_phases, slots)[:, :n_ph].astype(np.int64)
+    xcd = np.arange(256) & 7
+
+    def kind(p):
+        q = (p - 1) % (6 * L + 1)
+        return "out/Euler/in" if q == 6 * L else PHASE_NAMES[q % 6]
+
+    rows = {}
+    for p in range(2, n_ph):
+        for x in range(8):
+            m = xcd == x
+            prev = t[m, p - 1, 2].max()
+            rows.setdefault(kind(p), []).append(((t[m, p, 2].max() - prev) / 100.0,
+                                                 np.median(t[m, p, 1] - prev) / 100.0,
+                                                 np.median(t[m, p, 2] - t[m, p, 1]) / 100.0))
+    print(f"persistent loop, {d.n_layers} layers x {d.n_steps} steps, batch 1: traced chunk "
+          f"{a.elapsed_time(b):.3f} ms ({n_ph} phases)")
+    print("phase                 span_us  lag_us  work_us   (medians over 8 XCDs x instances)")
+    per_layer = 0.0
+    for k in PHASE_NAMES + ["out/Euler/in"]:
+        v = np.array(rows[k])
+        med = np.median(v, axis=0)
+        if k != "out/Euler/in":
+            per_layer += med[0]
+        print(f"{k:20s} {med[0]:8.2f} {med[1]:7.2f} {med[2]:8.2f}")
+    print(f"sum of the layer's phase spans: {per_layer:.2f} us")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,9 +322,12 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
-    ap.add_argument("--variants", default="int4,rope,gated,prefill,capsule,b32,wam,wam_unipc,wam_tp4",
+    ap.add_argument("--variants", default="int4,rope,gated,prefill,persistent,capsule,b32,wam,wam_unipc,wam_tp4",
                     help="comma-separated variants to measure after the batch-1 line: int4, rope, gated, "
-                         "prefill, capsule, b32, wam, wam_unipc (needs wam), wam_tp4")
+                         "prefill, persistent, capsule, b32, wam, wam_unipc (needs wam), wam_tp4")
+    ap.add_argument("--persistent-trace", action="store_true",
+                    help="instead of the bench line: run the batch-1 loop as the persistent kernel with the "
+                         "phase-trace build (libphyai_trace.so) and print its per-phase breakdown")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device-to-device (a kernel of "
                          "known traffic for calibrating hardware byte counters)")
@@ -283,6 +342,8 @@ def main():
     import synth
     import flow_matching_action_cached_amd as fm
 
+    if args.persistent_trace:
+        fm.load_library(fm.LIB_PATH.replace("libphyai.so", "libphyai_trace.so"))
     d = synth.CONFIGS["pi05"]
     inputs = synth.make_expert_inputs(d, 0)
     w, kp, vp, noise = device_inputs(d, inputs, torch)
@@ -292,6 +353,10 @@ def main():
     ex.set_timestep_tables(schedule(d.n_steps))
     out = torch.empty_like(noise)
     print(f"[bench] setup done: {d}", file=sys.stderr, flush=True)
+    if args.persistent_trace:
+        persistent_trace(d, ex, noise, out, np, torch)
+        ex.close()
+        return
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -473,6 +538,30 @@ def main():
         variants["prefill_816_batch1"] = {"ms_per_prefix": round(msp, 4), "algorithmic_tflop": round(pf / 1e12, 4),
                                           "mfma_frac": round(pf / (msp * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         print(f"[bench] prefill variant: {msp:.4f} ms per prefix", file=sys.stderr, flush=True)
+
+    if "persistent" in todo:
+        # the same batch-1 workload as one persistent kernel (opt-in loop form)
+        ep = fm.ActionExpert.from_dims(d)
+        ep.set_weights(w)
+        ep.set_prefix_kv(kp, vp)
+        ep.set_timestep_tables(schedule(d.n_steps))
+        ep.set_persistent(True)
+        form = ep.loop_form(1)
+        for _ in range(args.warmup):
+            ep.denoise(noise, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            ep.denoise(noise, out)
+        b.record()
+        ep.sync()
+        msq = a.elapsed_time(b) / args.steps
+        ep.close()
+        variants["persistent_batch1"] = {"ms_per_chunk": round(msq, 4), "chunks_per_s": round(1000.0 / msq, 2),
+                                         "loop_form": "persistent" if form == 1 else "graph",
+                                         "hbm_frac": round(chunk_bytes(d) / (msq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] persistent variant: {msq:.4f} ms/chunk (form {form})", file=sys.stderr, flush=True)
 
     if "capsule" in todo:
         # execution-state capsules of the 816-token prefix: save (async kernels), restore
