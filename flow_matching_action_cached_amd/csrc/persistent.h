@@ -20,7 +20,8 @@ struct PersistLayout {
 struct PersistBufs {
   char* act;            // N * L activation blocks
   char* fin;            // N final blocks
-  uint64_t* flag_wg;    // [kPersistWGs] last finished phase (epoch) of each workgroup
+  uint64_t* flag_wg;    // [8][32] last finished phase (epoch) of each workgroup, XCD-major:
+                        // workgroup w (XCD w mod 8, index w / 8 there) at (w mod 8) 32 + w / 8
   uint64_t* flag_part;  // [D/32][8] last residual partial (epoch) of each (tile pair, XCD)
   unsigned* ctl;        // [0] abort word (sticky until the host resets it), [1] failing epoch, [2] placement
   float* part;          // residual partials, two slots (output projection, down projection)
