@@ -50,10 +50,13 @@ def _run(d, inputs, persistent=True, reps=1, max_batch=None):
     return outs, form
 
 
-@pytest.mark.parametrize("batch,chunk,prefix", [(1, 16, 64), (2, 16, 64), (4, 16, 100), (1, 50, 64), (3, 20, 1)])
+@pytest.mark.parametrize("batch,chunk,prefix", [(1, 16, 64), (2, 16, 64), (4, 16, 100), (1, 50, 64), (3, 20, 1),
+                                                (4, 16, 330), (1, 16, 1100)])
 def test_small_persistent_matches_oracle(batch, chunk, prefix):
-    """Reduced shape: 1-4 samples (16 to 64 token rows: one to four row tiles, ragged), one-
-    and several-block key splits, a one-token prefix."""
+    """Reduced shape: 1-4 samples (16 to 64 token rows: one to four row tiles, ragged), a
+    one-token prefix, one-block key splits, and two-block splits with a one-block last split
+    (4 x 16 rows over 346 keys: 11 blocks in 6 splits; 16 rows over 1116 keys: 35 blocks in
+    18 splits)."""
     d = dataclasses.replace(SMALL, batch=batch, chunk_len=chunk, prefix_len=prefix)
     _say(f"case: persistent small, batch {batch}, chunk {chunk}, prefix {prefix}")
     inp = synth.make_expert_inputs(d, 0)
