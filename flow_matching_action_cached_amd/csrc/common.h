@@ -117,6 +117,22 @@ __host__ __device__ __forceinline__ int sw4_shift(int k) {
 }
 
 // fp32 -> storage element (bf16: round to nearest even).
+// Store of an activation that a later launch reads.  WT: write-through (agent scope), the
+// line goes out to memory at once instead of staying dirty in this XCD's L2 until the
+// write-back at the end of the kernel -- cheaper for the few kilobytes a weight-streaming
+// GEMM's workgroup writes, dearer for the megabytes of a tiled GEMM's.
+template <bool WT, class T>
+__device__ __forceinline__ void st_act(T* p, T v) {
+  if constexpr (!WT) {
+    *p = v;
+  } else if constexpr (sizeof(T) == 4) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(p), __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 template <class T> __device__ __forceinline__ T to_elem(float v);
 template <> __device__ __forceinline__ float to_elem<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 to_elem<bf16>(float v) { return (bf16)v; }

@@ -44,38 +44,41 @@ __device__ __forceinline__ float rope_rotate(const Dims& d, int m, int col, floa
 }
 
 // QKV output y of token row m, column col: q rows go to q [M][Hq*dh]; the chunk's own
-// K and V go straight into the cache after the prefix rows (V transposed).
-template <class AT>
+// K and V go straight into the cache after the prefix rows (V transposed).  WT: write-through
+// stores (st_act), for the weight-streaming GEMMs.
+template <class AT, bool WT = false>
 __device__ __forceinline__ void qkv_store(const Dims& d, const Bufs& bf, int layer, int m, int col, float y) {
   const int qd = d.Hq * d.dh, kd = d.Hkv * d.dh;
   const int b = m / d.H, t = m % d.H;
   if (col < qd) {
-    static_cast<AT*>(bf.q)[(size_t)m * qd + col] = to_elem<AT>(y);
+    st_act<WT>(static_cast<AT*>(bf.q) + (size_t)m * qd + col, to_elem<AT>(y));
   } else if (col < qd + kd) {
     const int r = (col - qd) / d.dh, dd = (col - qd) % d.dh;
-    static_cast<AT*>(bf.kc)[((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd] = to_elem<AT>(y);
+    st_act<WT>(static_cast<AT*>(bf.kc) + ((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.KS + d.P + t) * d.dh + dd,
+          to_elem<AT>(y));
   } else {
     const int r = (col - qd - kd) / d.dh, dd = (col - qd - kd) % d.dh;
-    static_cast<AT*>(bf.vt)[((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t] = to_elem<AT>(y);
+    st_act<WT>(static_cast<AT*>(bf.vt) + ((((size_t)b * d.Lc + layer) * d.Hkv + r) * d.dh + dd) * d.KS + d.P + t,
+          to_elem<AT>(y));
   }
 }
 
 // Residual update of token row m, column col: h += delta; hs = h * (1 + scale of the next
 // norm) in the GEMM input type (swizzled).  Returns the new h (for the row statistics).
-template <class AT>
+template <class AT, bool WT = false>
 __device__ __forceinline__ float resid_store(const Dims& d, const Bufs& bf, int m, int col, float h_old, float delta,
                                              float sc1) {
   const float hn = h_old + delta;
-  bf.h[(size_t)m * d.D + col] = hn;
-  static_cast<AT*>(bf.hs)[sw_idx(m, col, d.D)] = to_elem<AT>(hn * sc1);
+  st_act<WT>(bf.h + (size_t)m * d.D + col, hn);
+  st_act<WT>(static_cast<AT*>(bf.hs) + sw_idx(m, col, d.D), to_elem<AT>(hn * sc1));
   return hn;
 }
 
 // GeGLU output of token row m, feature f from the gate and up pre-activations (norm folded
 // in): act = gelu_tanh(gate) * up, swizzled [Mpad][F] in the GEMM input type.
-template <class AT>
+template <class AT, bool WT = false>
 __device__ __forceinline__ void geglu_store(const Dims& d, const Bufs& bf, int m, int f, float yg, float yu) {
-  static_cast<AT*>(bf.act)[sw_idx(m, f, d.F)] = to_elem<AT>(gelu_tanh(yg) * yu);
+  st_act<WT>(static_cast<AT*>(bf.act) + sw_idx(m, f, d.F), to_elem<AT>(gelu_tanh(yg) * yu));
 }
 
 // LDS-tiled GEMM family (gemm_tiled.hip) for more than 64 token rows, bf16 only.

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
       float y = rinv_s[m] * tot[0][i] + epi_c0;
       if (d.rope_theta > 0.f) y = rope_rotate(d, m, col, y, __shfl_xor(y, 1, 64));  // all lanes shuffle
       if (m >= d.M) continue;
-      qkv_store<AT>(d, bf, g.layer, m, col, y);
+      qkv_store<AT, true>(d, bf, g.layer, m, col, y);
     }
   } else if constexpr (EPI == EPI_RESID) {
     const int col = nrow[0] + r16;
@@ -271,9 +271,9 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + grp * 4 + i;
-      const float hn = m < d.M ? resid_store<AT>(d, bf, m, col, epi_h[i], epi_c1 * tot[0][i], sc1) : 0.f;
+      const float hn = m < d.M ? resid_store<AT, true>(d, bf, m, col, epi_h[i], epi_c1 * tot[0][i], sc1) : 0.f;
       const float sq = sum16(hn * hn);
-      if (r16 == 0 && m < d.M) bf.ssq[(size_t)m * (d.D / 16) + tile] = sq;
+      if (r16 == 0 && m < d.M) st_act<true>(bf.ssq + (size_t)m * (d.D / 16) + tile, sq);
     }
   } else {  // EPI_GEGLU
     const int f = nrow[0] + r16;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + grp * 4 + i;
       if (m >= d.M) continue;
-      geglu_store<AT>(d, bf, m, f, rinv_s[m] * tot[0][i] + epi_c0, rinv_s[m] * tot[NT - 1][i] + epi_c1);
+      geglu_store<AT, true>(d, bf, m, f, rinv_s[m] * tot[0][i] + epi_c0, rinv_s[m] * tot[NT - 1][i] + epi_c1);
     }
   }
   PHASE_MARK(7);
