@@ -105,7 +105,26 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.phyai_set_timestep_tables(None, None, 0) == 1
     assert lib.phyai_set_graph_mode(None, 1) == 1
     assert lib.phyai_get_modulation(None, None) == 1
+    assert lib.phyai_denoise_noalloc(None, None, 1, 1, None) == 1
+    assert lib.phyai_time_loop_stages(None, None, 1, 1, None, None) == 1
+    assert lib.phyai_set_persistent(None, 1) == 1
+    assert lib.phyai_loop_form(None, 1) == -1
+    assert lib.phyai_enqueue_kernel_repeat(None, 0, 0, 1) == 1
     lib.phyai_destroy(None)
+
+
+def test_unipc_weights_argument_checks(lib):
+    """The host-side UniPC step weights reject what they cannot take, without a device."""
+    f = ctypes.c_float
+    out = (f * 64)()
+    dec = (f * 3)(1.0, 0.6, 0.2)
+    assert lib.phyai_unipc_weights(None, 3, 1, out) == 1                       # null schedule
+    assert lib.phyai_unipc_weights(dec, 3, 3, out) == 1                        # order 3
+    assert lib.phyai_unipc_weights(dec, 0, 1, out) == 1                        # no steps
+    assert lib.phyai_unipc_weights((f * 3)(1.0, 0.6, 0.6), 3, 2, out) == 1     # not strictly decreasing
+    assert lib.phyai_unipc_weights((f * 3)(1.2, 0.6, 0.2), 3, 2, out) == 1     # starts above 1
+    assert lib.phyai_unipc_weights((f * 3)(1.0, 0.6, 0.0), 3, 2, out) == 1     # reaches 0 before the end
+    assert lib.phyai_unipc_weights(dec, 3, 2, out) == 0
 
 
 def test_quantizer_argument_checks(lib):
