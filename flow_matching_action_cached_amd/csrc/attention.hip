@@ -447,28 +447,33 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
 // weights split s by 2^(m_s - M) l_s (M the largest m_s) and writes the normalised output
 // columns of the slot to o.  Slot u of a lane holds output columns 32u + 4 grp + i and
 // 32u + 16 + 4 grp + i (bf16 partials) or 16u + 4 grp + i (fp32), row r16 of the tile.
+// The arguments are the scalars the first loads need, in the order the kernel-argument
+// preload puts them in SGPRs at wave launch (no wait for the argument fetch): the split
+// workspace, the output o, the split count, the (sample, KV head, query tile) items, query
+// tiles per KV head, KV heads, query heads per KV head, chunk tokens.
 template <class AT, int DH, int SM>
-__global__ __launch_bounds__(64) void k_attn_merge(Dims d, Bufs bf, int S) {
+__global__ __launch_bounds__(64) void k_attn_merge(const float* attn_ws, void* o_out, int S, int nitems, int QT,
+                                                   int Hkv, int gq, int H) {
   constexpr int ES = sizeof(AT);
   constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;
   constexpr uint32_t STRIDE = PAY * 1024 + 128;
-  const int gq = d.Hq / d.Hkv, QT = (gq * d.H + 15) / 16;
   const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4;
   const int u = blockIdx.x % PAY, item = blockIdx.x / PAY;  // one wave per (query tile, slot)
-  if (item >= d.B * d.Hkv * QT) return;
-  const int qt = item % QT, r = (item / QT) % d.Hkv, b = item / QT / d.Hkv;
-  const int qrow = qt * 16 + r16;
-  if (qrow >= gq * d.H) return;
-  const int head = r * gq + qrow / d.H, m = b * d.H + qrow % d.H;
-  const char* ws = reinterpret_cast<const char*>(bf.attn_ws) + (size_t)item * S * STRIDE;
+  if (item >= nitems) return;
+  // The item's splits through one buffer resource: the split offset is a scalar operand of
+  // each load and the lane offsets are the same for every split.
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(attn_ws) + (size_t)item * S * STRIDE), (short)0,
+      (int)(S * STRIDE), 0x00020000);
+  const uint32_t o_m = PAY * 1024 + r16 * 4, o_p = (u * 64 + lane) * 16;
   float ms[SM], ls[SM];
   u32x4 pv[SM];
 #pragma unroll
   for (int s2 = 0; s2 < SM; ++s2) {
-    const char* sp = ws + (size_t)min(s2, S - 1) * STRIDE;
-    ms[s2] = *reinterpret_cast<const float*>(sp + PAY * 1024 + r16 * 4);
-    ls[s2] = *reinterpret_cast<const float*>(sp + PAY * 1024 + 64 + r16 * 4);
-    pv[s2] = *reinterpret_cast<const u32x4*>(sp + (u * 64 + lane) * 16);
+    const uint32_t so = (uint32_t)min(s2, S - 1) * STRIDE;
+    ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m, so, 0));
+    ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m + 64, so, 0));
+    pv[s2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, o_p, so, 0));
   }
   float M = -INFINITY;
 #pragma unroll
@@ -491,8 +496,13 @@ __global__ __launch_bounds__(64) void k_attn_merge(Dims d, Bufs bf, int S) {
     }
   }
   const float inv = 1.0f / den;
-  const int qd = d.Hq * DH;
-  AT* op = static_cast<AT*>(bf.o);
+  // this lane's row (rows past the last query row of the tile: nothing to write)
+  const int qt = item % QT, r = (item / QT) % Hkv, b = item / QT / Hkv;
+  const int qrow = qt * 16 + r16;
+  if (qrow >= gq * H) return;
+  const int head = r * gq + qrow / H, m = b * H + qrow % H;
+  const int qd = gq * Hkv * DH;
+  AT* op = static_cast<AT*>(o_out);
 #pragma unroll
   for (int t = 0; t < (ES == 2 ? 2 : 1); ++t) {
     const int col = (ES == 2 ? 32 * u + 16 * t : 16 * u) + grp * 4;
@@ -763,12 +773,16 @@ int attn_wide_tiles(int dh) { return dh <= 128 ? 16 : 8; }
 
 template <class AT>
 static hipError_t launch_attn_merge(const Dims& d, const Bufs& b, int S, hipStream_t st) {
-  const int QT = ((d.Hq / d.Hkv) * d.H + 15) / 16;
+  const int gq = d.Hq / d.Hkv, QT = (gq * d.H + 15) / 16, nitems = d.B * d.Hkv * QT;
   const int pay = sizeof(AT) == 2 ? d.dh / 32 : d.dh / 16;
-  dim3 mgrid(d.B * d.Hkv * QT * pay), mblock(64);
+  dim3 mgrid(nitems * pay), mblock(64);
 #define PHYAI_MERGE(DH)                                                                          \
-  if (S > 16) hipLaunchKernelGGL((k_attn_merge<AT, DH, 32>), mgrid, mblock, 0, st, d, b, S);      \
-  else hipLaunchKernelGGL((k_attn_merge<AT, DH, 16>), mgrid, mblock, 0, st, d, b, S);
+  if (S > 16)                                                                                        \
+    hipLaunchKernelGGL((k_attn_merge<AT, DH, 32>), mgrid, mblock, 0, st, b.attn_ws, b.o, S, nitems, QT, d.Hkv, gq, \
+                       d.H);                                                                           \
+  else                                                                                               \
+    hipLaunchKernelGGL((k_attn_merge<AT, DH, 16>), mgrid, mblock, 0, st, b.attn_ws, b.o, S, nitems, QT, d.Hkv, gq, \
+                       d.H);
   switch (d.dh) {
     case 32: PHYAI_MERGE(32) break;
     case 64: PHYAI_MERGE(64) break;
