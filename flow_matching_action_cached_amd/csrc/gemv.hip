@@ -41,12 +41,13 @@ __device__ __forceinline__ bf16x8 int4_frag_biased(uint32_t w) {
 }
 
 // ------------------------------------------------------------------ weight-streaming GEMM
-// The operands that the weight and activation loads need (W, A, K, splits, second row
-// block) lead the argument list as scalars: they are preloaded into SGPRs at wave launch,
-// so the loads do not wait for the kernel-argument fetch.
+// The operands that the weight and activation loads need (W, A, K, log2 of the split
+// count, second row block, k-blocks per split) lead the argument list as scalars: they are
+// preloaded into SGPRs at wave launch, so the loads wait neither for the kernel-argument
+// fetch nor for an integer division.
 template <class AT, class WT, int MT, int NT, int KBW, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, int Kp, int Sp, int nsec, Dims d,
-                                              Bufs bf, GemmLaunch g) {
+__global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, int Kp, int slog, int nsec, int kbs,
+                                              Dims d, Bufs bf, GemmLaunch g) {
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_GEGLU);
   constexpr bool INT4 = __is_same(WT, i4);
   __shared__ f32x4 red[4][NT][MT][64];
@@ -54,14 +55,13 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
   __shared__ unsigned flag;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int s = blockIdx.x % Sp, tile = blockIdx.x / Sp;
+  const int s = blockIdx.x & ((1 << slog) - 1), tile = blockIdx.x >> slog;
   int nrow[NT];
   nrow[0] = tile * 16;
   if (NT == 2) nrow[NT - 1] = nsec + tile * 16;
 
   PHASE_MARK(0);
   // this wave's k-blocks: [kbeg, min(kbeg + KBW, kend)), contiguous
-  const int KB = Kp / 32, kbs = KB / Sp;
   const int kbeg = s * kbs + w * KBW, kend = s * kbs + kbs;
 
   // ---- 1. loads: first the weights (HBM) and activations (L2), whose addresses come from
@@ -289,7 +289,9 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
 
 template <class AT, class WT, int EPI, int NT, int MT>
 static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& g, int tiles, hipStream_t st) {
+  if (g.S <= 0 || (g.S & (g.S - 1))) return hipErrorInvalidValue;   // splits: a power of two
   const int kbs = g.K / 32 / g.S;        // k-blocks per split (a multiple of 4), shared by 4 waves
+  const int slog = __builtin_ctz((unsigned)g.S);
   // every wave owns exactly kbw k-blocks; int4 waves own whole 128-wide quads (one scale
   // group each), so splits of fewer than four quads leave the surplus waves idle
   const int qps = kbs / 4;
@@ -297,10 +299,10 @@ static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& 
   if (__is_same(WT, i4) && qps > 4 && qps % 4) return hipErrorInvalidValue;
   dim3 grid(tiles * g.S), block(256);
   switch (kbw) {
-    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
-    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, g.W, g.A, g.K, g.S, g.n_second, d, b, g); break;
+    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
+    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
