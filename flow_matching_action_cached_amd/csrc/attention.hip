@@ -441,59 +441,97 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
   PHASE_MARK(7);
 }
 
-// Merge of the key splits of the few-row attention, one launch after it: a one-wave
-// workgroup per (query tile, 16-byte slot); each lane reads its slot and its row's (m, l)
-// from every split,
-// weights split s by 2^(m_s - M) l_s (M the largest m_s) and writes the normalised output
-// columns of the slot to o.  Slot u of a lane holds output columns 32u + 4 grp + i and
-// 32u + 16 + 4 grp + i (bf16 partials) or 16u + 4 grp + i (fp32), row r16 of the tile.
-// The arguments are the scalars the first loads need, in the order the kernel-argument
-// preload puts them in SGPRs at wave launch (no wait for the argument fetch): the split
-// workspace, the output o, the split count, the (sample, KV head, query tile) items, query
-// tiles per KV head, KV heads, query heads per KV head, chunk tokens.
+// Merge of the key splits of the few-row attention, one launch after it: a four-wave
+// workgroup per (query tile, 16-byte slot).  Wave w takes the splits [w spw, w spw + spw)
+// (spw = ceil(S / 4)) and forms their log-sum-exp state: its largest m_s as M_w,
+// den_w = sum 2^(m_s - M_w) l_s and acc_w = sum 2^(m_s - M_w) l_s (O_s / l_s); wave 0 then
+// combines the four states in wave order with the weights 2^(M_w - M), M the largest M_w,
+// and writes acc / den, the normalised output columns of the slot, to o.  Four waves keep
+// four times the loads of one in flight on the CU.  Slot u of a lane holds output columns
+// 32u + 4 grp + i and 32u + 16 + 4 grp + i (bf16 partials) or 16u + 4 grp + i (fp32), row r16
+// of the tile.  The arguments are the scalars the first loads need, in the order the
+// kernel-argument preload puts them in SGPRs at wave launch (no wait for the argument
+// fetch): the split workspace, the output o, the split count, the (sample, KV head, query
+// tile) items, query tiles per KV head, KV heads, query heads per KV head, chunk tokens.
 template <class AT, int DH, int SM>
-__global__ __launch_bounds__(64) void k_attn_merge(const float* attn_ws, void* o_out, int S, int nitems, int QT,
-                                                   int Hkv, int gq, int H) {
+__global__ __launch_bounds__(256) void k_attn_merge(const float* attn_ws, void* o_out, int S, int nitems, int QT,
+                                                    int Hkv, int gq, int H) {
   constexpr int ES = sizeof(AT);
   constexpr int PAY = ES == 2 ? DH / 32 : DH / 16;
   constexpr uint32_t STRIDE = PAY * 1024 + 128;
-  const int lane = threadIdx.x, r16 = lane & 15, grp = lane >> 4;
-  const int u = blockIdx.x % PAY, item = blockIdx.x / PAY;  // one wave per (query tile, slot)
+  constexpr int NWV = 4, SPW = SM / NWV;     // waves; split capacity of a wave's registers
+  constexpr int NA = ES == 2 ? 2 : 1;        // f32x4 accumulators per lane
+  __shared__ f32x4 c_acc[NWV - 1][NA][64];
+  __shared__ float c_m[NWV - 1][64], c_den[NWV - 1][64];
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.x % PAY, item = blockIdx.x / PAY;  // one workgroup per (query tile, slot)
   if (item >= nitems) return;
-  // The item's splits through one buffer resource: the split offset is a scalar operand of
-  // each load and the lane offsets are the same for every split.
+  const int spw = (S + NWV - 1) / NWV, s0 = w * spw, ns = max(0, min(S - s0, spw));  // this wave's splits
+  // the item's splits through one buffer resource: the split offset is the scalar operand of
+  // each load and the lane offsets are the same for every split
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(reinterpret_cast<const char*>(attn_ws) + (size_t)item * S * STRIDE), (short)0,
       (int)(S * STRIDE), 0x00020000);
   const uint32_t o_m = PAY * 1024 + r16 * 4, o_p = (u * 64 + lane) * 16;
-  float ms[SM], ls[SM];
-  u32x4 pv[SM];
+  float ms[SPW], ls[SPW];
+  u32x4 pv[SPW];
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2) {
-    const uint32_t so = (uint32_t)min(s2, S - 1) * STRIDE;
-    ms[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m, so, 0));
-    ls[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m + 64, so, 0));
-    pv[s2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, o_p, so, 0));
+  for (int j = 0; j < SPW; ++j) {
+    const uint32_t so = (uint32_t)min(s0 + j, S - 1) * STRIDE;
+    ms[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m, so, 0));
+    ls[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, o_m + 64, so, 0));
+    pv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, o_p, so, 0));
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2)
-    if (s2 < S) M = fmaxf(M, ms[s2]);
+  for (int j = 0; j < SPW; ++j)
+    if (j < ns) M = fmaxf(M, ms[j]);
   float den = 0.f;
-  f32x4 acc[ES == 2 ? 2 : 1];
+  f32x4 acc[NA];
 #pragma unroll
-  for (int t = 0; t < (ES == 2 ? 2 : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s2 = 0; s2 < SM; ++s2) {
-    const float wgt = s2 < S ? exp2f(ms[s2] - M) * ls[s2] : 0.f;
+  for (int j = 0; j < SPW; ++j) {
+    const float wgt = j < ns ? exp2f(ms[j] - M) * ls[j] : 0.f;
     den += wgt;
     if constexpr (ES == 2) {
-      const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[s2]);
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, pv[j]);
       acc[0] += wgt * f32x4{(float)pk[0], (float)pk[1], (float)pk[2], (float)pk[3]};
       acc[1] += wgt * f32x4{(float)pk[4], (float)pk[5], (float)pk[6], (float)pk[7]};
     } else {
-      acc[0] += wgt * __builtin_bit_cast(f32x4, pv[s2]);
+      acc[0] += wgt * __builtin_bit_cast(f32x4, pv[j]);
     }
+  }
+  // the four states, combined by wave 0 in wave order (a wave without splits has den 0 and
+  // M = -inf: weight 0)
+  if (w > 0) {
+    c_m[w - 1][lane] = M;
+    c_den[w - 1][lane] = den;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) c_acc[w - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (w > 0) return;
+  float Mw[NWV];
+  Mw[0] = M;
+#pragma unroll
+  for (int v = 1; v < NWV; ++v) Mw[v] = c_m[v - 1][lane];
+  float Mx = Mw[0];
+#pragma unroll
+  for (int v = 1; v < NWV; ++v) Mx = fmaxf(Mx, Mw[v]);
+  {
+    const float f0 = exp2f(Mw[0] - Mx);
+    den *= f0;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) acc[t] *= f0;
+  }
+#pragma unroll
+  for (int v = 1; v < NWV; ++v) {
+    const float f = Mw[v] == -INFINITY ? 0.f : exp2f(Mw[v] - Mx);
+    den += f * c_den[v - 1][lane];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) acc[t] += f * c_acc[v - 1][t][lane];
   }
   const float inv = 1.0f / den;
   // this lane's row (rows past the last query row of the tile: nothing to write)
@@ -504,7 +542,7 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* attn_ws, void* o
   const int qd = gq * Hkv * DH;
   AT* op = static_cast<AT*>(o_out);
 #pragma unroll
-  for (int t = 0; t < (ES == 2 ? 2 : 1); ++t) {
+  for (int t = 0; t < NA; ++t) {
     const int col = (ES == 2 ? 32 * u + 16 * t : 16 * u) + grp * 4;
     AT* dst = op + sw_idx(m, head * DH + col, qd);
 #pragma unroll
@@ -775,7 +813,7 @@ template <class AT>
 static hipError_t launch_attn_merge(const Dims& d, const Bufs& b, int S, hipStream_t st) {
   const int gq = d.Hq / d.Hkv, QT = (gq * d.H + 15) / 16, nitems = d.B * d.Hkv * QT;
   const int pay = sizeof(AT) == 2 ? d.dh / 32 : d.dh / 16;
-  dim3 mgrid(nitems * pay), mblock(64);
+  dim3 mgrid(nitems * pay), mblock(256);
 #define PHYAI_MERGE(DH)                                                                          \
   if (S > 16)                                                                                        \
     hipLaunchKernelGGL((k_attn_merge<AT, DH, 32>), mgrid, mblock, 0, st, b.attn_ws, b.o, S, nitems, QT, d.Hkv, gq, \
