@@ -41,9 +41,9 @@ MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 # write x1.0).  They describe the kernel sources they were taken on: the hash covers every
 # source file of the library, and any change makes the bench report traffic null.
 PROFILED_TRAFFIC = {
-    "sources_sha256": "d57feabdb72e86215f799f8d289272177de7eb0a78ee1d1f36e71eeeef1cd120",
-    "bytes": {"qkv": 6959104, "attention": 8951298, "attn_merge": 6812672, "o_proj": 7727998,
-              "gate_up": 18927617, "down": 13810577, "out_euler": 2142149},
+    "sources_sha256": "0fb01a64c716dbbb114bc1ab90bf0e431e24df2bfd0732ee1e6cdffd8cd95127",
+    "bytes": {"qkv": 6942720, "attention": 8948226, "attn_merge": 6722561, "o_proj": 7720899,
+              "gate_up": 18929665, "down": 13798579, "out_euler": 2142132},
 }
 
 
