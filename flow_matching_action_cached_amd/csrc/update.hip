@@ -14,6 +14,20 @@ namespace phyai {
 PHYAI_PHASE_TRACE_READER(phyai_phase_trace_update)
 #endif
 
+// An io-typed value loaded as a 32-bit word with nothing computed from it yet (bf16: the
+// zero-extended bits), widened to fp32 only where it is used: a conversion next to the load
+// would make the wave wait for the load there.
+template <class T> __device__ __forceinline__ uint32_t ld_bits(const T* p);
+template <> __device__ __forceinline__ uint32_t ld_bits<float>(const float* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+template <> __device__ __forceinline__ uint32_t ld_bits<bf16>(const bf16* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+template <class T> __device__ __forceinline__ float bits_f32(uint32_t v) {
+  return __builtin_bit_cast(float, sizeof(T) == 2 ? v << 16 : v);
+}
+
 // ------------------------------------------------------------------ out-projection + Euler + in-projection
 // k_prev >= 0: final adaptive norm of step k_prev, v = rinv (hs W_out^T) + W_out shift +
 // b_out, x += dt v.  k_next >= 0: in-projection h = x W_in^T + b_in for step k_next,
@@ -40,14 +54,43 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
   const int rt = blockIdx.x / cs, cpart = blockIdx.x - rt * cs, m0 = rt * 16;
   const int nta = (d.A + 15) / 16;  // 16-column output tiles of the out-projection (A <= 256)
   PHASE_MARK(0);
-  if (k_prev >= 0) {
-    {  // final-norm statistics of the tile's rows: 16 threads per row
-      const int r = tid >> 4, j0 = tid & 15, m = min(m0 + r, d.M - 1), n16 = d.D / 16;
-      float ss = 0.f;
-      for (int j = j0; j < n16; j += 16) ss += bf.ssq[(size_t)m * n16 + j];
-      ss = sum16(ss);
-      if (j0 == 0) rinv_s[r] = 1.0f / sqrtf(ss / (float)d.D + d.eps);
+  // Operands that need nothing computed here are loaded up front, so that their round trips
+  // overlap the out-projection's instead of following it: the in-projection weights, bias
+  // and scale of this wave's first pass, the final-norm statistics, and the state, W_out
+  // shift and bias of this thread's first update element.  The loads are unconditional
+  // (indices clamped to valid rows, columns and steps; what a launch does not use is
+  // ignored) and nothing is computed from them here, so no wait follows them.
+  const IOT* wi = static_cast<const IOT*>(bf.w_in);
+  const IOT* bi = static_cast<const IOT*>(bf.b_in);
+  const int ntn = d.D / 16, ntb = cpart * (ntn / cs), nte = ntb + ntn / cs;
+  WF wv0[4];
+  uint32_t b00[4];
+  float sc10[4];
+  {
+    const float* scl = bf.mod + (size_t)max(k_next, 0) * d.nmod * 2 * d.D;  // norm 0, scale row
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = min(ntb + w + 4 * j, nte - 1) * 16 + r16;
+      wv0[j] = load_frag(wi + (size_t)n * d.A + min(grp * 8, d.A - 8));
+      b00[j] = ld_bits(bi + n);
+      sc10[j] = scl[n];
     }
+  }
+  const int sr = tid >> 4, sj0 = tid & 15, n16 = d.D / 16;   // statistics: 16 threads per row
+  float ssv[8];
+  float xv0[4], cva0;
+  uint32_t boa0;
+  {
+    const int sm = min(m0 + sr, d.M - 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ssv[q] = bf.ssq[(size_t)sm * n16 + min(sj0 + 16 * q, n16 - 1)];
+    const int l = tid & 63, a = min((tid >> 6) * 16 + (l & 15), d.A - 1);
+    cva0 = bf.cvec[(size_t)max(k_prev, 0) * bf.cv_stride + bf.cv_out_off + a];
+    boa0 = ld_bits(static_cast<const IOT*>(bf.b_out) + a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv0[i] = bf.x[(size_t)min(m0 + 4 * (l >> 4) + i, d.M - 1) * d.A + a];
+  }
+  if (k_prev >= 0) {
     PHASE_MARK(1);
     const AT* hs = static_cast<const AT*>(bf.hs);
     const IOT* wo = static_cast<const IOT*>(bf.w_out);
@@ -74,6 +117,14 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
       red[w][nt0][lane] = acc[0];
       if (nt0 + 1 < nta) red[w][nt0 + 1][lane] = acc[1];
     }
+    {  // final-norm statistics of the tile's rows, summed in column order
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss += sj0 + 16 * q < n16 ? ssv[q] : 0.f;
+      for (int j = sj0 + 128; j < n16; j += 16) ss += bf.ssq[(size_t)min(m0 + sr, d.M - 1) * n16 + j];
+      ss = sum16(ss);
+      if (sj0 == 0) rinv_s[sr] = 1.0f / sqrtf(ss / (float)d.D + d.eps);
+    }
     PHASE_MARK(2);
     __syncthreads();
     const IOT* bo = static_cast<const IOT*>(bf.b_out);
@@ -84,12 +135,13 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
     for (int e = tid; e < nta * 64; e += 256) {
       const int nt = e >> 6, l = e & 63, a = nt * 16 + (l & 15);
       const f32x4 s = ((red[0][nt][l] + red[1][nt][l]) + red[2][nt][l]) + red[3][nt][l];
+      const bool first = e == tid;   // this thread's first element: operands loaded up front
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * (l >> 4) + i, m = m0 + r;
         if (m < d.M && a < d.A) {
-          const float v = rinv_s[r] * s[i] + cv[a] + to_f32(bo[a]);
-          const float xn = bf.x[(size_t)m * d.A + a] + dt * v;
+          const float v = rinv_s[r] * s[i] + (first ? cva0 : cv[a]) + (first ? bits_f32<IOT>(boa0) : to_f32(bo[a]));
+          const float xn = (first ? xv0[i] : bf.x[(size_t)m * d.A + a]) + dt * v;
           xs[r][a] = xn;
           if (cs == 1) bf.x[(size_t)m * d.A + a] = xn;
         }
@@ -128,13 +180,10 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
   // in-projection on fp32 MFMA (exact products of the fp32 state and the weights):
   // H = X W_in^T + b_in, one 16 x 16 output tile per MFMA chain, K = A in 32-wide chunks
   // (columns past A are zero in xs and in the weight fragments)
-  const IOT* wi = static_cast<const IOT*>(bf.w_in);
-  const IOT* bi = static_cast<const IOT*>(bf.b_in);
   const float* scl = bf.mod + (size_t)k_next * d.nmod * 2 * d.D;  // norm 0, scale row
   AT* hsw = static_cast<AT*>(bf.hs);
-  const int kc_n = (d.A + 31) / 32, ntn = d.D / 16;
+  const int kc_n = (d.A + 31) / 32;
   // this workgroup's column tiles: [ntb, nte), four of a wave's (nt0 + 4 j) at a time
-  const int ntb = cpart * (ntn / cs), nte = ntb + ntn / cs;
   for (int nt0 = ntb + w; nt0 < nte; nt0 += 16) {
     f32x4 acc[4];
     float b0[4], sc1[4];
@@ -143,9 +192,16 @@ __global__ __launch_bounds__(256) void k_out_rows(Dims d, Bufs bf, int k_prev, i
     for (int kc = 0; kc < kc_n; ++kc) {
       const int a0 = kc * 32 + grp * 8;
       WF wv[4];
+      const bool first = nt0 == ntb + w && kc == 0;   // loaded up front
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = min(nt0 + 4 * j, nte - 1) * 16 + r16;
+        if (first) {
+          wv[j] = wv0[j];
+          b0[j] = bits_f32<IOT>(b00[j]);
+          sc1[j] = 1.0f + sc10[j];
+          continue;
+        }
         wv[j] = load_frag(wi + (size_t)n * d.A + min(a0, d.A - 8));
         if (kc == 0) {  // the epilogue's bias and scale, with the first weights
           b0[j] = to_f32(bi[n]);
