@@ -564,10 +564,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
   constexpr int NB = DH <= 64 ? 4 : 2;   // 32-key blocks per group (registers: 2 waves per SIMD)
   constexpr int NK = NB * 32;
   constexpr int KROW = DH + 8;           // K row: DH + 16 B pad
-  // V^T row: NK keys + 8 B pad.  The fragment reads are 8-byte pairs along a row at rows
-  // r16 = 0..15; a row stride of 2 mod 32 dwords puts the 16 rows on distinct banks (a
-  // 16-byte pad, 4 mod 32, paired rows r and r + 8: 40.5 -> 37.6 us per batch-32 launch).
-  constexpr int VROW = NK + 4;
+  // V^T row: NK keys + 16 B pad, the keys of each 32-key block permuted so that the eight
+  // keys a lane's probability fragment holds (4 grp + i and 16 + 4 grp + i, i < 4) are
+  // adjacent: key 16 h + 4 g + i sits at 8 g + 4 h + i.  A V fragment is then one 16-byte
+  // read, at rows r16 = 0..15 with a stride of 4 mod 32 dwords (eight lanes per cycle on
+  // distinct banks).
+  constexpr int VROW = NK + 8;
   constexpr int KCPR = DH / 8, VCPR = NK / 8;
   constexpr int KCH = NK * KCPR, VCH = DH * VCPR;
   constexpr int CPT = (KCH + VCH) / (64 * NW);
@@ -646,9 +648,13 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
                         : vs[buf] + ((c - KCH) / VCPR) * VROW + ((c - KCH) % VCPR) * 8;
       if (c < KCH) {
         *reinterpret_cast<u32x4*>(dst) = stage[i];
-      } else {  // V^T rows are 8-byte aligned
-        reinterpret_cast<u32x2*>(dst)[0] = u32x2{stage[i][0], stage[i][1]};
-        reinterpret_cast<u32x2*>(dst)[1] = u32x2{stage[i][2], stage[i][3]};
+      } else {
+        // keys k .. k+7 of a block (k = 0, 8, 16, 24): two runs of four, g = k % 16 / 4 and
+        // g + 1, half h = k / 16, to 8 g + 4 h and 8 (g + 1) + 4 h
+        const int k32 = (((c - KCH) % VCPR) * 8) % 32, h = k32 >> 4, g = (k32 & 15) >> 2;
+        AT* blk = dst - k32;
+        *reinterpret_cast<u32x2*>(blk + 8 * g + 4 * h) = u32x2{stage[i][0], stage[i][1]};
+        *reinterpret_cast<u32x2*>(blk + 8 * (g + 1) + 4 * h) = u32x2{stage[i][2], stage[i][3]};
       }
     }
   };
@@ -774,8 +780,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_wide(Dims d, Bufs bf, int laye
         Frag vf[VB];
 #pragma unroll
         for (int t = 0; t < VB; ++t) {
-          const AT* vp = vb_ + ((t0 + t) * 16 + r16) * VROW + j * 32 + grp * 4;
-          vf[t] = load_frag_split4(vp, vp + 16);
+          vf[t] = load_frag(vb_ + ((t0 + t) * 16 + r16) * VROW + j * 32 + grp * 8);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
