@@ -114,6 +114,21 @@ def test_tiny_ragged_prefix_lengths(prefix_len):
     assert rel_err(got, ex.denoise(inp, d)) <= 1e-4
 
 
+@pytest.mark.parametrize("wd,tol,batch", [("f32", 1e-4, 1), ("bf16", 2e-2, 3)])
+def test_wide_action_dim_matches_oracle(wd, tol, batch):
+    """Action dim 72 (four and a half 16-column tiles) with 20 chunk tokens: the
+    out-projection / Euler / in-projection kernel updates a second element per thread
+    (5 x 64 > 256 threads) and runs its in-projection over three 32-wide chunks, beyond the
+    operands it loads up front for the first element and the first pass."""
+    d = dataclasses.replace(TINY, action_dim=72, chunk_len=20, weight_dtype=wd, batch=batch)
+    _say(f"case: action dim 72, {wd}, batch {batch}")
+    inp = synth.make_expert_inputs(d, 2)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"  rel err {err:.3e}")
+    assert err <= tol
+
+
 def test_pi05_bf16_matches_oracle():
     _say("case: pi05 bf16 batch 1, seed 0")
     inp = synth.make_expert_inputs(PI05, 0)
