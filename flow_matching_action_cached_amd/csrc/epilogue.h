@@ -25,6 +25,7 @@ struct GemmLaunch {
   const float* cvec;         // norm-folded bias of this step/layer (QKV, GEGLU)
   const float* scale_next;   // raw scale of the norm that consumes h (RESID)
   const float* gate;         // residual gate of the block this GEMM closes (RESID; null: none)
+  int wnt;                   // 1: weights read with the non-temporal policy (weight-streaming GEMMs)
 };
 
 // Rotary position embedding of the QKV output y at token row m, column col (PhyAI reading

@@ -40,14 +40,24 @@ __device__ __forceinline__ bf16x8 int4_frag_biased(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// A weight fragment read with the non-temporal policy (buffer load, nt), through resource r
+// over the weights at base: for weights that the caches should not keep (bf16; fp32 weights
+// take the plain load).
+__device__ __forceinline__ bf16x8 load_frag_nt(__amdgpu_buffer_rsrc_t r, const bf16* base, const bf16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((p - base) * 2), 0, 2));
+}
+__device__ __forceinline__ f32x8 load_frag_nt(__amdgpu_buffer_rsrc_t, const float*, const float* p) { return load_frag(p); }
+
 // ------------------------------------------------------------------ weight-streaming GEMM
 // The operands that the weight and activation loads need (W, A, K, log2 of the split
-// count, second row block, k-blocks per split) lead the argument list as scalars: they are
-// preloaded into SGPRs at wave launch, so the loads wait neither for the kernel-argument
-// fetch nor for an integer division.
+// count, second row block, k-blocks per split, non-temporal weights) lead the argument list
+// as scalars: they are preloaded into SGPRs at wave launch, so the loads wait neither for
+// the kernel-argument fetch nor for an integer division.  wnt: the weights are read with the
+// non-temporal policy (this layer's weights are not meant to stay in the memory-side cache
+// until the next step; see resident_weight_layers).
 template <class AT, class WT, int MT, int NT, int KBW, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, int Kp, int slog, int nsec, int kbs,
-                                              Dims d, Bufs bf, GemmLaunch g) {
+                                              int wnt, Dims d, Bufs bf, GemmLaunch g) {
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_GEGLU);
   constexpr bool INT4 = __is_same(WT, i4);
   __shared__ f32x4 red[4][NT][MT][64];
@@ -79,14 +89,28 @@ __global__ __launch_bounds__(256) void k_gemm(const void* Wp, const void* Ap, in
   u32x4 wq[NQW][NT];                                               // int4: one 16-byte slot per quad
   float wsc[NQW][NT];
   if (wave_active) {
+    if constexpr (!INT4) {
+      // every weight fragment of the wave, then the activations (one branch per policy, so
+      // that each load's cache policy is a constant)
+      auto load_w = [&](auto ntc) {
+        constexpr bool NTL = decltype(ntc)::value;
+        const __amdgpu_buffer_rsrc_t wr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(Wp), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < KBW; ++i)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const WT* p = static_cast<const WT*>(Wp) + sw_frag(nrow[nt] >> 4, kbeg + i, Kp, lane);
+            wf[i][nt] = NTL ? load_frag_nt(wr, static_cast<const WT*>(Wp), p) : load_frag(p);
+          }
+      };
+      if (wnt) load_w(std::true_type{});
+      else load_w(std::false_type{});
+    }
 #pragma unroll
     for (int i = 0; i < KBW; ++i) {
       const int kb = kbeg + i;
-      if constexpr (!INT4) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          wf[i][nt] = load_frag(static_cast<const WT*>(Wp) + sw_frag(nrow[nt] >> 4, kb, Kp, lane));
-      } else {
+      if constexpr (INT4) {
         if ((i & 3) == 0) {
           const int q = kb >> 2;
 #pragma unroll
@@ -299,10 +323,10 @@ static hipError_t launch_gemm_q(const Dims& d, const Bufs& b, const GemmLaunch& 
   if (__is_same(WT, i4) && qps > 4 && qps % 4) return hipErrorInvalidValue;
   dim3 grid(tiles * g.S), block(256);
   switch (kbw) {
-    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
-    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, d, b, g); break;
+    case 1: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 1, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, g.wnt, d, b, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 2, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, g.wnt, d, b, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 4, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, g.wnt, d, b, g); break;
+    case 8: hipLaunchKernelGGL((k_gemm<AT, WT, MT, NT, 8, EPI>), grid, block, 0, st, g.W, g.A, g.K, slog, g.n_second, kbs, g.wnt, d, b, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
