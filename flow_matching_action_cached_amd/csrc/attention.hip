@@ -265,7 +265,30 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
     for (int jh = 0; jh < NBH; ++jh) {
       const int j = jb + jh;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      if (g0 + j <= glast) {
+      if (g0 + j <= glast && !(ES == 4 && DH > 128)) {
+        // every K fragment of the block read before the first product (one LDS round trip,
+        // not one per product), and the dh sum as two interleaved chains per key half
+        // (fp32 fragments of dh > 128 would not fit the registers: read per product below)
+        Frag kf[DH / 32][2];
+#pragma unroll
+        for (int jj = 0; jj < DH / 32; ++jj) {
+          kf[jj][0] = load_frag(ks + (j * 32 + r16) * KROW + 32 * jj + grp * 8);
+          kf[jj][1] = load_frag(ks + (j * 32 + 16 + r16) * KROW + 32 * jj + grp * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < DH / 32; jj += 2) {
+          s0 = mma(kf[jj][0], qf[jj], s0);
+          s1 = mma(kf[jj][1], qf[jj], s1);
+          if (jj + 1 < DH / 32) {
+            e0 = mma(kf[jj + 1][0], qf[jj + 1], e0);
+            e1 = mma(kf[jj + 1][1], qf[jj + 1], e1);
+          }
+        }
+        s0 += e0;
+        s1 += e1;
+      } else if (g0 + j <= glast) {
 #pragma unroll
         for (int jj = 0; jj < DH / 32; ++jj) {
           s0 = mma(load_frag(ks + (j * 32 + r16) * KROW + 32 * jj + grp * 8), qf[jj], s0);
@@ -309,10 +332,19 @@ __global__ __launch_bounds__(NB >= 2 ? 512 : 256) void k_attn(Dims d, Bufs bf, i
         l_part += p;
         pf[e] = to_elem<AT>(p);
       }
+      // V fragments in batches of up to 8, each batch read before its products
+      constexpr int VB = DH / 16 < 8 ? DH / 16 : 8;
 #pragma unroll
-      for (int t = 0; t < DH / 16; ++t) {
-        const AT* vp = vs + (t * 16 + r16) * VROW + j * 32 + grp * 4;
-        o[t] = mma(load_frag_split4(vp, vp + 16), pf, o[t]);
+      for (int t0 = 0; t0 < DH / 16; t0 += VB) {
+        Frag vf[VB];
+#pragma unroll
+        for (int t = 0; t < VB; ++t) {
+          const AT* vp = vs + ((t0 + t) * 16 + r16) * VROW + j * 32 + grp * 4;
+          vf[t] = load_frag_split4(vp, vp + 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < VB; ++t) o[t0 + t] = mma(vf[t], pf, o[t0 + t]);
       }
     }
   }
