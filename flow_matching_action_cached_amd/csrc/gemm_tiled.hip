@@ -152,6 +152,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_tiled(Dims d, Bufs bf, 
 #pragma unroll
           for (int t = 0; t < WNT; ++t)
             bw[t] = __builtin_bit_cast(bf16x8, stage(j)[LA + (wn * WNT + t) * BKB + kb][lane]);
+          // every fragment of the k-block read before its products: one LDS round trip per
+          // k-block instead of one per fragment
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < WMT; ++i)
 #pragma unroll
