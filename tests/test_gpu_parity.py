@@ -114,6 +114,21 @@ def test_tiny_ragged_prefix_lengths(prefix_len):
     assert rel_err(got, ex.denoise(inp, d)) <= 1e-4
 
 
+@pytest.mark.parametrize("prefix_len", [1, 33, 1008, 1009])
+def test_tiny_bf16_few_row_attention_key_ranges(prefix_len):
+    """bf16 at batch 1 (4 query tiles) across key ranges of the split kernel: 17 keys (one
+    block, a single split with no merge launch), 49 (two one-block splits, the second
+    ragged), 1024 (32 one-block splits, the merge width) and 1025 (33 blocks: 17 two-block
+    splits, the last holding one block)."""
+    d = dataclasses.replace(TINY, prefix_len=prefix_len, weight_dtype="bf16")
+    _say(f"case: tiny bf16, prefix {prefix_len}")
+    inp = synth.make_expert_inputs(d, 4)
+    got = _run(d, inp)
+    err = rel_err(got, ex.denoise(inp, d))
+    _say(f"tiny bf16 prefix {prefix_len} rel err {err:.3e}")
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("wd,tol,batch", [("f32", 1e-4, 1), ("bf16", 2e-2, 3)])
 def test_wide_action_dim_matches_oracle(wd, tol, batch):
     """Action dim 72 (four and a half 16-column tiles) with 20 chunk tokens: the
